@@ -1,0 +1,304 @@
+"""Plain fp64 CPU oracle for causal differential attention and Grouped
+Differential Attention (GDA).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+link this module; only the test suite, the smoke check and the CPU-baseline
+leg of the benchmark use it.  It shares no code with the HIP kernels.
+
+Pages this file follows (cited by title and section):
+
+* [DA-blog]  "Differential Attention in Large Language Models: How Denoising
+  Subtraction Eliminates Attention Noise and Outlier Activations" (llms.blog):
+  section "The Mechanics of Attention Noise" (standard attention equation),
+  section "Differential Attention Architecture" (projection equations and the
+  DiffAttn equation), section "Learnable Lambda Re-parameterization" (lambda
+  and lambda_init equations), section "Headwise Normalization" (head_bar_i
+  equation).
+* [GDA]  "Grouped Differential Attention" (mlsanity.com), "Abstract": signal
+  heads outnumber noise-control heads, and the noise heads are repeated the
+  way GQA repeats key/value heads.
+* [DT-summary]  "Differential Transformer" (atlas.scime.ai), "Approach" and
+  the "Measured effects" table (the per-head norm is called GroupNorm there).
+
+What the method computes is exact: a fused kernel reaches the same real-valued
+function, only the rounding order differs.  So this oracle is the definition
+written out, in float64, with a full-row softmax (no online rescaling, no
+blocking over keys).  Readings taken where the pages are silent:
+
+* causal masking (query i sees keys 0..i) unless ``causal=False``;
+* the softmax scale is 1/sqrt(d) with d the width of one Q/K half, for both maps;
+* lambda and lambda_init are one scalar each per call (per layer);
+* the per-head norm is RMS (no mean subtraction) over the dv output channels,
+  with eps added to the mean of squares, then times (1 - lambda_init) and an
+  optional per-channel weight;
+* in GDA each noise head owns both its Q2 and its K2; signal head h uses noise
+  head noise_of_signal[h] (default h // (H_s / H_n)) and key/value head
+  kv_of_signal[h] (default h // (H_s / H_kv)).
+
+Every function here is pinned by the CPU tests against closed forms, library
+routines and brute force; none is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "lambda_init_schedule",
+    "lambda_reparam",
+    "consecutive_map",
+    "softmax_rows",
+    "head_rms_norm",
+    "diff_attention",
+    "diff_attention_rows",
+    "gda_decode",
+    "brute_diff_attention",
+    "causal_pairs",
+    "flops_alg",
+    "flops_exec",
+]
+
+
+# ---------------------------------------------------------------------------
+# Scalars: [DA-blog] "Learnable Lambda Re-parameterization"
+# ---------------------------------------------------------------------------
+
+def lambda_init_schedule(layer: int) -> float:
+    """lambda_init for 1-based layer index ``layer``: 0.8 minus 0.6 times
+    exp(-0.3 (layer - 1)) ([DA-blog], lambda_init equation)."""
+    return 0.8 - 0.6 * math.exp(-0.3 * (layer - 1))
+
+
+def lambda_reparam(lq1, lk1, lq2, lk2, lambda_init: float) -> float:
+    """lambda from the four learnable vectors: exp(lq1 . lk1) - exp(lq2 . lk2)
+    + lambda_init ([DA-blog], lambda equation).  The kernels take the folded
+    scalar; this exists so the tests can state where that scalar comes from."""
+    a = float(np.dot(np.asarray(lq1, np.float64), np.asarray(lk1, np.float64)))
+    b = float(np.dot(np.asarray(lq2, np.float64), np.asarray(lk2, np.float64)))
+    return math.exp(a) - math.exp(b) + lambda_init
+
+
+# ---------------------------------------------------------------------------
+# Head maps: [GDA] "Abstract" (noise heads repeated GQA-style)
+# ---------------------------------------------------------------------------
+
+def consecutive_map(h_s: int, h_x: int) -> np.ndarray:
+    """Signal head h -> shared head h // (h_s / h_x): consecutive grouping,
+    the GQA convention the GDA abstract refers to."""
+    if h_x <= 0 or h_s % h_x != 0:
+        raise ValueError(f"{h_s} signal heads cannot be grouped over {h_x} heads")
+    return np.arange(h_s, dtype=np.int64) // (h_s // h_x)
+
+
+# ---------------------------------------------------------------------------
+# Building blocks
+# ---------------------------------------------------------------------------
+
+def softmax_rows(s: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis; -inf entries get weight 0.  Each row is a
+    strictly positive distribution over its unmasked entries that sums to one
+    ([DA-blog] introduction).  The row max is subtracted before exp, which
+    changes nothing mathematically."""
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def head_rms_norm(o: np.ndarray, lambda_init: float, eps: float,
+                  weight: np.ndarray | None = None) -> np.ndarray:
+    """(1 - lambda_init) * RMSNorm(o) over the last axis ([DA-blog] "Headwise
+    Normalization", head_bar_i equation): o / sqrt(mean(o^2) + eps), times an
+    optional per-channel weight, times (1 - lambda_init)."""
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    y = o / np.sqrt(ms + eps)
+    if weight is not None:
+        y = y * np.asarray(weight, np.float64)
+    return (1.0 - lambda_init) * y
+
+
+def _as64(x) -> np.ndarray:
+    if hasattr(x, "detach"):  # a torch tensor handed in by a test
+        x = x.detach().to("cpu")
+        if str(x.dtype) in ("torch.bfloat16", "torch.float16"):
+            x = x.float()
+        x = x.double().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _maps(h_s, h_n, h_kv, noise_of_signal, kv_of_signal):
+    nz = consecutive_map(h_s, h_n) if noise_of_signal is None else np.asarray(noise_of_signal, np.int64)
+    kv = consecutive_map(h_s, h_kv) if kv_of_signal is None else np.asarray(kv_of_signal, np.int64)
+    if nz.shape != (h_s,) or kv.shape != (h_s,):
+        raise ValueError("head maps must have one entry per signal head")
+    if nz.min(initial=0) < 0 or nz.max(initial=0) >= h_n or kv.min(initial=0) < 0 or kv.max(initial=0) >= h_kv:
+        raise ValueError("head map entry out of range")
+    return nz, kv
+
+
+# ---------------------------------------------------------------------------
+# The forward: [DA-blog] DiffAttn equation + head_bar_i equation, [GDA] grouping
+# ---------------------------------------------------------------------------
+
+def diff_attention_rows(q1, q2, k1, k2, v, lam: float, lambda_init: float, *,
+                        rows, eps: float = 1e-5, norm_weight=None, causal: bool = True,
+                        noise_of_signal=None, kv_of_signal=None, normalize: bool = True,
+                        heads=None, batches=None, block: int = 256) -> np.ndarray:
+    """Output rows ``rows`` (query positions) of the forward, for the batches
+    ``batches`` and signal heads ``heads`` (default: all).
+
+    Shapes (BSHD, last dim contiguous):
+      q1 [B,N,H_s,d]   q2 [B,N,H_n,d]   k1 [B,N,H_kv,d]   k2 [B,N,H_n,d]
+      v  [B,N,H_kv,dv]
+    Returns float64 [len(batches), len(rows), len(heads), dv].
+
+    Per signal head h and query i ([DA-blog] DiffAttn equation):
+      s1_j = q1[i,h] . k1[j,kv(h)] / sqrt(d),  s2_j = q2[i,nz(h)] . k2[j,nz(h)] / sqrt(d)
+      a1 = softmax(s1), a2 = softmax(s2)  over visible keys j (j <= i if causal)
+      o  = sum_j (a1_j - lam * a2_j) v[j,kv(h)]
+    then ([DA-blog] head_bar_i equation) y = (1 - lambda_init) RMSNorm(o),
+    skipped when ``normalize`` is False (the raw DiffAttn output).
+    """
+    q1, q2, k1, k2, v = (_as64(t) for t in (q1, q2, k1, k2, v))
+    B, N, h_s, d = q1.shape
+    h_n = q2.shape[2]
+    h_kv = k1.shape[2]
+    dv = v.shape[3]
+    if q2.shape != (B, N, h_n, d) or k2.shape != (B, N, h_n, d):
+        raise ValueError("q2/k2 must be [B,N,H_n,d]")
+    if k1.shape != (B, N, h_kv, d) or v.shape[:3] != (B, N, h_kv):
+        raise ValueError("k1 must be [B,N,H_kv,d] and v [B,N,H_kv,dv]")
+    nz, kv = _maps(h_s, h_n, h_kv, noise_of_signal, kv_of_signal)
+    rows = np.asarray(rows, np.int64).reshape(-1)
+    heads = np.arange(h_s) if heads is None else np.asarray(heads, np.int64).reshape(-1)
+    batches = np.arange(B) if batches is None else np.asarray(batches, np.int64).reshape(-1)
+    w = None if norm_weight is None else _as64(norm_weight).reshape(dv)
+    scale = 1.0 / math.sqrt(d)
+    out = np.zeros((len(batches), len(rows), len(heads), dv), np.float64)
+    keys = np.arange(N)
+    for bi, b in enumerate(batches):
+        for hi, h in enumerate(heads):
+            for r0 in range(0, len(rows), block):
+                rr = rows[r0:r0 + block]
+                s1 = (q1[b, rr, h, :] @ k1[b, :, kv[h], :].T) * scale
+                s2 = (q2[b, rr, nz[h], :] @ k2[b, :, nz[h], :].T) * scale
+                if causal:
+                    hidden = keys[None, :] > rr[:, None]
+                    s1 = np.where(hidden, -np.inf, s1)
+                    s2 = np.where(hidden, -np.inf, s2)
+                a = softmax_rows(s1) - lam * softmax_rows(s2)
+                o = a @ v[b, :, kv[h], :]
+                out[bi, r0:r0 + len(rr), hi, :] = (
+                    head_rms_norm(o, lambda_init, eps, w) if normalize else o)
+    return out
+
+
+def diff_attention(q1, q2, k1, k2, v, lam: float, lambda_init: float, **kw) -> np.ndarray:
+    """All rows of the forward: float64 [B,N,H_s,dv].  Plain differential
+    attention is the case H_n = H_kv = H_s; GDA is H_s > H_n."""
+    n = _as64(q1).shape[1] if not hasattr(q1, "shape") else q1.shape[1]
+    return diff_attention_rows(q1, q2, k1, k2, v, lam, lambda_init, rows=np.arange(n), **kw)
+
+
+def gda_decode(q1, q2, k1_cache, k2_cache, v_cache, seq_lens, lam: float, lambda_init: float, *,
+               eps: float = 1e-5, norm_weight=None, noise_of_signal=None, kv_of_signal=None,
+               normalize: bool = True, batches=None) -> np.ndarray:
+    """One new query per sequence against its cache (the serving step).
+
+      q1 [B,H_s,d]  q2 [B,H_n,d]
+      k1_cache [B,H_kv,Lmax,d]  k2_cache [B,H_n,Lmax,d]  v_cache [B,H_kv,Lmax,dv]
+      seq_lens [B]: the query sees cache positions 0..L_b-1 (the cache already
+      holds the current token, so this is the last row of a causal prefill).
+    Returns float64 [len(batches), H_s, dv]; a sequence with L_b = 0 gives zeros.
+    Same formulas as ``diff_attention_rows``.
+    """
+    q1, q2, k1c, k2c, vc = (_as64(t) for t in (q1, q2, k1_cache, k2_cache, v_cache))
+    lens = np.asarray(_as64(seq_lens), np.int64).reshape(-1)
+    B, h_s, d = q1.shape
+    h_n = q2.shape[1]
+    h_kv = k1c.shape[1]
+    dv = vc.shape[3]
+    nz, kv = _maps(h_s, h_n, h_kv, noise_of_signal, kv_of_signal)
+    w = None if norm_weight is None else _as64(norm_weight).reshape(dv)
+    batches = np.arange(B) if batches is None else np.asarray(batches, np.int64).reshape(-1)
+    scale = 1.0 / math.sqrt(d)
+    out = np.zeros((len(batches), h_s, dv), np.float64)
+    for bi, b in enumerate(batches):
+        L = int(lens[b])
+        if L <= 0:
+            continue
+        for h in range(h_s):
+            s1 = (k1c[b, kv[h], :L, :] @ q1[b, h, :]) * scale
+            s2 = (k2c[b, nz[h], :L, :] @ q2[b, nz[h], :]) * scale
+            a = softmax_rows(s1) - lam * softmax_rows(s2)
+            o = a @ vc[b, kv[h], :L, :]
+            out[bi, h, :] = head_rms_norm(o, lambda_init, eps, w) if normalize else o
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Brute force: literal loops for tiny inputs (pins the vectorised oracle)
+# ---------------------------------------------------------------------------
+
+def brute_diff_attention(q1, q2, k1, k2, v, lam, lambda_init, *, eps=1e-5, causal=True,
+                         noise_of_signal=None, kv_of_signal=None, normalize=True):
+    """Pure-Python scalar loops over the same definition; only for N, d tiny."""
+    q1, q2, k1, k2, v = (_as64(t).tolist() for t in (q1, q2, k1, k2, v))
+    B, N, h_s, d = len(q1), len(q1[0]), len(q1[0][0]), len(q1[0][0][0])
+    h_n, h_kv, dv = len(q2[0][0]), len(k1[0][0]), len(v[0][0][0])
+    nz = [h // (h_s // h_n) for h in range(h_s)] if noise_of_signal is None else list(noise_of_signal)
+    kv = [h // (h_s // h_kv) for h in range(h_s)] if kv_of_signal is None else list(kv_of_signal)
+    out = [[[[0.0] * dv for _ in range(h_s)] for _ in range(N)] for _ in range(B)]
+    for b in range(B):
+        for h in range(h_s):
+            for i in range(N):
+                last = i if causal else N - 1
+                s1, s2 = [], []
+                for j in range(last + 1):
+                    t1 = 0.0
+                    t2 = 0.0
+                    for c in range(d):
+                        t1 += q1[b][i][h][c] * k1[b][j][kv[h]][c]
+                        t2 += q2[b][i][nz[h]][c] * k2[b][j][nz[h]][c]
+                    s1.append(t1 / math.sqrt(d))
+                    s2.append(t2 / math.sqrt(d))
+                e1 = [math.exp(x - max(s1)) for x in s1]
+                e2 = [math.exp(x - max(s2)) for x in s2]
+                z1, z2 = sum(e1), sum(e2)
+                o = [0.0] * dv
+                for j in range(last + 1):
+                    wgt = e1[j] / z1 - lam * e2[j] / z2
+                    for c in range(dv):
+                        o[c] += wgt * v[b][j][kv[h]][c]
+                if normalize:
+                    ms = sum(x * x for x in o) / dv
+                    o = [(1.0 - lambda_init) * x / math.sqrt(ms + eps) for x in o]
+                out[b][i][h] = o
+    return np.asarray(out, np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Work accounting used by the benchmark's roofline
+# ---------------------------------------------------------------------------
+
+def causal_pairs(B: int, N: int) -> int:
+    """Number of (query, key) pairs with key <= query: B * N (N + 1) / 2."""
+    return B * N * (N + 1) // 2
+
+
+def flops_alg(B, N, h_s, h_n, d, dv, causal=True) -> int:
+    """Products the DiffAttn equation names, each counted once: Q1K1^T per
+    signal head (2d per pair), Q2K2^T once per noise head (2d per pair), one
+    (A1 - lam A2) V per signal head (2 dv per pair)."""
+    pairs = causal_pairs(B, N) if causal else B * N * N
+    return pairs * (h_s * 2 * d + h_n * 2 * d + h_s * 2 * dv)
+
+
+def flops_exec(B, N, h_s, h_n, h_kv, d, dv, causal=True, noise_of_signal=None, kv_of_signal=None) -> int:
+    """flops_alg plus the second P.V an exact one-pass kernel must issue: one
+    more 2 dv per pair for every distinct (noise head, kv head) combination."""
+    nz, kv = _maps(h_s, h_n, h_kv, noise_of_signal, kv_of_signal)
+    distinct = len({(int(a), int(b)) for a, b in zip(nz, kv)})
+    pairs = causal_pairs(B, N) if causal else B * N * N
+    return flops_alg(B, N, h_s, h_n, d, dv, causal) + pairs * distinct * 2 * dv

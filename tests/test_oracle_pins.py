@@ -1,0 +1,282 @@
+"""CPU pins for the fp64 oracle: each checks it against something other than
+itself (library routines, closed forms, brute force, facts the pages fix).
+
+Pages cited (by title and section):
+* [DA-blog] "Differential Attention in Large Language Models: How Denoising
+  Subtraction Eliminates Attention Noise and Outlier Activations" (llms.blog).
+* [GDA] "Grouped Differential Attention" (mlsanity.com), "Abstract".
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import diffattn_oracle as O
+from differential_attention_diff_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def tiny(B=1, N=7, hs=2, hn=2, hkv=2, d=3, dv=4, seed=0):
+    return (rnd((B, N, hs, d), seed), rnd((B, N, hn, d), seed + 1), rnd((B, N, hkv, d), seed + 2),
+            rnd((B, N, hn, d), seed + 3), rnd((B, N, hkv, dv), seed + 4))
+
+
+def sdpa(q, k, v, causal):
+    """torch's scaled-dot-product attention in fp64, BSHD in/out, scale 1/sqrt(d)."""
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(np.transpose(x, (0, 2, 1, 3))))
+    d = q.shape[-1]
+    o = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=causal,
+                                                         scale=1.0 / math.sqrt(d))
+    return np.transpose(o.numpy(), (0, 2, 1, 3))
+
+
+def rms_torch(o, lam_init, eps):
+    x = torch.from_numpy(np.ascontiguousarray(o))
+    return (1 - lam_init) * torch.nn.functional.rms_norm(x, (o.shape[-1],), eps=eps).numpy()
+
+
+# --- brute force on tiny inputs ------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [
+    dict(B=1, N=5, hs=1, hn=1, hkv=1, d=2, dv=4),
+    dict(B=2, N=9, hs=2, hn=2, hkv=2, d=3, dv=6),
+    dict(B=1, N=8, hs=6, hn=2, hkv=6, d=4, dv=8),     # GDA 3:1
+    dict(B=1, N=6, hs=4, hn=1, hkv=2, d=2, dv=4),     # GDA 4:1 + GQA
+])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("normalize", [True, False])
+def test_blocked_equals_brute(shape, causal, normalize):
+    q1, q2, k1, k2, v = tiny(**shape, seed=11)
+    lam, li = 0.65, 0.3
+    a = O.diff_attention(q1, q2, k1, k2, v, lam, li, causal=causal, normalize=normalize, block=3)
+    b = O.brute_diff_attention(q1, q2, k1, k2, v, lam, li, causal=causal, normalize=normalize)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+def test_explicit_maps_equal_brute():
+    q1, q2, k1, k2, v = tiny(B=1, N=6, hs=4, hn=2, hkv=2, d=3, dv=4, seed=5)
+    nz, kv = [1, 0, 1, 0], [0, 0, 1, 1]
+    a = O.diff_attention(q1, q2, k1, k2, v, 0.4, 0.2, noise_of_signal=nz, kv_of_signal=kv)
+    b = O.brute_diff_attention(q1, q2, k1, k2, v, 0.4, 0.2, noise_of_signal=nz, kv_of_signal=kv)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)
+
+
+# --- worked example by hand (closed form) -------------------------------------------------
+
+def test_hand_worked_example():
+    # N=2, d=1 (scale 1), one head, dv=2.  Row 1: s1 = [0, ln 3] -> a1 = [1/4, 3/4];
+    # s2 = [0, 0] -> a2 = [1/2, 1/2]; lam = 1/2 -> weights [0, 1/2]; v1 = [3, -1] -> o = [1.5, -0.5].
+    # Row 0 sees key 0 only: o = (1 - lam) v0 = [0.5, 1].
+    q1 = np.array([0.7, 1.0]).reshape(1, 2, 1, 1)
+    k1 = np.array([0.0, math.log(3.0)]).reshape(1, 2, 1, 1)
+    q2 = np.array([-2.0, 1.0]).reshape(1, 2, 1, 1)
+    k2 = np.zeros((1, 2, 1, 1))
+    v = np.array([[1.0, 2.0], [3.0, -1.0]]).reshape(1, 2, 1, 2)
+    raw = O.diff_attention(q1, q2, k1, k2, v, 0.5, 0.0, normalize=False)[0, :, 0, :]
+    np.testing.assert_allclose(raw, [[0.5, 1.0], [1.5, -0.5]], rtol=0, atol=1e-15)
+    y = O.diff_attention(q1, q2, k1, k2, v, 0.5, 0.75, eps=0.0)[0, :, 0, :]
+    # mean(o^2): row 0 -> 0.625, row 1 -> 1.25; y = 0.25 * o / sqrt(mean)
+    np.testing.assert_allclose(y, 0.25 * np.array([[0.5, 1.0] / np.sqrt(0.625), [1.5, -0.5] / np.sqrt(1.25)]),
+                               rtol=1e-14)
+
+
+# --- lambda = 0 is standard attention ([DA-blog] standard attention vs DiffAttn equation) ----
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_lambda_zero_is_sdpa(causal):
+    q1, q2, k1, k2, v = tiny(B=2, N=33, hs=3, hn=3, hkv=3, d=8, dv=16, seed=2)
+    li, eps = 0.35, 1e-5
+    got = O.diff_attention(q1, q2, k1, k2, v, 0.0, li, eps=eps, causal=causal)
+    want = rms_torch(sdpa(q1, k1, v, causal), li, eps)
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-12)
+
+
+def test_stream2_is_sdpa():
+    # O(0) - O(1) = A2 V: pins the second map (its scale, mask and softmax)
+    q1, q2, k1, k2, v = tiny(B=1, N=40, hs=2, hn=2, hkv=2, d=8, dv=16, seed=3)
+    o0 = O.diff_attention(q1, q2, k1, k2, v, 0.0, 0.0, normalize=False)
+    o1 = O.diff_attention(q1, q2, k1, k2, v, 1.0, 0.0, normalize=False)
+    np.testing.assert_allclose(o0 - o1, sdpa(q2, k2, v, True), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("lam", [-0.5, 0.3, 0.8, 1.7])
+def test_affine_in_lambda(lam):
+    q1, q2, k1, k2, v = tiny(B=1, N=20, hs=2, hn=2, hkv=2, d=4, dv=8, seed=4)
+    f = lambda l: O.diff_attention(q1, q2, k1, k2, v, l, 0.0, normalize=False)
+    o0, o1 = f(0.0), f(1.0)
+    np.testing.assert_allclose(f(lam), o0 - lam * (o0 - o1), rtol=1e-11, atol=1e-12)
+
+
+# --- cancellation: identical maps with lambda = 1 give exactly zero ([DA-blog] DiffAttn) ----
+
+def test_identical_streams_cancel_exactly():
+    q1, _, k1, _, v = tiny(B=1, N=17, hs=2, hn=2, hkv=2, d=4, dv=8, seed=6)
+    raw = O.diff_attention(q1, q1, k1, k1, v, 1.0, 0.8, normalize=False)
+    assert np.all(raw == 0.0)
+    y = O.diff_attention(q1, q1, k1, k1, v, 1.0, 0.8)
+    assert np.all(y == 0.0)
+
+
+# --- row sums: each row of A1 - lam A2 sums to 1 - lam ([DA-blog] softmax sums to one) ----
+
+def test_row_sum_via_ones_channel():
+    q1, q2, k1, k2, v = tiny(B=1, N=25, hs=2, hn=2, hkv=2, d=4, dv=8, seed=7)
+    v[..., 3] = 1.0
+    lam = 0.83
+    raw = O.diff_attention(q1, q2, k1, k2, v, lam, 0.0, normalize=False)
+    np.testing.assert_allclose(raw[..., 3], 1.0 - lam, rtol=0, atol=1e-13)
+
+
+def test_all_ones_value_closed_form():
+    q1, q2, k1, k2, v = tiny(B=1, N=12, hs=2, hn=2, hkv=2, d=4, dv=8, seed=8)
+    v[:] = 1.0
+    lam, li, eps = 0.6, 0.25, 1e-5
+    y = O.diff_attention(q1, q2, k1, k2, v, lam, li, eps=eps)
+    want = (1 - li) * (1 - lam) / math.sqrt((1 - lam) ** 2 + eps)
+    np.testing.assert_allclose(y, want, rtol=1e-13)
+
+
+def test_row_zero_closed_form():
+    q1, q2, k1, k2, v = tiny(B=2, N=10, hs=3, hn=3, hkv=3, d=4, dv=8, seed=9)
+    lam = 0.42
+    raw = O.diff_attention(q1, q2, k1, k2, v, lam, 0.0, normalize=False)
+    np.testing.assert_allclose(raw[:, 0], (1 - lam) * v[:, 0], rtol=1e-14, atol=1e-15)
+
+
+# --- the max subtraction: large logits, key shift invariance -------------------------------
+
+def test_key_shift_invariance_large_logits():
+    rng = np.random.default_rng(10)
+    d = 8
+    grid = lambda shape, lo, hi: rng.integers(lo, hi + 1, shape) / 8.0  # dyadic, exact in bf16
+    q1 = grid((1, 16, 1, d), -16, 16)
+    k1 = grid((1, 16, 1, d), -16, 16)
+    q2, k2, v = grid((1, 16, 1, d), -8, 8), grid((1, 16, 1, d), -8, 8), grid((1, 16, 1, 2 * d), -8, 8)
+    u = np.full(d, 20.0)  # shifts each row of logits by q.u/sqrt(d), up to ~+-70
+    a = O.diff_attention(q1, q2, k1, k2, v, 0.7, 0.1)
+    b = O.diff_attention(q1, q2, k1 + u, k2, v, 0.7, 0.1)
+    assert np.max(np.abs(np.einsum("bnhd,d->bnh", q1, u))) / math.sqrt(d) > 50
+    assert np.all(np.isfinite(b))
+    np.testing.assert_allclose(a, b, rtol=1e-9, atol=1e-10)
+
+
+# --- the norm ([DA-blog] "Headwise Normalization") -----------------------------------------
+
+def test_head_norm_matches_torch_and_closed_form():
+    o = rnd((5, 3, 16), 12)
+    np.testing.assert_allclose(O.head_rms_norm(o, 0.3, 1e-5), rms_torch(o, 0.3, 1e-5), rtol=1e-13)
+    c = np.full((1, 16), -2.5)
+    np.testing.assert_allclose(O.head_rms_norm(c, 0.2, 1e-5), 0.8 * -2.5 / math.sqrt(6.25 + 1e-5), rtol=1e-14)
+    w = np.linspace(-1, 2, 16)
+    np.testing.assert_allclose(O.head_rms_norm(o, 0.3, 1e-5, w), rms_torch(o, 0.3, 1e-5) * w, rtol=1e-13)
+
+
+# --- GDA grouping ([GDA] "Abstract": noise heads repeated GQA-style) -----------------------
+
+def test_gda_with_equal_heads_is_plain_diff():
+    q1, q2, k1, k2, v = tiny(B=1, N=15, hs=4, hn=4, hkv=4, d=4, dv=8, seed=13)
+    a = O.diff_attention(q1, q2, k1, k2, v, 0.5, 0.2)
+    b = O.brute_diff_attention(q1, q2, k1, k2, v, 0.5, 0.2, noise_of_signal=range(4), kv_of_signal=range(4))
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("hs,hn,hkv", [(6, 2, 6), (8, 2, 4), (4, 1, 1)])
+def test_gda_equals_repeated_plain_diff(hs, hn, hkv):
+    q1, q2, k1, k2, v = tiny(B=2, N=13, hs=hs, hn=hn, hkv=hkv, d=4, dv=8, seed=14)
+    a = O.diff_attention(q1, q2, k1, k2, v, 0.7, 0.7)
+    rep = lambda x, g: np.repeat(x, g, axis=2)  # repeat_interleave along heads
+    b = O.diff_attention(q1, rep(q2, hs // hn), rep(k1, hs // hkv), rep(k2, hs // hn), rep(v, hs // hkv), 0.7, 0.7)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
+    t = torch.from_numpy
+    np.testing.assert_array_equal(rep(q2, hs // hn), t(q2).repeat_interleave(hs // hn, dim=2).numpy())
+
+
+# --- lambda scalars ([DA-blog] "Learnable Lambda Re-parameterization") ----------------------
+
+def test_lambda_init_schedule_golden():
+    with open(os.path.join(GOLDEN, "lambda_init_schedule.json")) as f:
+        g = json.load(f)
+    assert O.lambda_init_schedule(g["first_layer"]) == pytest.approx(g["value_at_first_layer"], abs=1e-15)
+    assert O.lambda_init_schedule(200) == pytest.approx(g["deep_layer_limit"], abs=1e-12)
+    vals = [O.lambda_init_schedule(l) for l in range(1, 40)]
+    assert all(b > a for a, b in zip(vals, vals[1:]))
+    # the 3B-like workload's constants come from layer 12 of this schedule
+    assert W.LAMBDA_INIT_L12 == pytest.approx(O.lambda_init_schedule(12), abs=1e-15)
+
+
+def test_lambda_reparam():
+    assert O.lambda_reparam([0, 0], [1, 1], [0, 0], [2, 2], 0.8) == pytest.approx(0.8)
+    assert O.lambda_reparam([1.0], [0.5], [0.0], [0.0], 0.2) == pytest.approx(math.exp(0.5) - 1 + 0.2)
+
+
+# --- decode is the last row of the prefill --------------------------------------------------
+
+def test_decode_is_last_prefill_row():
+    B, L, hs, hn, hkv, d, dv = 3, 11, 6, 2, 2, 4, 8
+    q1, q2, k1, k2, v = tiny(B=B, N=L, hs=hs, hn=hn, hkv=hkv, d=d, dv=dv, seed=15)
+    lens = np.array([11, 5, 1])
+    t = lambda x: np.transpose(x, (0, 2, 1, 3))  # BSHD -> cache layout [B,H,L,D]
+    for b in range(B):
+        Lb = lens[b]
+        pre = O.diff_attention_rows(q1, q2, k1, k2, v, 0.6, 0.4, rows=[Lb - 1], batches=[b])[0, 0]
+        # the decode query is the prefill query at position Lb-1; it sees cache positions 0..Lb-1
+        dec = O.gda_decode(q1[:, Lb - 1], q2[:, Lb - 1], t(k1), t(k2), t(v), lens, 0.6, 0.4, batches=[b])[0]
+        np.testing.assert_allclose(dec, pre, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_empty_sequence_is_zero():
+    q1, q2, k1, k2, v = tiny(B=2, N=4, hs=2, hn=1, hkv=1, d=2, dv=4, seed=16)
+    t = lambda x: np.transpose(x, (0, 2, 1, 3))
+    out = O.gda_decode(q1[:, 0], q2[:, 0], t(k1), t(k2), t(v), [0, 4], 0.5, 0.5)
+    assert np.all(out[0] == 0.0) and np.all(np.isfinite(out[1])) and np.any(out[1] != 0)
+
+
+def test_rows_subset_matches_full():
+    q1, q2, k1, k2, v = tiny(B=2, N=30, hs=4, hn=2, hkv=2, d=4, dv=8, seed=17)
+    full = O.diff_attention(q1, q2, k1, k2, v, 0.9, 0.1)
+    rows = [29, 0, 17, 3]
+    sub = O.diff_attention_rows(q1, q2, k1, k2, v, 0.9, 0.1, rows=rows, heads=[3, 1], batches=[1])
+    np.testing.assert_array_equal(sub[0], full[1][rows][:, [3, 1]])
+
+
+# --- work accounting (used by the roofline) -------------------------------------------------
+
+def test_flop_counts_by_enumeration():
+    B, N = 2, 9
+    pairs = sum(1 for _ in range(B) for i in range(N) for j in range(i + 1))
+    assert O.causal_pairs(B, N) == pairs
+    # 3:1 GDA, d=4, dv=8: per pair 6 QK1 + 2 QK2 (2d each) + 6 PV (2dv) = 64 + 96 = 160; exec adds 6 PV
+    assert O.flops_alg(B, N, 6, 2, 4, 8) == pairs * 160
+    assert O.flops_exec(B, N, 6, 2, 6, 4, 8) == pairs * (160 + 6 * 16)
+    # the 3B-like workload figure quoted alongside the bench
+    assert O.flops_alg(4, 4096, 24, 24, 64, 128) == 33562624 * 24 * 512
+
+
+# --- the pins catch plausible mistakes (mistakes planted in the oracle, on the CPU) ---------
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    q1, q2, k1, k2, v = tiny(B=1, N=33, hs=2, hn=2, hkv=2, d=8, dv=16, seed=2)
+    want = rms_torch(sdpa(q1, k1, v, True), 0.35, 1e-5)
+
+    def check():
+        got = O.diff_attention(q1, q2, k1, k2, v, 0.0, 0.35, eps=1e-5)
+        return np.allclose(got, want, rtol=1e-9, atol=1e-10)
+
+    assert check()
+    real_softmax = O.softmax_rows
+    monkeypatch.setattr(O, "softmax_rows", lambda s: real_softmax(s * math.sqrt(0.5)))  # 1/sqrt(2d) scale
+    assert not check()
+    monkeypatch.setattr(O, "softmax_rows", real_softmax)
+    real_norm = O.head_rms_norm
+    monkeypatch.setattr(O, "head_rms_norm", lambda o, li, eps, w=None: real_norm(o - o.mean(-1, keepdims=True), li, eps, w))
+    assert not check()  # mean-centred GroupNorm instead of RMS
