@@ -1,0 +1,346 @@
+// C-ABI layer of libdiffattn.so: argument validation (pure host code, run
+// before any HIP call), head-map resolution and kernel dispatch.
+//
+// The operations and their arguments follow "Differential Attention in Large
+// Language Models: How Denoising Subtraction Eliminates Attention Noise and
+// Outlier Activations" (llms.blog), sections "Differential Attention
+// Architecture" (Q1/Q2, K1/K2 of width d, V of width 2d, the DiffAttn
+// equation), "Learnable Lambda Re-parameterization" and "Headwise
+// Normalization", and the head grouping of "Grouped Differential Attention"
+// (mlsanity.com), "Abstract".
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+da_status fail(da_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+da_status fail(da_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+da_status hip_fail(hipError_t e, const char* what) {
+  return fail(DA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Byte extent [lo, hi) of a strided tensor whose last dim is contiguous.
+struct Extent {
+  uintptr_t lo, hi;
+};
+
+Extent extent(const void* p, const int64_t* dims, const int64_t* strides, int nlead, int64_t last, int esize) {
+  int64_t maxoff = last - 1;
+  for (int i = 0; i < nlead; ++i) maxoff += (dims[i] - 1) * strides[i];
+  return {(uintptr_t)p, (uintptr_t)p + (uintptr_t)((maxoff + 1) * esize)};
+}
+
+bool overlaps(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
+
+da_status check_strides(const char* name, const void* p, const int64_t* s, int n, int esize) {
+  if (!p) return fail(DA_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(DA_EINVAL, "%s is not 16-byte aligned", name);
+  for (int i = 0; i < n; ++i) {
+    if (s[i] < 0) return fail(DA_EINVAL, "%s has a negative stride", name);
+    if ((s[i] * esize) % 16 != 0) return fail(DA_EINVAL, "%s stride %d (%lld elements) is not a multiple of 16 bytes",
+                                              name, i, (long long)s[i]);
+  }
+  return DA_OK;
+}
+
+// Resolve and check the head maps.  Each noise head must serve exactly g
+// signal heads and each kv head exactly H_s/H_kv (GQA-style repetition).
+da_status resolve_maps(int Hs, int Hn, int Hkv, const int32_t* nzmap, const int32_t* kvmap, int16_t* nz,
+                       int16_t* kv, int16_t* members) {
+  const int g = Hs / Hn, gk = Hs / Hkv;
+  int cnt_n[DA_MAX_HEADS] = {0}, cnt_k[DA_MAX_HEADS] = {0};
+  for (int h = 0; h < Hs; ++h) {
+    int n = nzmap ? nzmap[h] : h / g;
+    int k = kvmap ? kvmap[h] : h / gk;
+    if (n < 0 || n >= Hn) return fail(DA_EINVAL, "noise_of_signal[%d] = %d out of [0, %d)", h, n, Hn);
+    if (k < 0 || k >= Hkv) return fail(DA_EINVAL, "kv_of_signal[%d] = %d out of [0, %d)", h, k, Hkv);
+    nz[h] = (int16_t)n;
+    kv[h] = (int16_t)k;
+    cnt_n[n]++;
+    cnt_k[k]++;
+  }
+  for (int n = 0; n < Hn; ++n)
+    if (cnt_n[n] != g) return fail(DA_EINVAL, "noise head %d serves %d signal heads, expected %d", n, cnt_n[n], g);
+  for (int k = 0; k < Hkv; ++k)
+    if (cnt_k[k] != gk) return fail(DA_EINVAL, "kv head %d serves %d signal heads, expected %d", k, cnt_k[k], gk);
+  int fill[DA_MAX_HEADS] = {0};
+  for (int h = 0; h < Hs; ++h) {
+    int n = nz[h];
+    members[n * g + fill[n]++] = (int16_t)h;
+  }
+  return DA_OK;
+}
+
+da_status check_common_shapes(int64_t B, int64_t N, int64_t Hs, int64_t Hn, int64_t Hkv, int64_t d, int64_t dv,
+                              int32_t dtype, float lam, float lam_init, float eps) {
+  if (dtype != DA_F32 && dtype != DA_BF16) return fail(DA_EINVAL, "unknown dtype %d", (int)dtype);
+  if (B < 0 || N < 0) return fail(DA_EINVAL, "negative batch or length");
+  if (B > INT32_MAX || N > INT32_MAX) return fail(DA_EINVAL, "batch or length exceeds int32");
+  if (Hs < 1 || Hn < 1 || Hkv < 1) return fail(DA_EINVAL, "head counts must be >= 1");
+  if (Hs > DA_MAX_HEADS) return fail(DA_EINVAL, "H_s = %lld exceeds %d", (long long)Hs, DA_MAX_HEADS);
+  if (Hs % Hn != 0) return fail(DA_EINVAL, "H_s (%lld) is not a multiple of H_n (%lld)", (long long)Hs, (long long)Hn);
+  if (Hs % Hkv != 0)
+    return fail(DA_EINVAL, "H_s (%lld) is not a multiple of H_kv (%lld)", (long long)Hs, (long long)Hkv);
+  if (dv != 2 * d) return fail(DA_EINVAL, "dv (%lld) must equal 2*d (d = %lld)", (long long)dv, (long long)d);
+  if (d != 32 && d != 64) return fail(DA_EUNSUPPORTED, "d = %lld: kernels exist for d in {32, 64}", (long long)d);
+  if (!isfinite(lam) || !isfinite(lam_init)) return fail(DA_EINVAL, "lambda and lambda_init must be finite");
+  if (!(eps >= 0.0f) || !isfinite(eps)) return fail(DA_EINVAL, "eps must be finite and >= 0");
+  return DA_OK;
+}
+
+da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain) {
+  if (!a) return fail(DA_EINVAL, "args is NULL");
+  da_status st = check_common_shapes(a->B, a->N, a->H_s, a->H_n, a->H_kv, a->d, a->dv, a->dtype, a->lambda,
+                                     a->lambda_init, a->eps);
+  if (st != DA_OK) return st;
+  if (a->flags & ~(uint32_t)(DA_CAUSAL | DA_NO_NORM)) return fail(DA_EINVAL, "unknown flag bits 0x%x", a->flags);
+  if (plain) {
+    if (a->H_n != a->H_s || a->H_kv != a->H_s)
+      return fail(DA_EINVAL, "diffattn_fwd needs H_n == H_kv == H_s (use gda_fwd for grouped heads)");
+    if (a->noise_of_signal || a->kv_of_signal) return fail(DA_EINVAL, "diffattn_fwd takes no head maps");
+  }
+  const int es = a->dtype == DA_BF16 ? 2 : 4;
+  struct T {
+    const char* name;
+    const void* p;
+    const int64_t* s;
+    int64_t heads, last;
+  } ts[6] = {{"q1", a->q1, a->s_q1, a->H_s, a->d},   {"q2", a->q2, a->s_q2, a->H_n, a->d},
+             {"k1", a->k1, a->s_k1, a->H_kv, a->d},  {"k2", a->k2, a->s_k2, a->H_n, a->d},
+             {"v", a->v, a->s_v, a->H_kv, a->dv},    {"out", a->out, a->s_out, a->H_s, a->dv}};
+  for (auto& t : ts)
+    if ((st = check_strides(t.name, t.p, t.s, 3, es)) != DA_OK) return st;
+  if (a->norm_w && ((uintptr_t)a->norm_w & 3u)) return fail(DA_EINVAL, "norm_w is not 4-byte aligned");
+  if (a->lse && ((uintptr_t)a->lse & 3u)) return fail(DA_EINVAL, "lse is not 4-byte aligned");
+
+  da::FwdParams p;
+  memset(&p, 0, sizeof p);
+  if ((st = resolve_maps((int)a->H_s, (int)a->H_n, (int)a->H_kv, a->noise_of_signal, a->kv_of_signal, p.nz, p.kv,
+                         p.members)) != DA_OK)
+    return st;
+  if (a->B == 0 || a->N == 0) return DA_OK;
+
+  Extent eo;
+  {
+    int64_t dims[3] = {a->B, a->N, a->H_s};
+    eo = extent(a->out, dims, a->s_out, 3, a->dv, es);
+  }
+  for (int i = 0; i < 5; ++i) {
+    int64_t dims[3] = {a->B, a->N, ts[i].heads};
+    if (overlaps(eo, extent(ts[i].p, dims, ts[i].s, 3, ts[i].last, es)))
+      return fail(DA_EINVAL, "out overlaps %s", ts[i].name);
+  }
+  if (a->lse) {
+    Extent el{(uintptr_t)a->lse, (uintptr_t)(a->lse + 2 * a->B * a->H_s * a->N)};
+    if (overlaps(el, eo)) return fail(DA_EINVAL, "lse overlaps out");
+    for (int i = 0; i < 5; ++i) {
+      int64_t dims[3] = {a->B, a->N, ts[i].heads};
+      if (overlaps(el, extent(ts[i].p, dims, ts[i].s, 3, ts[i].last, es)))
+        return fail(DA_EINVAL, "lse overlaps %s", ts[i].name);
+    }
+  }
+
+  p.q1 = a->q1;
+  p.q2 = a->q2;
+  p.k1 = a->k1;
+  p.k2 = a->k2;
+  p.v = a->v;
+  p.out = a->out;
+  p.norm_w = a->norm_w;
+  p.lse = a->lse;
+  for (int i = 0; i < 3; ++i) {
+    p.sq1[i] = a->s_q1[i];
+    p.sq2[i] = a->s_q2[i];
+    p.sk1[i] = a->s_k1[i];
+    p.sk2[i] = a->s_k2[i];
+    p.sv[i] = a->s_v[i];
+    p.so[i] = a->s_out[i];
+  }
+  p.B = (int)a->B;
+  p.N = (int)a->N;
+  p.Hs = (int)a->H_s;
+  p.Hn = (int)a->H_n;
+  p.Hkv = (int)a->H_kv;
+  p.d = (int)a->d;
+  p.dv = (int)a->dv;
+  p.g = (int)(a->H_s / a->H_n);
+  p.causal = (a->flags & DA_CAUSAL) ? 1 : 0;
+  p.normalize = (a->flags & DA_NO_NORM) ? 0 : 1;
+  p.lam = a->lambda;
+  p.lam_init = a->lambda_init;
+  p.eps = a->eps;
+  p.sm_scale = (float)(1.0 / sqrt((double)a->d));
+  p.sm_scale_log2 = (float)(1.4426950408889634 / sqrt((double)a->d));
+
+  hipError_t e = a->dtype == DA_BF16 ? da::launch_fwd_bf16(p, (hipStream_t)stream)
+                                     : da::launch_fwd_f32(p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return DA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// decode
+// ---------------------------------------------------------------------------
+
+constexpr int kDefaultChunk = 512;
+constexpr int kMaxChunk = 2048;
+constexpr int kDecodeMaxQueries = 8;  // g + 1 scored queries per noise group
+
+da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p) {
+  if (!a) return fail(DA_EINVAL, "args is NULL");
+  da_status st = check_common_shapes(a->B, a->Lmax, a->H_s, a->H_n, a->H_kv, a->d, a->dv, a->dtype, a->lambda,
+                                     a->lambda_init, a->eps);
+  if (st != DA_OK) return st;
+  if (a->dtype != DA_BF16) return fail(DA_EUNSUPPORTED, "gda_decode has a bf16 kernel only");
+  if (a->d != 64) return fail(DA_EUNSUPPORTED, "gda_decode has a d = 64 kernel only");
+  if (a->flags & ~(uint32_t)DA_NO_NORM) return fail(DA_EINVAL, "gda_decode accepts only DA_NO_NORM");
+  if (a->chunk < 0 || a->chunk % 64 != 0) return fail(DA_EINVAL, "chunk must be 0 or a positive multiple of 64");
+  if (a->chunk > kMaxChunk) return fail(DA_EUNSUPPORTED, "chunk %lld exceeds %d", (long long)a->chunk, kMaxChunk);
+  if (a->H_s / a->H_n + 1 > kDecodeMaxQueries)
+    return fail(DA_EUNSUPPORTED, "gda_decode supports up to %d signal heads per noise head", kDecodeMaxQueries - 1);
+  const int es = 2;
+  struct T {
+    const char* name;
+    const void* p;
+    const int64_t* s;
+    int nlead;
+  } ts[6] = {{"q1", a->q1, a->s_q1, 2},       {"q2", a->q2, a->s_q2, 2},       {"k1_cache", a->k1_cache, a->s_k1, 3},
+             {"k2_cache", a->k2_cache, a->s_k2, 3}, {"v_cache", a->v_cache, a->s_v, 3}, {"out", a->out, a->s_out, 2}};
+  for (auto& t : ts)
+    if ((st = check_strides(t.name, t.p, t.s, t.nlead, es)) != DA_OK) return st;
+  if (!a->seq_lens) return fail(DA_EINVAL, "seq_lens is NULL");
+  if ((uintptr_t)a->seq_lens & 3u) return fail(DA_EINVAL, "seq_lens is not 4-byte aligned");
+  if (a->norm_w && ((uintptr_t)a->norm_w & 3u)) return fail(DA_EINVAL, "norm_w is not 4-byte aligned");
+
+  memset(p, 0, sizeof *p);
+  int16_t nz[DA_MAX_HEADS];
+  if ((st = resolve_maps((int)a->H_s, (int)a->H_n, (int)a->H_kv, a->noise_of_signal, a->kv_of_signal, nz, p->kv,
+                         p->members)) != DA_OK)
+    return st;
+  const int Hs = (int)a->H_s, Hn = (int)a->H_n, g = Hs / Hn;
+  int umax = 0;
+  for (int n = 0; n < Hn; ++n) {
+    int u = 0;
+    for (int j = 0; j < g; ++j) {
+      int h = p->members[n * g + j];
+      int k = p->kv[h], idx = -1;
+      for (int t = 0; t < u; ++t)
+        if (p->ukv[n * g + t] == k) idx = t;
+      if (idx < 0) {
+        idx = u;
+        p->ukv[n * g + u++] = (int16_t)k;
+      }
+      p->uidx[h] = (int16_t)idx;
+    }
+    p->nu[n] = (int16_t)u;
+    umax = std::max(umax, u);
+  }
+  int64_t chunk = a->chunk ? a->chunk : kDefaultChunk;
+  int64_t lmax_r = (a->Lmax + 63) / 64 * 64;
+  if (chunk > lmax_r) chunk = std::max<int64_t>(64, lmax_r);
+  p->chunk = (int)chunk;
+  p->nchunks = (int)((a->Lmax + chunk - 1) / chunk);
+  p->slots = g + umax;
+  p->q1 = a->q1;
+  p->q2 = a->q2;
+  p->k1 = a->k1_cache;
+  p->k2 = a->k2_cache;
+  p->v = a->v_cache;
+  p->seq_lens = a->seq_lens;
+  p->out = a->out;
+  p->norm_w = a->norm_w;
+  for (int i = 0; i < 2; ++i) {
+    p->sq1[i] = a->s_q1[i];
+    p->sq2[i] = a->s_q2[i];
+    p->so[i] = a->s_out[i];
+  }
+  for (int i = 0; i < 3; ++i) {
+    p->sk1[i] = a->s_k1[i];
+    p->sk2[i] = a->s_k2[i];
+    p->sv[i] = a->s_v[i];
+  }
+  p->B = (int)a->B;
+  p->Lmax = (int)a->Lmax;
+  p->Hs = Hs;
+  p->Hn = Hn;
+  p->Hkv = (int)a->H_kv;
+  p->d = (int)a->d;
+  p->dv = (int)a->dv;
+  p->g = g;
+  p->normalize = (a->flags & DA_NO_NORM) ? 0 : 1;
+  p->lam = a->lambda;
+  p->lam_init = a->lambda_init;
+  p->eps = a->eps;
+  p->sm_scale_log2 = (float)(1.4426950408889634 / sqrt((double)a->d));
+  return DA_OK;
+}
+
+size_t decode_ws_bytes(const da::DecodeParams& p) {
+  return (size_t)p.B * p.Hn * p.nchunks * da::decode_ws_floats_per_chunk(p.slots, p.dv) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+da_status diffattn_fwd(const da_fwd_args* args, void* stream) { return fwd_impl(args, stream, true); }
+
+da_status gda_fwd(const da_fwd_args* args, void* stream) { return fwd_impl(args, stream, false); }
+
+size_t gda_decode_workspace_bytes(const da_decode_args* args) {
+  da::DecodeParams p;
+  if (decode_prepare(args, &p) != DA_OK) return 0;
+  return decode_ws_bytes(p);
+}
+
+da_status gda_decode(const da_decode_args* args, void* workspace, size_t workspace_bytes, void* stream) {
+  da::DecodeParams p;
+  da_status st = decode_prepare(args, &p);
+  if (st != DA_OK) return st;
+  if (p.B == 0) return DA_OK;  // Lmax == 0 still launches: every output row is zero
+  const size_t need = decode_ws_bytes(p);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(DA_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace ? workspace_bytes : (size_t)0);
+  if (workspace && ((uintptr_t)workspace & 15u)) return fail(DA_EINVAL, "workspace is not 16-byte aligned");
+  p.ws = (float*)workspace;
+  hipError_t e = da::launch_decode(p, args->dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return DA_OK;
+}
+
+const char* da_status_str(int status) {
+  switch (status) {
+    case DA_OK: return "DA_OK: success";
+    case DA_EINVAL: return "DA_EINVAL: invalid argument";
+    case DA_EUNSUPPORTED: return "DA_EUNSUPPORTED: no kernel for this request";
+    case DA_EHIP: return "DA_EHIP: HIP runtime or launch failure";
+    case DA_EWORKSPACE: return "DA_EWORKSPACE: workspace missing or too small";
+    default: return "unknown status";
+  }
+}
+
+const char* da_last_error(void) { return g_last_error.c_str(); }
+
+int da_abi_version(void) { return DA_ABI_VERSION; }
+
+}  // extern "C"

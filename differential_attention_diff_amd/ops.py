@@ -1,0 +1,224 @@
+"""Python binding of libdiffattn.so (ctypes): argument marshalling only.
+
+Every step of the computation runs in the library's HIP kernels; this module
+turns torch tensors into device pointers, element strides and the current HIP
+stream, and raises if the library is missing or returns an error.  Entry
+points mirror the C ABI: ``diffattn_fwd``, ``gda_fwd``, ``gda_decode`` (plus
+``gda_decode_workspace_bytes``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdiffattn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "diffattn.h")
+
+DA_OK, DA_EINVAL, DA_EUNSUPPORTED, DA_EHIP, DA_EWORKSPACE = range(5)
+DA_F32, DA_BF16 = 0, 1
+DA_CAUSAL, DA_NO_NORM = 1, 2
+
+_i64x3 = ctypes.c_int64 * 3
+_i64x2 = ctypes.c_int64 * 2
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("q1", ctypes.c_void_p), ("q2", ctypes.c_void_p), ("k1", ctypes.c_void_p), ("k2", ctypes.c_void_p),
+        ("v", ctypes.c_void_p), ("out", ctypes.c_void_p),
+        ("B", ctypes.c_int64), ("N", ctypes.c_int64), ("H_s", ctypes.c_int64), ("H_n", ctypes.c_int64),
+        ("H_kv", ctypes.c_int64), ("d", ctypes.c_int64), ("dv", ctypes.c_int64),
+        ("s_q1", _i64x3), ("s_q2", _i64x3), ("s_k1", _i64x3), ("s_k2", _i64x3), ("s_v", _i64x3),
+        ("s_out", _i64x3),
+        ("noise_of_signal", ctypes.POINTER(ctypes.c_int32)), ("kv_of_signal", ctypes.POINTER(ctypes.c_int32)),
+        ("lambda_", ctypes.c_float), ("lambda_init", ctypes.c_float), ("eps", ctypes.c_float),
+        ("norm_w", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+    ]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("q1", ctypes.c_void_p), ("q2", ctypes.c_void_p), ("k1_cache", ctypes.c_void_p),
+        ("k2_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("B", ctypes.c_int64), ("Lmax", ctypes.c_int64), ("H_s", ctypes.c_int64), ("H_n", ctypes.c_int64),
+        ("H_kv", ctypes.c_int64), ("d", ctypes.c_int64), ("dv", ctypes.c_int64), ("chunk", ctypes.c_int64),
+        ("s_q1", _i64x2), ("s_q2", _i64x2), ("s_out", _i64x2),
+        ("s_k1", _i64x3), ("s_k2", _i64x3), ("s_v", _i64x3),
+        ("noise_of_signal", ctypes.POINTER(ctypes.c_int32)), ("kv_of_signal", ctypes.POINTER(ctypes.c_int32)),
+        ("lambda_", ctypes.c_float), ("lambda_init", ctypes.c_float), ("eps", ctypes.c_float),
+        ("norm_w", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+    ]
+
+
+class DiffAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{status_str(status)} -- {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdiffattn.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m differential_attention_diff_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.diffattn_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
+        L.gda_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
+        L.diffattn_fwd.restype = L.gda_fwd.restype = ctypes.c_int
+        L.gda_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
+        L.gda_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.gda_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.gda_decode.restype = ctypes.c_int
+        L.da_status_str.argtypes = [ctypes.c_int]
+        L.da_status_str.restype = ctypes.c_char_p
+        L.da_last_error.argtypes = []
+        L.da_last_error.restype = ctypes.c_char_p
+        L.da_abi_version.argtypes = []
+        L.da_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/diffattn.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\([^;]*\)\s*;", text, flags=re.M)
+
+
+def status_str(status: int) -> str:
+    return lib().da_status_str(status).decode()
+
+
+def last_error() -> str:
+    return lib().da_last_error().decode()
+
+
+def _check(status: int):
+    if status != DA_OK:
+        raise DiffAttnError(status, last_error())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DA_BF16
+    if t.dtype == torch.float32:
+        return DA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _map(m, hs):
+    if m is None:
+        return None, None
+    arr = (ctypes.c_int32 * hs)(*[int(x) for x in m])
+    return ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), arr
+
+
+def _lead(t: torch.Tensor, k: int):
+    if t.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    return [int(s) for s in t.stride()[:k]]
+
+
+def fwd_args(q1, q2, k1, k2, v, out, lam, lam_init, *, eps=1e-5, norm_weight=None, causal=True, normalize=True,
+             noise_of_signal=None, kv_of_signal=None, lse=None):
+    """Fill the C argument struct from BSHD tensors (returns (args, keepalive))."""
+    B, N, hs, d = q1.shape
+    a = FwdArgs()
+    a.q1, a.q2, a.k1, a.k2, a.v, a.out = (t.data_ptr() for t in (q1, q2, k1, k2, v, out))
+    a.B, a.N, a.H_s, a.H_n, a.H_kv, a.d, a.dv = B, N, hs, q2.shape[2], k1.shape[2], d, v.shape[3]
+    a.s_q1[:], a.s_q2[:], a.s_k1[:] = _lead(q1, 3), _lead(q2, 3), _lead(k1, 3)
+    a.s_k2[:], a.s_v[:], a.s_out[:] = _lead(k2, 3), _lead(v, 3), _lead(out, 3)
+    nz, nz_keep = _map(noise_of_signal, hs)
+    kv, kv_keep = _map(kv_of_signal, hs)
+    a.noise_of_signal, a.kv_of_signal = nz, kv
+    a.lambda_, a.lambda_init, a.eps = float(lam), float(lam_init), float(eps)
+    a.norm_w = None if norm_weight is None else norm_weight.data_ptr()
+    a.lse = None if lse is None else lse.data_ptr()
+    a.dtype = _dtype_code(q1)
+    a.flags = (DA_CAUSAL if causal else 0) | (0 if normalize else DA_NO_NORM)
+    return a, (nz_keep, kv_keep)
+
+
+def _fwd(entry, q1, q2, k1, k2, v, lam, lam_init, out=None, stream=None, **kw):
+    if out is None:
+        out = torch.empty(q1.shape[:3] + (v.shape[3],), dtype=q1.dtype, device=q1.device)
+    a, keep = fwd_args(q1, q2, k1, k2, v, out, lam, lam_init, **kw)
+    _check(entry(ctypes.byref(a), _stream(stream)))
+    del keep
+    return out
+
+
+def diffattn_fwd(q1, q2, k1, k2, v, lam, lam_init, *, out=None, stream=None, **kw):
+    """Plain differential attention forward (H_n = H_kv = H_s); see include/diffattn.h."""
+    return _fwd(lib().diffattn_fwd, q1, q2, k1, k2, v, lam, lam_init, out=out, stream=stream, **kw)
+
+
+def gda_fwd(q1, q2, k1, k2, v, lam, lam_init, *, out=None, stream=None, **kw):
+    """Grouped differential attention forward; see include/diffattn.h."""
+    return _fwd(lib().gda_fwd, q1, q2, k1, k2, v, lam, lam_init, out=out, stream=stream, **kw)
+
+
+def decode_args(q1, q2, k1c, k2c, vc, seq_lens, out, lam, lam_init, *, eps=1e-5, norm_weight=None, normalize=True,
+                chunk=0, noise_of_signal=None, kv_of_signal=None):
+    B, hs, d = q1.shape
+    a = DecodeArgs()
+    a.q1, a.q2, a.k1_cache, a.k2_cache, a.v_cache = (t.data_ptr() for t in (q1, q2, k1c, k2c, vc))
+    a.seq_lens = seq_lens.data_ptr()
+    a.out = 0 if out is None else out.data_ptr()
+    a.B, a.Lmax, a.H_s, a.H_n, a.H_kv, a.d, a.dv = B, k1c.shape[2], hs, q2.shape[1], k1c.shape[1], d, vc.shape[3]
+    a.chunk = int(chunk)
+    a.s_q1[:], a.s_q2[:] = _lead(q1, 2), _lead(q2, 2)
+    a.s_out[:] = [hs * vc.shape[3], vc.shape[3]] if out is None else _lead(out, 2)
+    a.s_k1[:], a.s_k2[:], a.s_v[:] = _lead(k1c, 3), _lead(k2c, 3), _lead(vc, 3)
+    nz, nz_keep = _map(noise_of_signal, hs)
+    kv, kv_keep = _map(kv_of_signal, hs)
+    a.noise_of_signal, a.kv_of_signal = nz, kv
+    a.lambda_, a.lambda_init, a.eps = float(lam), float(lam_init), float(eps)
+    a.norm_w = None if norm_weight is None else norm_weight.data_ptr()
+    a.dtype = _dtype_code(q1)
+    a.flags = 0 if normalize else DA_NO_NORM
+    return a, (nz_keep, kv_keep)
+
+
+def gda_decode_workspace_bytes(q1, q2, k1c, k2c, vc, seq_lens, **kw) -> int:
+    a, keep = decode_args(q1, q2, k1c, k2c, vc, seq_lens, None, 0.0, 0.0,
+                          **{k: v for k, v in kw.items() if k not in ("lam", "lam_init")})
+    return int(lib().gda_decode_workspace_bytes(ctypes.byref(a)))
+
+
+def gda_decode(q1, q2, k1c, k2c, vc, seq_lens, lam, lam_init, *, out=None, workspace=None, stream=None, **kw):
+    """Split-K GDA decode; caches [B,H,Lmax,D]; see include/diffattn.h."""
+    if out is None:
+        out = torch.empty((q1.shape[0], q1.shape[1], vc.shape[3]), dtype=q1.dtype, device=q1.device)
+    a, keep = decode_args(q1, q2, k1c, k2c, vc, seq_lens, out, lam, lam_init, **kw)
+    need = int(lib().gda_decode_workspace_bytes(ctypes.byref(a)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
+    _check(lib().gda_decode(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                            _stream(stream)))
+    del keep
+    return out

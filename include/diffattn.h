@@ -1,0 +1,169 @@
+/*
+ * diffattn.h -- C ABI of libdiffattn.so: fused causal differential attention
+ * and Grouped Differential Attention (GDA) on AMD Instinct MI355X (gfx950).
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [DA-blog] "Differential Attention in Large Language Models: How Denoising
+ *             Subtraction Eliminates Attention Noise and Outlier Activations"
+ *             (llms.blog): "Differential Attention Architecture" (the
+ *             projections into Q1/Q2, K1/K2 halves of width d and V of width
+ *             2d, and the DiffAttn equation), "Learnable Lambda
+ *             Re-parameterization" (lambda, lambda_init), "Headwise
+ *             Normalization" (head_bar_i = (1 - lambda_init) RMSNorm(head_i)).
+ *   [GDA]     "Grouped Differential Attention" (mlsanity.com), "Abstract":
+ *             more signal heads than noise-control heads, the noise heads
+ *             repeated the way GQA repeats key/value heads.
+ *
+ * Per signal head h, query i and visible keys j (j <= i when causal):
+ *   A1 = softmax_j(Q1[i,h] . K1[j,kv(h)] / sqrt(d))
+ *   A2 = softmax_j(Q2[i,nz(h)] . K2[j,nz(h)] / sqrt(d))
+ *   o  = sum_j (A1_j - lambda A2_j) V[j,kv(h)]                       [DA-blog] DiffAttn
+ *   out[i,h,:] = (1 - lambda_init) * w * o / sqrt(mean_c(o_c^2) + eps) [DA-blog] head_bar_i
+ * with nz(h) = h / (H_s/H_n) and kv(h) = h / (H_s/H_kv) unless explicit maps
+ * are given.  Plain differential attention is H_n = H_kv = H_s.
+ *
+ * Conventions shared by every entry point
+ *   Memory   All tensor pointers are DEVICE pointers owned by the caller.  The
+ *            library never allocates or frees device memory and keeps no
+ *            state between calls.  Head maps are HOST arrays read during the
+ *            call.  Outputs must not overlap inputs.
+ *   Layout   Element strides (not bytes) for the listed leading dims; the last
+ *            dim is contiguous (stride 1).  Every row start must be 16-byte
+ *            aligned (pointer % 16 == 0, strides multiples of 16 bytes).
+ *   Dtypes   DA_BF16: bf16 storage, fp32 accumulation, bf16 output rounded to
+ *            nearest even.  DA_F32: fp32 throughout.
+ *   Shapes   dv == 2*d ([DA-blog]: W^V maps to 2d); d in {32, 64}.
+ *   Errors   A status code is returned; nothing is thrown and nothing aborts.
+ *            Arguments are validated on the host before any HIP call
+ *            (DA_EINVAL / DA_EUNSUPPORTED, nothing launched); launch failures
+ *            return DA_EHIP.  da_last_error() gives a thread-local message.
+ *   Streams  `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *            asynchronous on it; there is no host synchronisation.  Calls are
+ *            thread-safe; calls that write the same output race.
+ *   Empty    B == 0 or N == 0 is a valid no-op returning DA_OK.
+ */
+#ifndef DIFFATTN_H
+#define DIFFATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DA_ABI_VERSION 1
+#define DA_MAX_HEADS 256
+
+typedef enum {
+  DA_OK = 0,
+  DA_EINVAL = 1,        /* bad pointer, shape, stride, alignment, map or overlap */
+  DA_EUNSUPPORTED = 2,  /* valid request with no kernel (e.g. d not in {32,64}) */
+  DA_EHIP = 3,          /* a HIP runtime call or kernel launch failed */
+  DA_EWORKSPACE = 4     /* decode workspace missing or too small */
+} da_status;
+
+typedef enum { DA_F32 = 0, DA_BF16 = 1 } da_dtype;
+
+enum {
+  DA_CAUSAL = 1u,   /* query i sees keys 0..i (decoder self-attention); without
+                       it every query sees all N keys (the equation as printed) */
+  DA_NO_NORM = 2u   /* store the raw DiffAttn output o (no head norm, no
+                       (1 - lambda_init) factor) */
+};
+
+/* Prefill forward arguments (diffattn_fwd, gda_fwd).
+ *   q1  [B,N,H_s,d]   q2 [B,N,H_n,d]    k1 [B,N,H_kv,d]   k2 [B,N,H_n,d]
+ *   v   [B,N,H_kv,dv] out [B,N,H_s,dv]   (dtype `dtype`, device)
+ *   s_* element strides of dims (b, n, head) of each tensor.
+ *   noise_of_signal / kv_of_signal: host int32[H_s] or NULL (consecutive
+ *     grouping).  Each noise head must serve exactly H_s/H_n signal heads.
+ *   lambda: the folded per-layer scalar of [DA-blog] "Learnable Lambda
+ *     Re-parameterization" (any real value).  lambda_init: the same section's
+ *     per-layer constant, used only by the head norm.  eps > 0: added to the
+ *     mean of squares.  norm_w: device fp32 [dv] or NULL (unit weight).
+ *   lse: device fp32 [2][B][H_s][N] or NULL.  When given, receives the natural
+ *     log-sum-exp of each map's scaled logits per (b, h, i): lse[0] for A1,
+ *     lse[1] for A2 (what a backward pass re-uses). */
+typedef struct da_fwd_args {
+  const void* q1;
+  const void* q2;
+  const void* k1;
+  const void* k2;
+  const void* v;
+  void* out;
+  int64_t B, N, H_s, H_n, H_kv, d, dv;
+  int64_t s_q1[3], s_q2[3], s_k1[3], s_k2[3], s_v[3], s_out[3];
+  const int32_t* noise_of_signal;
+  const int32_t* kv_of_signal;
+  float lambda, lambda_init, eps;
+  const float* norm_w;
+  float* lse;
+  int32_t dtype;    /* da_dtype */
+  uint32_t flags;   /* DA_CAUSAL | DA_NO_NORM */
+} da_fwd_args;
+
+/* Plain differential attention ([DA-blog] DiffAttn + head_bar_i): requires
+ * H_n == H_kv == H_s and no explicit maps. */
+da_status diffattn_fwd(const da_fwd_args* args, void* stream);
+
+/* Grouped differential attention ([GDA] Abstract, GQA-style repetition of the
+ * noise heads; GQA key/value heads for K1/V): requires H_s % H_n == 0 and
+ * H_s % H_kv == 0.  With H_n == H_kv == H_s it equals diffattn_fwd. */
+da_status gda_fwd(const da_fwd_args* args, void* stream);
+
+/* Decode arguments (gda_decode): one new query per sequence against caches
+ * that already hold the current token, as in a serving step.
+ *   q1 [B,H_s,d]  q2 [B,H_n,d]  out [B,H_s,dv]        strides of (b, head)
+ *   k1_cache [B,H_kv,Lmax,d]  k2_cache [B,H_n,Lmax,d]  v_cache [B,H_kv,Lmax,dv]
+ *                                                     strides of (b, head, pos)
+ *   seq_lens: device int32[B]; sequence b's query sees positions 0..L_b-1.
+ *     0 <= L_b <= Lmax is the caller's contract (the kernels clamp to
+ *     [0, Lmax]); L_b == 0 yields a zero output row.
+ *   chunk: keys per split-K partial (multiple of 64, <= Lmax rounded up), 0 =
+ *     automatic.  The result does not depend on it beyond rounding order.
+ *   Everything else as in da_fwd_args (the causal flag is implied). */
+typedef struct da_decode_args {
+  const void* q1;
+  const void* q2;
+  const void* k1_cache;
+  const void* k2_cache;
+  const void* v_cache;
+  const int32_t* seq_lens;
+  void* out;
+  int64_t B, Lmax, H_s, H_n, H_kv, d, dv, chunk;
+  int64_t s_q1[2], s_q2[2], s_out[2];
+  int64_t s_k1[3], s_k2[3], s_v[3];
+  const int32_t* noise_of_signal;
+  const int32_t* kv_of_signal;
+  float lambda, lambda_init, eps;
+  const float* norm_w;
+  int32_t dtype;
+  uint32_t flags;   /* DA_NO_NORM only */
+} da_decode_args;
+
+/* Bytes of device workspace gda_decode needs for these arguments (0 on
+ * invalid arguments; check da_last_error()). */
+size_t gda_decode_workspace_bytes(const da_decode_args* args);
+
+/* Split-K GDA decode: a partial kernel streams each cached K1/V/K2 byte once
+ * per noise group and writes per-chunk (max, sum, unnormalised output) of both
+ * maps to `workspace` (device, caller-owned, >= gda_decode_workspace_bytes);
+ * a combine kernel merges the chunks, applies the lambda difference and the
+ * head norm.  Returns DA_EWORKSPACE if the workspace is NULL or too small. */
+da_status gda_decode(const da_decode_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* da_status_str(int status);
+
+/* Thread-local detail of the last non-OK status returned on this thread. */
+const char* da_last_error(void);
+
+/* DA_ABI_VERSION of the loaded library. */
+int da_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIFFATTN_H */

@@ -53,6 +53,7 @@ __all__ = [
     "head_rms_norm",
     "diff_attention",
     "diff_attention_rows",
+    "diff_attention_lse",
     "gda_decode",
     "brute_diff_attention",
     "causal_pairs",
@@ -199,6 +200,32 @@ def diff_attention(q1, q2, k1, k2, v, lam: float, lambda_init: float, **kw) -> n
     attention is the case H_n = H_kv = H_s; GDA is H_s > H_n."""
     n = _as64(q1).shape[1] if not hasattr(q1, "shape") else q1.shape[1]
     return diff_attention_rows(q1, q2, k1, k2, v, lam, lambda_init, rows=np.arange(n), **kw)
+
+
+def diff_attention_lse(q1, q2, k1, k2, *, rows, causal: bool = True, noise_of_signal=None,
+                       kv_of_signal=None, heads=None, batches=None) -> np.ndarray:
+    """Natural log-sum-exp of each map's scaled logits over the visible keys:
+    float64 [2, len(batches), len(rows), len(heads)], index 0 for the first
+    map (Q1 K1^T / sqrt(d)), 1 for the second.  softmax_j = exp(s_j - lse)."""
+    q1, q2, k1, k2 = (_as64(t) for t in (q1, q2, k1, k2))
+    B, N, h_s, d = q1.shape
+    h_n, h_kv = q2.shape[2], k1.shape[2]
+    nz, kv = _maps(h_s, h_n, h_kv, noise_of_signal, kv_of_signal)
+    rows = np.asarray(rows, np.int64).reshape(-1)
+    heads = np.arange(h_s) if heads is None else np.asarray(heads, np.int64).reshape(-1)
+    batches = np.arange(B) if batches is None else np.asarray(batches, np.int64).reshape(-1)
+    scale = 1.0 / math.sqrt(d)
+    out = np.zeros((2, len(batches), len(rows), len(heads)))
+    keys = np.arange(N)
+    for bi, b in enumerate(batches):
+        for hi, h in enumerate(heads):
+            for t, (qq, kk, hq, hk) in enumerate(((q1, k1, h, kv[h]), (q2, k2, nz[h], nz[h]))):
+                s = (qq[b, rows, hq, :] @ kk[b, :, hk, :].T) * scale
+                if causal:
+                    s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
+                m = np.max(s, axis=-1)
+                out[t, bi, :, hi] = m + np.log(np.sum(np.exp(s - m[:, None]), axis=-1))
+    return out
 
 
 def gda_decode(q1, q2, k1_cache, k2_cache, v_cache, seq_lens, lam: float, lambda_init: float, *,

@@ -1,0 +1,162 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/diffattn.h declares, and rejects invalid arguments on the
+host before any HIP call.  Pointers here are fake 16-byte-aligned addresses:
+validation never dereferences them, and no valid argument set is passed (that
+would reach a launch)."""
+
+import ctypes
+import os
+
+import pytest
+
+from differential_attention_diff_amd import ops
+
+FAKE = 0x7F0000000000  # aligned fake device addresses, 1 GiB apart
+GIB = 1 << 30
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ops.LIB_PATH):
+        from differential_attention_diff_amd import build
+        build.build()
+    return ops.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = ops.header_functions()
+    assert set(names) >= {"diffattn_fwd", "gda_fwd", "gda_decode", "gda_decode_workspace_bytes", "da_status_str",
+                          "da_last_error", "da_abi_version"}
+    for n in names:
+        assert hasattr(L, n), f"libdiffattn.so does not export {n}"
+
+
+def test_version_and_status_strings(L):
+    assert L.da_abi_version() == 1
+    for s in range(5):
+        assert ops.status_str(s).startswith("DA_")
+    assert ops.status_str(99) == "unknown status"
+
+
+def base_fwd(B=2, N=64, hs=6, hn=2, hkv=6, d=64, dtype=ops.DA_BF16):
+    a = ops.FwdArgs()
+    dv = 2 * d
+    a.q1, a.q2, a.k1, a.k2, a.v, a.out = (FAKE + i * GIB for i in range(6))
+    a.B, a.N, a.H_s, a.H_n, a.H_kv, a.d, a.dv = B, N, hs, hn, hkv, d, dv
+    a.s_q1[:] = [N * hs * d, hs * d, d]
+    a.s_q2[:] = [N * hn * d, hn * d, d]
+    a.s_k1[:] = [N * hkv * d, hkv * d, d]
+    a.s_k2[:] = [N * hn * d, hn * d, d]
+    a.s_v[:] = [N * hkv * dv, hkv * dv, dv]
+    a.s_out[:] = [N * hs * dv, hs * dv, dv]
+    a.lambda_, a.lambda_init, a.eps = 0.7, 0.7, 1e-5
+    a.dtype = dtype
+    a.flags = ops.DA_CAUSAL
+    return a
+
+
+def call(L, a, entry="gda_fwd"):
+    st = getattr(L, entry)(ctypes.byref(a), None)
+    return st, ops.last_error()
+
+
+@pytest.mark.parametrize("mutate,status,msg", [
+    (lambda a: setattr(a, "q1", None), ops.DA_EINVAL, "q1 is NULL"),
+    (lambda a: setattr(a, "out", None), ops.DA_EINVAL, "out is NULL"),
+    (lambda a: setattr(a, "k2", FAKE + 3 * GIB + 8), ops.DA_EINVAL, "16-byte aligned"),
+    (lambda a: setattr(a, "dv", 100), ops.DA_EINVAL, "2*d"),
+    (lambda a: (setattr(a, "d", 48), setattr(a, "dv", 96)), ops.DA_EUNSUPPORTED, "d in {32, 64}"),
+    (lambda a: setattr(a, "H_n", 4), ops.DA_EINVAL, "multiple of H_n"),
+    (lambda a: setattr(a, "H_kv", 4), ops.DA_EINVAL, "multiple of H_kv"),
+    (lambda a: setattr(a, "H_s", 512), ops.DA_EINVAL, "exceeds"),
+    (lambda a: setattr(a, "N", -1), ops.DA_EINVAL, "negative"),
+    (lambda a: a.s_v.__setitem__(1, 129), ops.DA_EINVAL, "multiple of 16 bytes"),
+    (lambda a: a.s_q1.__setitem__(0, -8), ops.DA_EINVAL, "negative stride"),
+    (lambda a: setattr(a, "flags", 8), ops.DA_EINVAL, "flag"),
+    (lambda a: setattr(a, "eps", -1.0), ops.DA_EINVAL, "eps"),
+    (lambda a: setattr(a, "lambda_", float("nan")), ops.DA_EINVAL, "finite"),
+    (lambda a: setattr(a, "dtype", 7), ops.DA_EINVAL, "dtype"),
+    (lambda a: setattr(a, "out", a.v), ops.DA_EINVAL, "overlaps v"),
+    (lambda a: setattr(a, "out", FAKE + 4 * GIB + 1024), ops.DA_EINVAL, "overlaps v"),
+])
+def test_fwd_validation(L, mutate, status, msg):
+    a = base_fwd()
+    mutate(a)
+    st, err = call(L, a)
+    assert st == status, err
+    assert msg in err
+
+
+def test_maps_validation(L):
+    a = base_fwd()
+    bad = (ctypes.c_int32 * 6)(0, 0, 0, 0, 1, 1)  # noise head 0 serves 4, expected 3
+    a.noise_of_signal = ctypes.cast(bad, ctypes.POINTER(ctypes.c_int32))
+    st, err = call(L, a)
+    assert st == ops.DA_EINVAL and "serves 4" in err
+    oob = (ctypes.c_int32 * 6)(0, 0, 0, 1, 1, 2)
+    a.noise_of_signal = ctypes.cast(oob, ctypes.POINTER(ctypes.c_int32))
+    st, err = call(L, a)
+    assert st == ops.DA_EINVAL and "out of" in err
+
+
+def test_plain_entry_requires_equal_heads(L):
+    st, err = call(L, base_fwd(), "diffattn_fwd")
+    assert st == ops.DA_EINVAL and "gda_fwd" in err
+    a = base_fwd(hs=4, hn=4, hkv=4)
+    keep = (ctypes.c_int32 * 4)(0, 1, 2, 3)
+    a.kv_of_signal = ctypes.cast(keep, ctypes.POINTER(ctypes.c_int32))
+    st, err = call(L, a, "diffattn_fwd")
+    assert st == ops.DA_EINVAL and "head maps" in err
+
+
+@pytest.mark.parametrize("B,N", [(0, 64), (2, 0)])
+def test_empty_is_noop(L, B, N):
+    a = base_fwd(B=B, N=N)
+    st, err = call(L, a)
+    assert st == ops.DA_OK, err
+
+
+def base_dec(B=64, L_=8192, hs=18, hn=6, hkv=6, d=64, chunk=0):
+    a = ops.DecodeArgs()
+    dv = 2 * d
+    a.q1, a.q2, a.k1_cache, a.k2_cache, a.v_cache, a.seq_lens, a.out = (FAKE + i * 64 * GIB for i in range(7))
+    a.B, a.Lmax, a.H_s, a.H_n, a.H_kv, a.d, a.dv, a.chunk = B, L_, hs, hn, hkv, d, dv, chunk
+    a.s_q1[:] = [hs * d, d]
+    a.s_q2[:] = [hn * d, d]
+    a.s_out[:] = [hs * dv, dv]
+    a.s_k1[:] = [hkv * L_ * d, L_ * d, d]
+    a.s_k2[:] = [hn * L_ * d, L_ * d, d]
+    a.s_v[:] = [hkv * L_ * dv, L_ * dv, dv]
+    a.lambda_, a.lambda_init, a.eps = 0.75, 0.75, 1e-5
+    a.dtype = ops.DA_BF16
+    return a
+
+
+def test_decode_workspace_bytes(L):
+    a = base_dec()
+    # per (b, group, chunk of 512): g + u = 3 + 1 slots of (dv + 2) floats
+    assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 64 * 6 * 16 * 4 * 130 * 4
+    a = base_dec(chunk=1024)
+    assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 64 * 6 * 8 * 4 * 130 * 4
+    a = base_dec(chunk=96)
+    assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 0 and "multiple of 64" in ops.last_error()
+
+
+def test_decode_validation(L):
+    a = base_dec()
+    st = L.gda_decode(ctypes.byref(a), None, 0, None)
+    assert st == ops.DA_EWORKSPACE, ops.last_error()
+    st = L.gda_decode(ctypes.byref(a), ctypes.c_void_p(FAKE + 63 * GIB), 1024, None)
+    assert st == ops.DA_EWORKSPACE and "needs" in ops.last_error()
+    a = base_dec(d=32)
+    assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EUNSUPPORTED
+    a = base_dec()
+    a.dtype = ops.DA_F32
+    assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EUNSUPPORTED
+    a = base_dec(hs=18, hn=2, hkv=2)  # 9 signal heads per noise head
+    assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EUNSUPPORTED
+    a = base_dec()
+    a.seq_lens = None
+    assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EINVAL
+    a = base_dec(B=0)
+    assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_OK

@@ -1,0 +1,102 @@
+"""GPU parity of gda_decode (split-K partial + combine) against the fp64
+oracle, through the C ABI: the full serving workload (every output), ragged
+and edge-case lengths, split-count independence, general head maps, and the
+decode = last-prefill-row property."""
+
+import numpy as np
+import pytest
+import torch
+
+from differential_attention_diff_amd import ops
+from differential_attention_diff_amd import workloads as W
+from oracle import diffattn_oracle as O
+from tests.helpers import as64, assert_parity, err_stats, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def decode_inputs(B, L, hs, hn, hkv, lens, seed, d=64):
+    g = torch.Generator("cpu").manual_seed(seed)
+    mk = lambda *s: torch.randn(*s, generator=g).bfloat16()
+    return {"q1": mk(B, hs, d), "q2": mk(B, hn, d), "k1_cache": mk(B, hkv, L, d), "k2_cache": mk(B, hn, L, d),
+            "v_cache": mk(B, hkv, L, 2 * d), "seq_lens": torch.tensor(lens, dtype=torch.int32)}
+
+
+def run(inp, lam, li, **kw):
+    d = to_dev(inp)
+    out = ops.gda_decode(d["q1"], d["q2"], d["k1_cache"], d["k2_cache"], d["v_cache"], d["seq_lens"], lam, li, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle(inp, lam, li, **kw):
+    return O.gda_decode(inp["q1"], inp["q2"], inp["k1_cache"], inp["k2_cache"], inp["v_cache"], inp["seq_lens"],
+                        lam, li, **kw)
+
+
+def test_small_ragged_lengths():
+    lens = [1, 2, 63, 64, 65, 511, 512, 513, 700, 1000]
+    inp = decode_inputs(len(lens), 1000, 6, 2, 2, lens, seed=21)
+    out = run(inp, 0.75, 0.75)
+    ma, rel = assert_parity(as64(out), oracle(inp, 0.75, 0.75), "bf16", "ragged decode")
+    print(f"ragged decode max-abs {ma:.3e} rel {rel:.3e}")
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 512, 2048])
+def test_split_count_independence(chunk):
+    lens = [4096, 3001, 1, 2048]
+    inp = decode_inputs(4, 4096, 6, 2, 2, lens, seed=22)
+    want = oracle(inp, 0.6, 0.5)
+    out = run(inp, 0.6, 0.5, chunk=chunk)
+    assert_parity(as64(out), want, "bf16", f"chunk={chunk}")
+    ref = run(inp, 0.6, 0.5, chunk=512)
+    ma, _ = err_stats(as64(out), as64(ref))
+    assert ma <= 2 * 2.0 ** -8  # differs from the default split by bf16 rounding only
+
+
+def test_zero_length_rows_are_zero():
+    inp = decode_inputs(3, 256, 4, 2, 2, [0, 256, 0], seed=23)
+    out = run(inp, 0.7, 0.7)
+    assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
+    assert_parity(as64(out), oracle(inp, 0.7, 0.7), "bf16", "zero-length")
+
+
+def test_general_maps_and_no_norm_and_weight():
+    # 8 signal heads, 2 noise heads, 4 kv heads; a group spans two kv heads (u = 2)
+    inp = decode_inputs(3, 700, 8, 2, 4, [700, 333, 64], seed=24)
+    out = run(inp, 0.8, 0.6)
+    assert_parity(as64(out), oracle(inp, 0.8, 0.6), "bf16", "GDA 4:1 + GQA decode")
+    nz, kv = [1, 1, 0, 0, 1, 0, 0, 1], [3, 0, 2, 1, 1, 3, 0, 2]
+    out = run(inp, 0.8, 0.6, noise_of_signal=nz, kv_of_signal=kv)
+    assert_parity(as64(out), oracle(inp, 0.8, 0.6, noise_of_signal=nz, kv_of_signal=kv), "bf16", "explicit maps")
+    raw = run(inp, 0.8, 0.6, normalize=False)
+    want = oracle(inp, 0.8, 0.6, normalize=False)
+    rms = float(np.sqrt(np.mean(want ** 2)))
+    assert_parity(as64(raw) / rms, want / rms, "bf16", "raw decode")
+    w = torch.linspace(-0.5, 1.5, 128, device="cuda")
+    out = run(inp, 0.8, 0.6, norm_weight=w)
+    assert_parity(as64(out), oracle(inp, 0.8, 0.6, norm_weight=as64(w)), "bf16", "norm weight")
+
+
+def test_decode_is_last_prefill_row():
+    B, N, hs, hn, hkv = 2, 300, 6, 2, 2
+    g = torch.Generator("cpu").manual_seed(25)
+    mk = lambda *s: torch.randn(*s, generator=g).bfloat16()
+    q1, q2, k1, k2, v = mk(B, N, hs, 64), mk(B, N, hn, 64), mk(B, N, hkv, 64), mk(B, N, hn, 64), mk(B, N, hkv, 128)
+    pre = ops.gda_fwd(q1.cuda(), q2.cuda(), k1.cuda(), k2.cuda(), v.cuda(), 0.7, 0.7)
+    t = lambda x: x.transpose(1, 2).contiguous()  # BSHD -> [B,H,L,D]
+    dec = ops.gda_decode(q1[:, -1].cuda(), q2[:, -1].cuda(), t(k1).cuda(), t(k2).cuda(), t(v).cuda(),
+                         torch.full((B,), N, dtype=torch.int32, device="cuda"), 0.7, 0.7)
+    torch.cuda.synchronize()
+    ma, _ = err_stats(as64(dec), as64(pre[:, -1]))
+    assert ma <= 2 * 2.0 ** -7
+
+
+def test_full_serving_workload_every_output():
+    w = W.WORKLOADS["gda_decode_bf16_b64_l8192"]
+    inp = W.make_decode_inputs(w)
+    print("[decode] inputs ready", flush=True)
+    out = run(inp, w.lam, w.lam_init)
+    want = oracle(inp, w.lam, w.lam_init)
+    ma, rel = assert_parity(as64(out), want, "bf16", "serving decode")
+    print(f"[decode] {w.B}x{w.H_s} outputs: max-abs {ma:.3e} rel-L2 {rel:.3e}", flush=True)

@@ -1,0 +1,108 @@
+"""Properties the pages fix, checked through the GPU path (C ABI):
+identical maps with lambda = 1 cancel to exactly zero; rows of A1 - lambda A2
+sum to 1 - lambda; row 0 sees only key 0; large logits are handled by the max
+subtraction (key-shift invariance); runs are bitwise deterministic.
+
+Pages: "Differential Attention in Large Language Models: How Denoising
+Subtraction Eliminates Attention Noise and Outlier Activations" (llms.blog),
+"Differential Attention Architecture" (DiffAttn equation and the A1 ~ A2
+remark) and the softmax properties stated in its introduction."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from differential_attention_diff_amd import ops
+from oracle import diffattn_oracle as O
+from tests.helpers import as64, assert_parity, rand_inputs, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def fwd(inp, lam, li, **kw):
+    d = to_dev(inp)
+    out = ops.gda_fwd(d["q1"], d["q2"], d["k1"], d["k2"], d["v"], lam, li, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("normalize", [True, False])
+def test_identical_maps_cancel_exactly(dtype, normalize):
+    inp = rand_inputs(B=2, N=200, hs=4, hn=4, hkv=4, d=64, dtype=dtype, seed=31)
+    inp["q2"], inp["k2"] = inp["q1"].clone(), inp["k1"].clone()
+    out = fwd(inp, 1.0, 0.8, normalize=normalize)
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_identical_maps_cancel_exactly_decode():
+    g = torch.Generator("cpu").manual_seed(32)
+    q = torch.randn(3, 4, 64, generator=g).bfloat16()
+    k = torch.randn(3, 4, 900, 64, generator=g).bfloat16()
+    v = torch.randn(3, 4, 900, 128, generator=g).bfloat16()
+    lens = torch.tensor([900, 17, 512], dtype=torch.int32)
+    out = ops.gda_decode(q.cuda(), q.cuda(), k.cuda(), k.cuda(), v.cuda(), lens.cuda(), 1.0, 0.75)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_row_sums_are_one_minus_lambda(dtype):
+    inp = rand_inputs(B=1, N=300, hs=6, hn=2, hkv=3, d=64, dtype=dtype, seed=33)
+    inp["v"][..., 5] = 1.0
+    lam = 0.7
+    raw = as64(fwd(inp, lam, 0.0, normalize=False))[..., 5]
+    tol = 1e-6 if dtype == torch.float32 else 2.0 ** -8  # bf16 output rounding of 0.3
+    assert np.max(np.abs(raw - (1 - lam))) <= tol
+
+
+def test_all_ones_value_closed_form():
+    inp = rand_inputs(B=1, N=130, hs=2, hn=2, hkv=2, d=64, dtype=torch.bfloat16, seed=34)
+    inp["v"][:] = 1.0
+    lam, li, eps = 0.6, 0.25, 1e-5
+    y = as64(fwd(inp, lam, li, eps=eps))
+    want = (1 - li) * (1 - lam) / math.sqrt((1 - lam) ** 2 + eps)
+    assert np.max(np.abs(y - want)) <= 2.0 ** -8
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_row_zero_closed_form(dtype):
+    inp = rand_inputs(B=2, N=100, hs=3, hn=3, hkv=3, d=64, dtype=dtype, seed=35)
+    lam = 0.42
+    raw = as64(fwd(inp, lam, 0.0, normalize=False))[:, 0]
+    want = (1 - lam) * as64(inp["v"])[:, 0]
+    tol = 1e-6 if dtype == torch.float32 else 2.0 ** -7
+    assert np.max(np.abs(raw - want)) <= tol * max(1.0, np.max(np.abs(want)))
+
+
+def test_large_logits_key_shift_invariance():
+    # dyadic grid values (multiples of 1/8): K1 + 24 stays exact in bf16
+    rng = np.random.default_rng(36)
+    B, N, H, d = 1, 260, 2, 64
+    grid = lambda lo, hi, shape: torch.from_numpy(rng.integers(lo, hi + 1, shape) / 8.0).float().bfloat16()
+    # q1 in [-8, 8]: with keys shifted by 24 the first map's logits reach ~100 (natural units),
+    # past fp32 exp's range without the max subtraction
+    inp = {"q1": grid(-64, 64, (B, N, H, d)), "q2": grid(-8, 8, (B, N, H, d)), "k1": grid(-8, 8, (B, N, H, d)),
+           "k2": grid(-8, 8, (B, N, H, d)), "v": grid(-8, 8, (B, N, H, 2 * d))}
+    shifted = dict(inp)
+    shifted["k1"] = (inp["k1"].float() + 24.0).bfloat16()
+    assert torch.equal(shifted["k1"].float() - 24.0, inp["k1"].float())
+    a = fwd(inp, 0.5, 0.5)
+    b = fwd(shifted, 0.5, 0.5)
+    assert torch.all(torch.isfinite(b.float()))
+    lse = O.diff_attention_lse(shifted["q1"], shifted["q2"], shifted["k1"], shifted["k2"], rows=np.arange(N))
+    assert np.max(lse[0]) > 90.0
+    want = O.diff_attention(shifted["q1"], shifted["q2"], shifted["k1"], shifted["k2"], shifted["v"], 0.5, 0.5)
+    assert_parity(as64(b), want, "bf16", "shifted keys")
+    assert_parity(as64(a), want, "bf16", "unshifted keys vs shifted oracle")
+
+
+def test_bitwise_deterministic():
+    inp = rand_inputs(B=2, N=700, hs=6, hn=2, hkv=6, d=64, dtype=torch.bfloat16, seed=37)
+    d = to_dev(inp)
+    a = ops.gda_fwd(d["q1"], d["q2"], d["k1"], d["k2"], d["v"], 0.7, 0.7)
+    b = ops.gda_fwd(d["q1"], d["q2"], d["k1"], d["k2"], d["v"], 0.7, 0.7)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

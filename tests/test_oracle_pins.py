@@ -280,3 +280,22 @@ def test_planted_mistakes_are_caught(monkeypatch):
     real_norm = O.head_rms_norm
     monkeypatch.setattr(O, "head_rms_norm", lambda o, li, eps, w=None: real_norm(o - o.mean(-1, keepdims=True), li, eps, w))
     assert not check()  # mean-centred GroupNorm instead of RMS
+
+
+# --- log-sum-exp export (used by the forward's optional lse output) -----------------------
+
+def test_lse_brute_and_softmax_identity():
+    q1, q2, k1, k2, v = tiny(B=1, N=6, hs=4, hn=2, hkv=2, d=3, dv=6, seed=18)
+    lse = O.diff_attention_lse(q1, q2, k1, k2, rows=np.arange(6))
+    for h in range(4):
+        for i in range(6):
+            s1 = [float(np.dot(q1[0, i, h], k1[0, j, h // 2])) / math.sqrt(3) for j in range(i + 1)]
+            s2 = [float(np.dot(q2[0, i, h // 2], k2[0, j, h // 2])) / math.sqrt(3) for j in range(i + 1)]
+            assert lse[0, 0, i, h] == pytest.approx(math.log(sum(math.exp(x) for x in s1)), rel=1e-12)
+            assert lse[1, 0, i, h] == pytest.approx(math.log(sum(math.exp(x) for x in s2)), rel=1e-12)
+    # softmax of map 2 recovered from lse reproduces A2 V = O(0) - O(1)
+    o0 = O.diff_attention(q1, q2, k1, k2, v, 0.0, 0.0, normalize=False)
+    o1 = O.diff_attention(q1, q2, k1, k2, v, 1.0, 0.0, normalize=False)
+    h, i = 3, 5
+    a2 = np.exp(np.array([np.dot(q2[0, i, 1], k2[0, j, 1]) / math.sqrt(3) for j in range(i + 1)]) - lse[1, 0, i, h])
+    np.testing.assert_allclose(a2 @ v[0, :i + 1, 1], (o0 - o1)[0, i, h], rtol=1e-12)
