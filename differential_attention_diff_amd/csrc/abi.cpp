@@ -119,6 +119,13 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain) {
       return fail(DA_EINVAL, "diffattn_fwd needs H_n == H_kv == H_s (use gda_fwd for grouped heads)");
     if (a->noise_of_signal || a->kv_of_signal) return fail(DA_EINVAL, "diffattn_fwd takes no head maps");
   }
+  da::FwdParams p;
+  memset(&p, 0, sizeof p);
+  if ((st = resolve_maps((int)a->H_s, (int)a->H_n, (int)a->H_kv, a->noise_of_signal, a->kv_of_signal, p.nz, p.kv,
+                         p.members)) != DA_OK)
+    return st;
+  if (a->B == 0 || a->N == 0) return DA_OK;  // empty: no pointer is touched (torch gives NULL for empty tensors)
+
   const int es = a->dtype == DA_BF16 ? 2 : 4;
   struct T {
     const char* name;
@@ -132,13 +139,6 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain) {
     if ((st = check_strides(t.name, t.p, t.s, 3, es)) != DA_OK) return st;
   if (a->norm_w && ((uintptr_t)a->norm_w & 3u)) return fail(DA_EINVAL, "norm_w is not 4-byte aligned");
   if (a->lse && ((uintptr_t)a->lse & 3u)) return fail(DA_EINVAL, "lse is not 4-byte aligned");
-
-  da::FwdParams p;
-  memset(&p, 0, sizeof p);
-  if ((st = resolve_maps((int)a->H_s, (int)a->H_n, (int)a->H_kv, a->noise_of_signal, a->kv_of_signal, p.nz, p.kv,
-                         p.members)) != DA_OK)
-    return st;
-  if (a->B == 0 || a->N == 0) return DA_OK;
 
   Extent eo;
   {
@@ -207,6 +207,7 @@ constexpr int kMaxChunk = 2048;
 constexpr int kDecodeMaxQueries = 8;  // g + 1 scored queries per noise group
 
 da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p) {
+  memset(p, 0, sizeof *p);  // B == 0 exits early with an all-zero (empty) parameter block
   if (!a) return fail(DA_EINVAL, "args is NULL");
   da_status st = check_common_shapes(a->B, a->Lmax, a->H_s, a->H_n, a->H_kv, a->d, a->dv, a->dtype, a->lambda,
                                      a->lambda_init, a->eps);
@@ -218,6 +219,7 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p) {
   if (a->chunk > kMaxChunk) return fail(DA_EUNSUPPORTED, "chunk %lld exceeds %d", (long long)a->chunk, kMaxChunk);
   if (a->H_s / a->H_n + 1 > kDecodeMaxQueries)
     return fail(DA_EUNSUPPORTED, "gda_decode supports up to %d signal heads per noise head", kDecodeMaxQueries - 1);
+  if (a->B == 0) return DA_OK;  // empty batch: nothing is validated further or touched
   const int es = 2;
   struct T {
     const char* name;
@@ -232,7 +234,6 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p) {
   if ((uintptr_t)a->seq_lens & 3u) return fail(DA_EINVAL, "seq_lens is not 4-byte aligned");
   if (a->norm_w && ((uintptr_t)a->norm_w & 3u)) return fail(DA_EINVAL, "norm_w is not 4-byte aligned");
 
-  memset(p, 0, sizeof *p);
   int16_t nz[DA_MAX_HEADS];
   if ((st = resolve_maps((int)a->H_s, (int)a->H_n, (int)a->H_kv, a->noise_of_signal, a->kv_of_signal, nz, p->kv,
                          p->members)) != DA_OK)

@@ -54,3 +54,11 @@ def rand_inputs(B, N, hs, hn, hkv, d, dtype, seed, v_std=1.0):
     mk = lambda *s: torch.randn(*s, generator=g).to(dtype)
     return {"q1": mk(B, N, hs, d), "q2": mk(B, N, hn, d), "k1": mk(B, N, hkv, d), "k2": mk(B, N, hn, d),
             "v": (torch.randn(B, N, hkv, 2 * d, generator=g) * v_std).to(dtype)}
+
+
+def norm_scale(want_raw: np.ndarray, lam_init: float, eps: float = 1e-5) -> np.ndarray:
+    """Per-row factor the head norm applies to the oracle's raw output,
+    (1 - lambda_init) / sqrt(mean(o^2) + eps): the bf16 bar is stated for the
+    normalised output, so a raw (DA_NO_NORM) result is held to it after the
+    same per-row scaling."""
+    return (1.0 - lam_init) / np.sqrt(np.mean(want_raw ** 2, axis=-1, keepdims=True) + eps)

@@ -160,3 +160,16 @@ def test_decode_validation(L):
     assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EINVAL
     a = base_dec(B=0)
     assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_OK
+
+
+def test_empty_with_null_pointers_is_noop(L):
+    # torch hands out NULL data pointers for empty tensors
+    for B, N in ((0, 64), (2, 0)):
+        a = base_fwd(B=B, N=N)
+        a.q1 = a.q2 = a.k1 = a.k2 = a.v = a.out = None
+        st, err = call(L, a)
+        assert st == ops.DA_OK, err
+    d = base_dec(B=0)
+    d.q1 = d.q2 = d.k1_cache = d.k2_cache = d.v_cache = d.seq_lens = d.out = None
+    assert L.gda_decode_workspace_bytes(ctypes.byref(d)) == 0
+    assert L.gda_decode(ctypes.byref(d), None, 0, None) == ops.DA_OK

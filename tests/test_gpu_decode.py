@@ -10,7 +10,7 @@ import torch
 from differential_attention_diff_amd import ops
 from differential_attention_diff_amd import workloads as W
 from oracle import diffattn_oracle as O
-from tests.helpers import as64, assert_parity, err_stats, to_dev
+from tests.helpers import as64, assert_parity, err_stats, norm_scale, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -71,8 +71,8 @@ def test_general_maps_and_no_norm_and_weight():
     assert_parity(as64(out), oracle(inp, 0.8, 0.6, noise_of_signal=nz, kv_of_signal=kv), "bf16", "explicit maps")
     raw = run(inp, 0.8, 0.6, normalize=False)
     want = oracle(inp, 0.8, 0.6, normalize=False)
-    rms = float(np.sqrt(np.mean(want ** 2)))
-    assert_parity(as64(raw) / rms, want / rms, "bf16", "raw decode")
+    sc = norm_scale(want, 0.6)
+    assert_parity(as64(raw) * sc, want * sc, "bf16", "raw decode")
     w = torch.linspace(-0.5, 1.5, 128, device="cuda")
     out = run(inp, 0.8, 0.6, norm_weight=w)
     assert_parity(as64(out), oracle(inp, 0.8, 0.6, norm_weight=as64(w)), "bf16", "norm weight")

@@ -54,7 +54,9 @@ def test_row_sums_are_one_minus_lambda(dtype):
     inp["v"][..., 5] = 1.0
     lam = 0.7
     raw = as64(fwd(inp, lam, 0.0, normalize=False))[..., 5]
-    tol = 1e-6 if dtype == torch.float32 else 2.0 ** -8  # bf16 output rounding of 0.3
+    # fp32: accumulation over up to 300 keys (sqrt(300) * 2^-24 * (1 + lambda) ~ 2e-6) -> the fp32 bar;
+    # bf16: output rounding of 0.3
+    tol = 1e-5 if dtype == torch.float32 else 2.0 ** -8
     assert np.max(np.abs(raw - (1 - lam))) <= tol
 
 
