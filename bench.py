@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused causal differential-attention forward on one MI355X.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-extra] [--no-cpu-baseline] [--out FILE]
+
+A step is one call of the hot path on one batch of synthetic, seeded input
+already resident in HBM: for the headline workload (the 3B-like Diff
+Transformer layer, 4 x 4096 tokens, 24 heads, d = 64, bf16) one gda_fwd /
+diffattn_fwd launch.  W untimed steps, then exactly K steps bracketed by
+torch.cuda.synchronize(), timed with HIP events recorded on the stream the
+kernels are launched on (torch's current stream, which the binding passes to
+the C ABI).  One JSON line is printed; `value` is F_alg TFLOP/s (each product
+of the DiffAttn equation counted once, causal pairs only).  The same line
+carries the roofline of the kernel (against the 2.5 PFLOP/s dense bf16 MFMA
+peak), the F_exec view (F_alg plus the second P.V an exact one-pass kernel
+must issue), the grouped (3:1) prefill and the split-K decode (HBM GB/s
+against 8 TB/s) measured the same way, and the fp64 CPU oracle timed on a
+bounded sample of the same workload on the host's cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from differential_attention_diff_amd import workloads as W  # noqa: E402
+
+METRIC = "diff-attn fwd TFLOP/s (% bf16 MFMA peak) at seq 4096; decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+
+# ---------------------------------------------------------------------------
+# work accounting (algorithmic; independent of how the kernels execute it)
+# ---------------------------------------------------------------------------
+
+def pairs(w):
+    return w.B * w.N * (w.N + 1) // 2 if w.causal else w.B * w.N * w.N
+
+
+def f_alg(w):
+    """QK1 per signal head + QK2 per noise head (2d each) + one PV per signal head (2dv), per causal pair."""
+    return pairs(w) * (w.H_s * 2 * w.d + w.H_n * 2 * w.d + w.H_s * 2 * w.dv)
+
+
+def f_exec(w):
+    """f_alg + one more PV (2dv) per distinct (noise head, kv head) combination (consecutive maps)."""
+    g, gk = w.H_s // w.H_n, w.H_s // w.H_kv
+    distinct = len({(h // g, h // gk) for h in range(w.H_s)})
+    return f_alg(w) + pairs(w) * distinct * 2 * w.dv
+
+
+def prefill_bytes(w):
+    e = 2 if w.dtype == "bf16" else 4
+    return e * w.B * w.N * ((w.H_s + w.H_n) * w.d + (w.H_kv + w.H_n) * w.d + w.H_kv * w.dv + w.H_s * w.dv)
+
+
+def decode_bytes(w, seq_lens):
+    """Each cached K1/V byte of every kv head and K2 byte of every noise head for positions < L_b,
+    plus the queries and the output."""
+    L = int(np.sum(seq_lens))
+    per_pos = 2 * (w.H_kv * w.d + w.H_n * w.d + w.H_kv * w.dv)
+    return L * per_pos + 2 * w.B * ((w.H_s + w.H_n) * w.d + w.H_s * w.dv)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle, as it stands, on a bounded sample
+# ---------------------------------------------------------------------------
+
+_CPU = {}
+
+
+def _limit_blas():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _oracle_unit(unit):
+    from oracle import diffattn_oracle as O
+    b, h = unit
+    a = _CPU
+    O.diff_attention_rows(a["q1"][b:b + 1], a["q2"][b:b + 1], a["k1"][b:b + 1], a["k2"][b:b + 1],
+                          a["v"][b:b + 1], a["lam"], a["lam_init"], rows=a["rows"], heads=[h], eps=a["eps"])
+    return 1
+
+
+def cpu_baseline(w, inp, nrows: int):
+    """Time the oracle on `nrows` query rows (spread over the sequence) for every (batch, signal head)
+    of the workload, one process per core; report F_alg TFLOP/s of that sample."""
+    import multiprocessing as mp
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    rows = np.unique(np.linspace(0, w.N - 1, nrows).round().astype(np.int64))
+    _CPU.clear()
+    _CPU.update({k: inp[k].float().double().numpy() for k in ("q1", "q2", "k1", "k2", "v")})
+    _CPU.update(rows=rows, lam=w.lam, lam_init=w.lam_init, eps=w.eps)
+    units = [(b, h) for b in range(w.B) for h in range(w.H_s)]
+    ctx = mp.get_context("fork")   # fork before any GPU initialisation in this process
+    with ctx.Pool(cores, initializer=_limit_blas) as pool:
+        pool.map(_oracle_unit, units[:cores])   # warm the workers (imports)
+        t0 = time.perf_counter()
+        pool.map(_oracle_unit, units, chunksize=1)
+        dt = time.perf_counter() - t0
+    vis = int(np.sum(rows + 1)) if w.causal else len(rows) * w.N
+    flops = w.B * vis * (w.H_s * 2 * w.d + w.H_n * 2 * w.d + w.H_s * 2 * w.dv)
+    _CPU.clear()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{len(rows)} query rows evenly spaced over [0, {w.N}) x {w.B} batches x {w.H_s} signal heads "
+                      f"of {w.name} (fp64 NumPy oracle, one process per core, BLAS 1 thread each); "
+                      f"F_alg of the sampled causal pairs / wall time"}
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+def time_steps(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per step
+
+
+def bench_prefill(w, steps, warmup, inp=None):
+    import torch
+    from differential_attention_diff_amd import ops
+    inp = W.make_prefill_inputs(w) if inp is None else inp
+    d = {k: v.cuda() for k, v in inp.items()}
+    out = torch.empty(w.B, w.N, w.H_s, w.dv, dtype=w.torch_dtype, device="cuda")
+    plain = w.H_n == w.H_s and w.H_kv == w.H_s
+    entry = ops.diffattn_fwd if plain else ops.gda_fwd
+    fn = lambda: entry(d["q1"], d["q2"], d["k1"], d["k2"], d["v"], w.lam, w.lam_init, out=out, eps=w.eps)
+    ms = time_steps(fn, steps, warmup)
+    fa, fe = f_alg(w), f_exec(w)
+    ach, ache = fa / (ms * 1e-3) / 1e12, fe / (ms * 1e-3) / 1e12
+    return {
+        "workload": w.name, "value": ach, "unit": "TFLOP/s", "ms_per_step": ms,
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "H_s": w.H_s, "H_n": w.H_n, "H_kv": w.H_kv, "d": w.d,
+                   "dv": w.dv, "causal": w.causal, "entry": "diffattn_fwd" if plain else "gda_fwd",
+                   "flop_convention": "F_alg"},
+        "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                     "flops_per_launch": fa, "kernel": "fwd_bf16_kernel<64>"},
+        "roofline_exec": {"achieved": ache, "frac": ache / PEAK_BF16_TFLOPS, "flops_per_launch": fe},
+        "algorithmic_bytes": prefill_bytes(w),
+    }
+
+
+def bench_decode(w, steps, warmup):
+    import torch
+    from differential_attention_diff_amd import ops
+    inp = W.make_decode_inputs(w)
+    d = {k: v.cuda() for k, v in inp.items()}
+    out = torch.empty(w.B, w.H_s, w.dv, dtype=w.torch_dtype, device="cuda")
+    nbytes = ops.gda_decode_workspace_bytes(d["q1"], d["q2"], d["k1_cache"], d["k2_cache"], d["v_cache"],
+                                            d["seq_lens"])
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    fn = lambda: ops.gda_decode(d["q1"], d["q2"], d["k1_cache"], d["k2_cache"], d["v_cache"], d["seq_lens"],
+                                w.lam, w.lam_init, out=out, workspace=ws, eps=w.eps)
+    ms = time_steps(fn, steps, warmup)
+    nb = decode_bytes(w, inp["seq_lens"].numpy())
+    gbs = nb / (ms * 1e-3) / 1e9
+    return {
+        "workload": w.name, "metric": "decode HBM GB/s", "value": gbs, "unit": "GB/s", "ms_per_step": ms,
+        "config": {"workload": w.name, "B": w.B, "Lmax": w.N, "len_range": list(w.len_range),
+                   "sum_seq_lens": int(inp["seq_lens"].sum()), "H_s": w.H_s, "H_n": w.H_n, "H_kv": w.H_kv,
+                   "d": w.d, "dv": w.dv, "entry": "gda_decode"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": nb,
+                     "kernel": "decode_partial_kernel + decode_combine_kernel (step time)"},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="diff3b_bf16_n4096", choices=[k for k in W.ORDER if k != "tiny_diff_f32"])
+    ap.add_argument("--no-extra", action="store_true", help="skip the grouped prefill and decode lines")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="query rows in the CPU-baseline sample (default: every row of the 4096-token workload)")
+    ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (sharding is described in the design "
+              "notes but not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    w = W.WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    inp = W.make_prefill_inputs(w) if w.kind == "prefill" else None
+
+    cpu = None
+    if not args.no_cpu_baseline and w.kind == "prefill":
+        print(f"[bench] CPU oracle baseline ({args.cpu_rows} rows sample)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, inp, args.cpu_rows)
+        print(f"[bench] CPU oracle: {cpu['seconds']} s on {cpu['cores']} cores", file=sys.stderr, flush=True)
+
+    import torch
+    print(f"[bench] GPU {torch.cuda.get_device_name(0)}: timing {w.name}", file=sys.stderr, flush=True)
+    head = bench_prefill(w, args.steps, args.warmup, inp) if w.kind == "prefill" else \
+        bench_decode(w, args.steps, args.warmup)
+    extra = []
+    if not args.no_extra:
+        for name in ("gda3to1_bf16_n4096", "gda_decode_bf16_b64_l8192"):
+            if name == w.name:
+                continue
+            ew = W.WORKLOADS[name]
+            print(f"[bench] timing {name}", file=sys.stderr, flush=True)
+            extra.append(bench_prefill(ew, args.steps, args.warmup) if ew.kind == "prefill"
+                         else bench_decode(ew, args.steps, args.warmup))
+
+    line = {
+        "metric": METRIC,
+        "value": round(head["value"], 3),
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": head["config"],
+        "roofline": head["roofline"],
+    }
+    if "roofline_exec" in head:
+        line["roofline_exec"] = head["roofline_exec"]
+    line["cpu_baseline"] = cpu
+    line["extra"] = extra
+    text = json.dumps(line)
+    print(text, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -206,7 +206,7 @@ constexpr int kDefaultChunk = 512;
 constexpr int kMaxChunk = 2048;
 constexpr int kDecodeMaxQueries = 8;  // g + 1 scored queries per noise group
 
-da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p) {
+da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool check_pointers) {
   memset(p, 0, sizeof *p);  // B == 0 exits early with an all-zero (empty) parameter block
   if (!a) return fail(DA_EINVAL, "args is NULL");
   da_status st = check_common_shapes(a->B, a->Lmax, a->H_s, a->H_n, a->H_kv, a->d, a->dv, a->dtype, a->lambda,
@@ -228,11 +228,13 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p) {
     int nlead;
   } ts[6] = {{"q1", a->q1, a->s_q1, 2},       {"q2", a->q2, a->s_q2, 2},       {"k1_cache", a->k1_cache, a->s_k1, 3},
              {"k2_cache", a->k2_cache, a->s_k2, 3}, {"v_cache", a->v_cache, a->s_v, 3}, {"out", a->out, a->s_out, 2}};
-  for (auto& t : ts)
-    if ((st = check_strides(t.name, t.p, t.s, t.nlead, es)) != DA_OK) return st;
-  if (!a->seq_lens) return fail(DA_EINVAL, "seq_lens is NULL");
-  if ((uintptr_t)a->seq_lens & 3u) return fail(DA_EINVAL, "seq_lens is not 4-byte aligned");
-  if (a->norm_w && ((uintptr_t)a->norm_w & 3u)) return fail(DA_EINVAL, "norm_w is not 4-byte aligned");
+  if (check_pointers) {
+    for (auto& t : ts)
+      if ((st = check_strides(t.name, t.p, t.s, t.nlead, es)) != DA_OK) return st;
+    if (!a->seq_lens) return fail(DA_EINVAL, "seq_lens is NULL");
+    if ((uintptr_t)a->seq_lens & 3u) return fail(DA_EINVAL, "seq_lens is not 4-byte aligned");
+    if (a->norm_w && ((uintptr_t)a->norm_w & 3u)) return fail(DA_EINVAL, "norm_w is not 4-byte aligned");
+  }
 
   int16_t nz[DA_MAX_HEADS];
   if ((st = resolve_maps((int)a->H_s, (int)a->H_n, (int)a->H_kv, a->noise_of_signal, a->kv_of_signal, nz, p->kv,
@@ -310,13 +312,13 @@ da_status gda_fwd(const da_fwd_args* args, void* stream) { return fwd_impl(args,
 
 size_t gda_decode_workspace_bytes(const da_decode_args* args) {
   da::DecodeParams p;
-  if (decode_prepare(args, &p) != DA_OK) return 0;
+  if (decode_prepare(args, &p, /*check_pointers=*/false) != DA_OK) return 0;  // shapes only
   return decode_ws_bytes(p);
 }
 
 da_status gda_decode(const da_decode_args* args, void* workspace, size_t workspace_bytes, void* stream) {
   da::DecodeParams p;
-  da_status st = decode_prepare(args, &p);
+  da_status st = decode_prepare(args, &p, /*check_pointers=*/true);
   if (st != DA_OK) return st;
   if (p.B == 0) return DA_OK;  // Lmax == 0 still launches: every output row is zero
   const size_t need = decode_ws_bytes(p);

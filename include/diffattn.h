@@ -142,8 +142,9 @@ typedef struct da_decode_args {
   uint32_t flags;   /* DA_NO_NORM only */
 } da_decode_args;
 
-/* Bytes of device workspace gda_decode needs for these arguments (0 on
- * invalid arguments; check da_last_error()). */
+/* Bytes of device workspace gda_decode needs for these arguments.  Depends on
+ * the shapes, head maps and chunk only: data pointers may be NULL.  Returns 0
+ * for an empty batch and on invalid shapes (then da_last_error() says why). */
 size_t gda_decode_workspace_bytes(const da_decode_args* args);
 
 /* Split-K GDA decode: a partial kernel streams each cached K1/V/K2 byte once

@@ -173,3 +173,9 @@ def test_empty_with_null_pointers_is_noop(L):
     d.q1 = d.q2 = d.k1_cache = d.k2_cache = d.v_cache = d.seq_lens = d.out = None
     assert L.gda_decode_workspace_bytes(ctypes.byref(d)) == 0
     assert L.gda_decode(ctypes.byref(d), None, 0, None) == ops.DA_OK
+
+
+def test_decode_workspace_query_ignores_pointers(L):
+    a = base_dec()
+    a.q1 = a.q2 = a.k1_cache = a.k2_cache = a.v_cache = a.seq_lens = a.out = None
+    assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 64 * 6 * 16 * 4 * 130 * 4
