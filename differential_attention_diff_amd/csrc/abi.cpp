@@ -202,7 +202,8 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain) {
 // decode
 // ---------------------------------------------------------------------------
 
-constexpr int kDefaultChunk = 512;
+constexpr int kDefaultChunk = 256;
+constexpr int kChunkQuantum = 128;  // positions per decode sub-chunk
 constexpr int kMaxChunk = 2048;
 constexpr int kDecodeMaxQueries = 8;  // g + 1 scored queries per noise group
 
@@ -215,7 +216,8 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool chec
   if (a->dtype != DA_BF16) return fail(DA_EUNSUPPORTED, "gda_decode has a bf16 kernel only");
   if (a->d != 64) return fail(DA_EUNSUPPORTED, "gda_decode has a d = 64 kernel only");
   if (a->flags & ~(uint32_t)DA_NO_NORM) return fail(DA_EINVAL, "gda_decode accepts only DA_NO_NORM");
-  if (a->chunk < 0 || a->chunk % 64 != 0) return fail(DA_EINVAL, "chunk must be 0 or a positive multiple of 64");
+  if (a->chunk < 0 || a->chunk % kChunkQuantum != 0)
+    return fail(DA_EINVAL, "chunk must be 0 or a positive multiple of %d", kChunkQuantum);
   if (a->chunk > kMaxChunk) return fail(DA_EUNSUPPORTED, "chunk %lld exceeds %d", (long long)a->chunk, kMaxChunk);
   if (a->H_s / a->H_n + 1 > kDecodeMaxQueries)
     return fail(DA_EUNSUPPORTED, "gda_decode supports up to %d signal heads per noise head", kDecodeMaxQueries - 1);
@@ -259,8 +261,8 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool chec
     umax = std::max(umax, u);
   }
   int64_t chunk = a->chunk ? a->chunk : kDefaultChunk;
-  int64_t lmax_r = (a->Lmax + 63) / 64 * 64;
-  if (chunk > lmax_r) chunk = std::max<int64_t>(64, lmax_r);
+  int64_t lmax_r = (a->Lmax + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
+  if (chunk > lmax_r) chunk = std::max<int64_t>(kChunkQuantum, lmax_r);
   p->chunk = (int)chunk;
   p->nchunks = (int)((a->Lmax + chunk - 1) / chunk);
   p->slots = g + umax;

@@ -120,8 +120,9 @@ da_status gda_fwd(const da_fwd_args* args, void* stream);
  *   seq_lens: device int32[B]; sequence b's query sees positions 0..L_b-1.
  *     0 <= L_b <= Lmax is the caller's contract (the kernels clamp to
  *     [0, Lmax]); L_b == 0 yields a zero output row.
- *   chunk: keys per split-K partial (multiple of 64, <= Lmax rounded up), 0 =
- *     automatic.  The result does not depend on it beyond rounding order.
+ *   chunk: cached positions per split-K partial (a multiple of 128, at most
+ *     2048), 0 = automatic (256).  The result does not depend on it beyond
+ *     rounding order.
  *   Everything else as in da_fwd_args (the causal flag is implied). */
 typedef struct da_decode_args {
   const void* q1;

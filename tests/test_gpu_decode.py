@@ -42,14 +42,14 @@ def test_small_ragged_lengths():
     print(f"ragged decode max-abs {ma:.3e} rel {rel:.3e}")
 
 
-@pytest.mark.parametrize("chunk", [64, 128, 512, 2048])
+@pytest.mark.parametrize("chunk", [128, 256, 1024, 2048])
 def test_split_count_independence(chunk):
     lens = [4096, 3001, 1, 2048]
     inp = decode_inputs(4, 4096, 6, 2, 2, lens, seed=22)
     want = oracle(inp, 0.6, 0.5)
     out = run(inp, 0.6, 0.5, chunk=chunk)
     assert_parity(as64(out), want, "bf16", f"chunk={chunk}")
-    ref = run(inp, 0.6, 0.5, chunk=512)
+    ref = run(inp, 0.6, 0.5, chunk=256)
     ma, _ = err_stats(as64(out), as64(ref))
     assert ma <= 2 * 2.0 ** -8  # differs from the default split by bf16 rounding only
 
