@@ -202,10 +202,11 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain) {
 // decode
 // ---------------------------------------------------------------------------
 
-constexpr int kDefaultChunk = 256;
+constexpr int kDefaultChunk = 512;
 constexpr int kChunkQuantum = 128;  // positions per decode sub-chunk
 constexpr int kMaxChunk = 2048;
 constexpr int kDecodeMaxQueries = 8;  // g + 1 scored queries per noise group
+constexpr int64_t kMaxPosStride = 1 << 19;  // elements; 2048 positions x 2 B x 2^19 < 2^31
 
 da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool check_pointers) {
   memset(p, 0, sizeof *p);  // B == 0 exits early with an all-zero (empty) parameter block
@@ -222,6 +223,9 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool chec
   if (a->H_s / a->H_n + 1 > kDecodeMaxQueries)
     return fail(DA_EUNSUPPORTED, "gda_decode supports up to %d signal heads per noise head", kDecodeMaxQueries - 1);
   if (a->B == 0) return DA_OK;  // empty batch: nothing is validated further or touched
+  // the partial kernel addresses a chunk's rows with 32-bit byte offsets
+  if (a->s_k1[2] > kMaxPosStride || a->s_k2[2] > kMaxPosStride || a->s_v[2] > kMaxPosStride)
+    return fail(DA_EUNSUPPORTED, "cache position stride exceeds %d elements", kMaxPosStride);
   const int es = 2;
   struct T {
     const char* name;

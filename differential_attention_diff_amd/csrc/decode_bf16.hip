@@ -81,8 +81,11 @@ __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp<kRowMirror>(x));
   return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
 }
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// x rounded to the nearest bf16 (ties to even), returned as the fp32 of that value
+__device__ __forceinline__ float round_bf16(float x) {
+  const __bf16 h = (__bf16)x;
+  return (float)h;
+}
 
 // dot of 8 bf16 pairs held in two u32x4 (lanes are copied to scalars first:
 // this compiler's __builtin_bit_cast of a vector element reads element 0)
@@ -98,11 +101,14 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
 
 // MAXO bounds both g + 1 (scored queries) and g + u (outputs); 4 covers 3:1 GDA
 // with one key/value head per group, 8 the general case.
-template <int MAXO>
-__global__ __launch_bounds__(kT) void decode_partial_kernel(DecodeParams p) {
+// MULTI: some noise group spans several key/value heads (u > 1); the kernel then
+// re-loads K1 / V per head inside the sub-chunk.  Without it the loops collapse.
+template <int MAXO, bool MULTI>
+__global__ __launch_bounds__(kT, 4) void decode_partial_kernel(DecodeParams p) {
   constexpr int kMaxQ = MAXO, kMaxOut = MAXO;
   __shared__ float S[kMaxQ][kC];                // scores, then weights, of the current sub-chunk
   __shared__ float ML[3][kMaxQ];                // running max, running sum, last rescale per query
+  __shared__ u32x4 QS[kMaxQ][kD / 8];           // the group's queries
   __shared__ float red[kT / 16][kMaxOut][kDV];  // partial outputs per 16-lane row group
   const int c = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -110,18 +116,19 @@ __global__ __launch_bounds__(kT) void decode_partial_kernel(DecodeParams p) {
   const int key_lo = c * p.chunk;
   if (key_lo >= L) return;  // uniform across the workgroup
   const int nk = min(p.chunk, L - key_lo);
-  const int g = p.g, nu = p.nu[n], nq = g + 1, nout = g + nu;
-  // Head-map entries, read once into registers before any cache load is in flight: the
-  // 16-bit tables are read with vector loads, and each such read would otherwise wait
-  // for every outstanding load of the chunk.
+  // Head-map entries, read once before any cache load is in flight (the 16-bit tables are
+  // read with vector loads, and each such read would otherwise wait for every outstanding
+  // load of the chunk) and kept in scalar registers: they are uniform.
+  auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+  const int g = p.g, nu = MULTI ? uni(p.nu[n]) : 1, nq = g + 1, nout = g + nu;
   int mem_h[kMaxQ], mem_kv[kMaxQ], ukv[kMaxOut];
 #pragma unroll
   for (int i = 0; i < kMaxQ; ++i) {
-    mem_h[i] = i < g ? p.members[n * g + i] : 0;
-    mem_kv[i] = i < g ? p.kv[mem_h[i]] : -1;
+    mem_h[i] = i < g ? uni(p.members[n * g + i]) : 0;
+    mem_kv[i] = i < g ? uni(p.kv[mem_h[i]]) : -1;
   }
 #pragma unroll
-  for (int u = 0; u < kMaxOut; ++u) ukv[u] = u < nu ? p.ukv[n * g + u] : -1;
+  for (int u = 0; u < kMaxOut; ++u) ukv[u] = u < nu ? uni(p.ukv[n * g + u]) : -1;
 
   // K layout: thread t holds rows t/8 + 32 i (i < 4), dims 8 (t%8) .. +7
   const int krow = tid >> 3, kcol = tid & 7;
@@ -132,38 +139,38 @@ __global__ __launch_bounds__(kT) void decode_partial_kernel(DecodeParams p) {
   // Rows [r0, r0 + ns) of the chunk (relative to key_lo).  Loads are branch-free so the
   // compiler can count them and wait for exactly the ones a step needs: a row past ns
   // re-reads row ns - 1 (in bounds); its score is masked and its weight is zero.
+  // Addresses: a uniform 64-bit base (scalar registers) plus a 32-bit per-lane byte
+  // offset (the host bounds the position stride so chunk offsets fit in 32 bits).
   auto load_k = [&](u32x4(&dst)[kKC], const void* base, const int64_t* st, int head, int r0, int ns) {
-    const __bf16* K = (const __bf16*)base + b * st[0] + head * st[1] + (int64_t)(key_lo + r0) * st[2];
+    const char* K = (const char*)((const __bf16*)base + b * st[0] + head * st[1] + (int64_t)(key_lo + r0) * st[2]);
+    const uint32_t rs = (uint32_t)st[2] * 2u;
 #pragma unroll
     for (int i = 0; i < kKC; ++i) {
-      const int r = min(krow + 32 * i, ns - 1);
-      dst[i] = *(const u32x4*)(K + (int64_t)r * st[2] + 8 * kcol);
+      const uint32_t r = (uint32_t)min(krow + 32 * i, ns - 1);
+      dst[i] = *(const u32x4*)(K + (r * rs + 16u * (uint32_t)kcol));
     }
   };
   auto load_v = [&](int head, int r0, int ns) {
-    const __bf16* V = (const __bf16*)p.v + b * p.sv[0] + head * p.sv[1] + (int64_t)(key_lo + r0) * p.sv[2];
+    const char* V = (const char*)((const __bf16*)p.v + b * p.sv[0] + head * p.sv[1] + (int64_t)(key_lo + r0) * p.sv[2]);
+    const uint32_t rs = (uint32_t)p.sv[2] * 2u;
 #pragma unroll
     for (int i = 0; i < kVC; ++i) {
-      const int r = min(vrow + 16 * i, ns - 1);
-      vr[i] = *(const u32x4*)(V + (int64_t)r * p.sv[2] + 8 * vcol);
+      const uint32_t r = (uint32_t)min(vrow + 16 * i, ns - 1);
+      vr[i] = *(const u32x4*)(V + (r * rs + 16u * (uint32_t)vcol));
     }
   };
-  // this thread's 8 dims of every query, loaded once (qi < g: signal member qi, qi = g: the noise query)
-  u32x4 qv[kMaxQ];
-#pragma unroll
-  for (int qi = 0; qi < kMaxQ; ++qi) {
-    u32x4 x = {0, 0, 0, 0};
-    if (qi <= g) {
-      const __bf16* q = qi < g ? (const __bf16*)p.q1 + b * p.sq1[0] + mem_h[qi] * p.sq1[1]
-                               : (const __bf16*)p.q2 + b * p.sq2[0] + n * p.sq2[1];
-      x = *(const u32x4*)(q + 8 * kcol);
-    }
-    qv[qi] = x;
+  // the group's queries in LDS (each thread reads its 8 dims when scoring):
+  // qs[qi] for qi < g the signal member qi, qs[g] the noise query
+  for (int i = tid; i < (g + 1) * (kD / 8); i += kT) {
+    const int qi = i / (kD / 8), col = i % (kD / 8);
+    const __bf16* q = qi < g ? (const __bf16*)p.q1 + b * p.sq1[0] + mem_h[qi] * p.sq1[1]
+                             : (const __bf16*)p.q2 + b * p.sq2[0] + n * p.sq2[1];
+    QS[qi][col] = *(const u32x4*)(q + 8 * col);
   }
   auto score_rows = [&](int qi, const u32x4(&kr)[kKC]) {
 #pragma unroll
     for (int i = 0; i < kKC; ++i) {
-      const float sc = sum8(dot8(kr[i], qv[qi]));
+      const float sc = sum8(dot8(kr[i], QS[qi][kcol]));
       if (kcol == 0) S[qi][krow + 32 * i] = sc * p.sm_scale_log2;
     }
   };
@@ -197,7 +204,7 @@ __global__ __launch_bounds__(kT) void decode_partial_kernel(DecodeParams p) {
     for (int qi = 0; qi < kMaxQ; ++qi)
       if (qi == g) score_rows(qi, k2r);
 #pragma unroll
-    for (int u = 0; u < kMaxOut; ++u) {
+    for (int u = 0; u < (MULTI ? kMaxOut : 1); ++u) {
       if (u < nu) {
         const int kvh = ukv[u];
         if (u > 0) load_k(k1r, p.k1, p.sk1, kvh, r0, ns);
@@ -219,8 +226,10 @@ __global__ __launch_bounds__(kT) void decode_partial_kernel(DecodeParams p) {
       const float s1 = lane + 64 < ns ? S[qi][lane + 64] : -INFINITY;
       const float mold = ML[0][qi];
       const float mnew = fmaxf(mold, wave_max(fmaxf(s0, s1)));
-      const float e0 = lane < ns ? __builtin_amdgcn_exp2f(s0 - mnew) : 0.f;
-      const float e1 = lane + 64 < ns ? __builtin_amdgcn_exp2f(s1 - mnew) : 0.f;
+      // weights are rounded to bf16 here: P.V consumes them as bf16 and the running sum
+      // accumulates the same rounded values
+      const float e0 = lane < ns ? round_bf16(__builtin_amdgcn_exp2f(s0 - mnew)) : 0.f;
+      const float e1 = lane + 64 < ns ? round_bf16(__builtin_amdgcn_exp2f(s1 - mnew)) : 0.f;
       S[qi][lane] = e0;
       S[qi][lane + 64] = e1;
       const float sum = wave_sum(e0 + e1);
@@ -242,20 +251,13 @@ __global__ __launch_bounds__(kT) void decode_partial_kernel(DecodeParams p) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < kMaxOut; ++u) {
+    for (int u = 0; u < (MULTI ? kMaxOut : 1); ++u) {
       if (u >= nu) continue;
       const int kvh = ukv[u];
       if (u > 0) load_v(kvh, r0, ns);
 #pragma unroll
       for (int i = 0; i < kVC; ++i) {
         const int r = vrow + 16 * i;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w = vr[i][e];
-          v[2 * e] = bf_lo(w);
-          v[2 * e + 1] = bf_hi(w);
-        }
 #pragma unroll
         for (int o = 0; o < kMaxOut; ++o) {
           int src = -1;
@@ -265,11 +267,23 @@ __global__ __launch_bounds__(kT) void decode_partial_kernel(DecodeParams p) {
             src = g;
           }
           if (src >= 0) {
-            const float w = S[src][r];
+            // the bf16 weight as the pairs (w, 0) and (0, w): v_dot2 against a V dword then
+            // yields w * v[2e] and w * v[2e + 1] without converting V to fp32
+            const uint32_t wb = __float_as_uint(S[src][r]) >> 16;
+            const uint32_t wlo = wb, whi = wb << 16;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[o][e] = __builtin_fmaf(w, v[e], acc[o][e]);
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t vw = vr[i][e];
+              acc[o][2 * e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, vw),
+                                                              __builtin_bit_cast(bf16x2, wlo), acc[o][2 * e], false);
+              acc[o][2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, vw),
+                                                                  __builtin_bit_cast(bf16x2, whi), acc[o][2 * e + 1],
+                                                                  false);
+            }
           }
         }
+        // one row's weights live at a time (keeps the kernel at 3 wavefronts per SIMD)
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (nxt < nk) {  // V registers are free: prefetch
@@ -364,10 +378,14 @@ hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t s) {
   if (p.d != kD || p.dv != kDV || p.g + 1 > kMaxQ || p.slots > kMaxOut || p.chunk % kC != 0)
     return hipErrorInvalidValue;
   if (p.nchunks > 0) {
-    if (p.g + 1 <= 4 && p.slots <= 4)
-      hipLaunchKernelGGL(decode_partial_kernel<4>, dim3(p.nchunks, p.Hn, p.B), dim3(kT), 0, s, p);
+    const dim3 grid(p.nchunks, p.Hn, p.B);
+    const bool multi = p.slots > p.g + 1;  // some group uses more than one key/value head
+    if (p.g + 1 <= 4 && p.slots <= 4 && !multi)
+      hipLaunchKernelGGL((decode_partial_kernel<4, false>), grid, dim3(kT), 0, s, p);
+    else if (!multi)
+      hipLaunchKernelGGL((decode_partial_kernel<8, false>), grid, dim3(kT), 0, s, p);
     else
-      hipLaunchKernelGGL(decode_partial_kernel<8>, dim3(p.nchunks, p.Hn, p.B), dim3(kT), 0, s, p);
+      hipLaunchKernelGGL((decode_partial_kernel<8, true>), grid, dim3(kT), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

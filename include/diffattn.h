@@ -121,7 +121,7 @@ da_status gda_fwd(const da_fwd_args* args, void* stream);
  *     0 <= L_b <= Lmax is the caller's contract (the kernels clamp to
  *     [0, Lmax]); L_b == 0 yields a zero output row.
  *   chunk: cached positions per split-K partial (a multiple of 128, at most
- *     2048), 0 = automatic (256).  The result does not depend on it beyond
+ *     2048), 0 = automatic (512).  The result does not depend on it beyond
  *     rounding order.
  *   Everything else as in da_fwd_args (the causal flag is implied). */
 typedef struct da_decode_args {
