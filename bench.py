@@ -2,7 +2,7 @@
 """Benchmark of the fused causal differential-attention forward on one MI355X.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-extra] [--no-cpu-baseline] [--out FILE]
+                  [--no-extra] [--no-cpu-baseline] [--out FILE] [--copy-calibration]
 
 A step is one call of the hot path on one batch of synthetic, seeded input
 already resident in HBM: for the headline workload (the 3B-like Diff
@@ -192,6 +192,19 @@ def bench_decode(w, steps, warmup):
     }
 
 
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
+    """Plain device-to-device copies of a known size: a profiler's FETCH_SIZE / WRITE_SIZE for
+    these dispatches should read nbytes each; the ratio scales the counters of the kernels."""
+    import torch
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"bytes_read_per_copy": nbytes, "bytes_written_per_copy": nbytes, "copies": reps}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -200,6 +213,9 @@ def main():
     ap.add_argument("--workload", default="diff3b_bf16_n4096", choices=[k for k in W.ORDER if k != "tiny_diff_f32"])
     ap.add_argument("--no-extra", action="store_true", help="skip the grouped prefill and decode lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed work, run 3 plain device copies of 1 GiB (reference dispatches that "
+                         "scale the FETCH_SIZE / WRITE_SIZE counters of a profiled run)")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows in the CPU-baseline sample (default: every row of the 4096-token workload)")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
@@ -254,6 +270,8 @@ def main():
         line["roofline_exec"] = head["roofline_exec"]
     line["cpu_baseline"] = cpu
     line["extra"] = extra
+    if args.copy_calibration:
+        line["copy_calibration"] = copy_calibration()
     text = json.dumps(line)
     print(text, flush=True)
     if args.out:

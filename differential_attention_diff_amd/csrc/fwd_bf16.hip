@@ -72,6 +72,7 @@ struct Cfg {
   static constexpr int KCH = KROW / 16;          // 16-B chunks per K row (8 for d = 64)
   static constexpr int VCH = VROW / 16;          // 16-B chunks per V row (16 for dv = 128)
   static constexpr int KSW = (KCH >= 8 ? 8 : KCH) - 1;   // K swizzle mask
+  static constexpr int VSH = VCH >= 16 ? 2 : 1;           // V swizzle: chunk ^ ((r mod 4) << VSH)
   static constexpr int KLOADS = KBYTES / 1024 / kWaves;  // 1-KiB DMA loads per wave per K tile
   static constexpr int VLOADS = VBYTES / 1024 / kWaves;
   static_assert(KLOADS >= 1 && VLOADS >= 1, "tile too small for 4 wavefronts");
@@ -80,15 +81,15 @@ struct Cfg {
 
 // LDS byte offset of 16-B chunk c of row r (XOR swizzle).  K: chunk ^ (r mod
 // 8) spreads the rows an MFMA operand read touches over all banks.  V:
-// chunk ^ 2 (r mod 4) puts the 4 rows a transposing read touches in distinct
-// 32-B bank windows.
+// chunk ^ ((r mod 4) << VSH) puts the 4 rows a transposing read touches in
+// distinct bank windows (64 B apart for dv = 128, 32 B for dv = 64).
 template <int D>
 __device__ __forceinline__ int k_off(int r, int c) {
   return r * Cfg<D>::KROW + ((c ^ (r & Cfg<D>::KSW)) << 4);
 }
 template <int D>
 __device__ __forceinline__ int v_off(int r, int c) {
-  return r * Cfg<D>::VROW + ((c ^ ((r & 3) << 1)) << 4);
+  return r * Cfg<D>::VROW + ((c ^ ((r & 3) << Cfg<D>::VSH)) << 4);
 }
 
 __device__ __forceinline__ float half_swap_max(float x) {
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     for (int i = 0; i < C::VLOADS; ++i) {
       const int j = wave * C::VLOADS + i;
       const int r = j * (1024 / C::VROW) + lane / C::VCH;
-      const uint32_t c16 = (uint32_t)(((lane % C::VCH) ^ ((r & 3) << 1)) << 4);
+      const uint32_t c16 = (uint32_t)(((lane % C::VCH) ^ ((r & 3) << C::VSH)) << 4);
       const uint32_t rr = (uint32_t)min(r, lim);
       __builtin_amdgcn_global_load_lds((const void*)(vb + (rr * rv + c16)),
                                        (lds_void*)(base + 2 * C::KBYTES + j * 1024), 16, 0, 0);
