@@ -12,31 +12,42 @@
 // shared GQA-style).
 //
 // Work decomposition
-//   * A workgroup (4 wavefronts x 32 queries) owns 128 queries of one (batch,
-//     signal head); two workgroups share a CU.  Workgroup ids are remapped so
-//     that each XCD (ids congruent mod 8) walks a contiguous range of (batch,
-//     noise group) items, longest causal block first, the signal heads of a
-//     noise group back to back: the group's K2/Q2 and the head's K1/V stay hot
-//     in that XCD's L2.
+//   * A workgroup owns 128 queries (4 groups of 32) of one (batch, signal
+//     head) and runs 8 wavefronts: one per (query group, softmax map).  The
+//     two wavefronts of a query group share a SIMD, each holds only its own
+//     map's O (64 registers), so a wavefront fits in 256 registers with room
+//     for the pipeline below.  Workgroup ids are remapped so that each XCD (ids
+//     congruent mod 8) walks a contiguous range of items ordered (batch, noise
+//     group, signal head of the group, query block longest causal block
+//     first): the ~32 workgroups an XCD runs at once share one head's K1/V and
+//     the group's K2, about 2 MB, which stays in that XCD's 4 MB L2.
 //   * K1, K2 and V tiles of 64 keys go straight from global memory into a
-//     two-slot LDS ring with global_load_lds_dwordx4 (no staging registers);
-//     16-byte chunks are XOR-swizzled by row so that neither the MFMA operand
-//     reads nor the transposing V reads conflict on LDS banks.  Tile t + 1 is
-//     in flight while tile t is computed; one barrier per tile.
-//   * Tiles below every wavefront's diagonal run a branch-free loop; only the
-//     (at most two) diagonal tiles test which 32-key blocks to skip or mask.
+//     four-slot LDS ring (global_load_lds_dwordx4, no staging registers); the
+//     two tiles after the two being read are in flight.  One barrier per
+//     tile.  16-byte chunks are XOR-swizzled by row so that neither the MFMA
+//     operand reads nor the transposing V reads conflict on LDS banks.  Each
+//     V tile feeds both maps' P.V products.
 //   * Scores are computed transposed, S^T = K Q^T on v_mfma_f32_32x32x16_bf16:
-//     lane (q, half) holds 16 keys of ONE query row, so the row max needs one
-//     v_permlane32_swap and the row sum none until the epilogue.
-//   * Each map keeps its running max m and sum l in fp32 per row; m moves only
-//     when a block's max exceeds it by more than 8 (log2 units), so the O
-//     rescale is rare, weights stay <= 2^8, and O/l is unchanged up to
+//     lane (q, half) holds 16 keys of ONE query row, so a row reduction needs
+//     one v_permlane32_swap and the row sum none until the epilogue.
+//   * Software pipeline over 32-key blocks j, one iteration per block: the
+//     softmax of block j (VALU) is interleaved with the score products of block
+//     j + 1 and the P.V products of block j - 1 (MFMA), and with the LDS
+//     operand reads for the next iteration.
+//   * Each map keeps a reference max m and a sum l in fp32 per row.  A block's
+//     weights are formed against m without computing the block max: one FMA,
+//     one exp2, half a conversion and half a dot2 per score.  Only when some
+//     lane's weights of a block sum past 2^12 (the first block, or a later
+//     block whose scores climb well above m) does the wavefront recompute the
+//     block's scores, move m to the row's running max, rescale O and l, and
+//     form the weights again.  Weights stay <= 2^12 and O/l is unchanged up to
 //     rounding.  l accumulates the bf16-rounded weights the P.V product uses.
-//   * P^T (bf16) feeds O^T += V^T P^T straight from registers; V^T fragments
-//     come from LDS with ds_read_b64_tr_b16 and each feeds the MFMAs of BOTH
-//     maps.
-//   * Epilogue: o = O1/l1 - lambda O2/l2, RMS over dv (in-lane + one swap),
-//     times (1 - lambda_init) w, round to bf16, store; optional LSE.
+//   * Blocks on or past a wavefront's causal diagonal (or past N) are masked;
+//     every wavefront of a workgroup walks the same blocks.
+//   * Epilogue: the map-2 wavefront hands O2/l2 to its partner through LDS;
+//     the map-1 wavefront forms o = O1/l1 - lambda O2/l2, the RMS over dv
+//     (in-lane + one swap), times (1 - lambda_init) w, rounds to bf16 and
+//     stores.  Each wavefront writes its map's LSE when asked.
 #include <math.h>
 
 #include "kernels.h"
@@ -50,20 +61,22 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-constexpr int kWaves = 4;
+constexpr int kGroups = 4;             // query groups per workgroup
+constexpr int kWaves = 2 * kGroups;    // one wavefront per (query group, map)
 constexpr int kQW = 32;                // queries per wavefront (MFMA N dim)
-constexpr int kQB = kWaves * kQW;      // queries per workgroup
+constexpr int kQB = kGroups * kQW;     // queries per workgroup
 constexpr int kKT = 64;                // keys per LDS tile
+constexpr int kKB = 32;                // keys per pipeline block
+constexpr int kSlots = 4;              // LDS ring slots
 constexpr int kThreads = kWaves * 64;
-constexpr float kRescaleSlack = 8.0f;  // log2 units a stale max may lag
+constexpr float kSumLimit = 4096.0f;   // lane weight sum that forces a reference move
 
 template <int D>
 struct Cfg {
-  static constexpr int DV = 2 * D;
+  static constexpr int DV = 2 * D, NCB = DV / 32, NKS = D / 16;
   static constexpr int KROW = D * 2;             // bytes per K row in LDS (no padding; swizzled)
   static constexpr int VROW = DV * 2;            // bytes per V row
   static constexpr int KBYTES = kKT * KROW;      // one K tile
@@ -73,14 +86,21 @@ struct Cfg {
   static constexpr int VCH = VROW / 16;          // 16-B chunks per V row (16 for dv = 128)
   static constexpr int KSW = (KCH >= 8 ? 8 : KCH) - 1;   // K swizzle mask
   static constexpr int VSH = VCH >= 16 ? 2 : 1;           // V swizzle: chunk ^ ((r mod 4) << VSH)
-  static constexpr int KLOADS = KBYTES / 1024 / kWaves;  // 1-KiB DMA loads per wave per K tile
-  static constexpr int VLOADS = VBYTES / 1024 / kWaves;
-  static_assert(KLOADS >= 1 && VLOADS >= 1, "tile too small for 4 wavefronts");
+  static constexpr int KRPL = 1024 / KROW, VRPL = 1024 / VROW;  // rows per KiB
+  // tile DMA: waves 0-1 load K1, 2-3 K2, 4-7 V, TLOADS KiB each
+  static constexpr int TLOADS = STAGE / 1024 / kWaves;
+  static constexpr int QBYTES = kQB * KROW;      // the workgroup's Q1 (or Q2) rows
+  static constexpr int QLOADS = 2 * QBYTES / 1024 / kWaves;
+  static_assert(TLOADS * 2 * 1024 == KBYTES && TLOADS * 4 * 1024 == VBYTES, "tile split over waves");
+  static_assert(QLOADS * 4 * 1024 == QBYTES, "Q split over waves");
   static_assert(VCH >= 8, "V swizzle needs 8 chunks per row");
+  static_assert(KRPL % (KSW + 1) == 0 && VRPL % 4 == 0, "swizzle term must depend on the lane only");
+  static_assert(2 * QBYTES <= STAGE, "Q1 and Q2 are staged in one ring slot");
+  static_assert(kGroups * kQW * DV * 4 <= 2 * STAGE, "O2 hand-off fits in two ring slots");
 };
 
-// LDS byte offset of 16-B chunk c of row r (XOR swizzle).  K: chunk ^ (r mod
-// 8) spreads the rows an MFMA operand read touches over all banks.  V:
+// LDS byte offset of 16-B chunk c of row r (XOR swizzle).  K (and Q): chunk ^
+// (r mod 8) spreads the rows an MFMA operand read touches over all banks.  V:
 // chunk ^ ((r mod 4) << VSH) puts the 4 rows a transposing read touches in
 // distinct bank windows (64 B apart for dv = 128, 32 B for dv = 64).
 template <int D>
@@ -92,139 +112,231 @@ __device__ __forceinline__ int v_off(int r, int c) {
   return r * Cfg<D>::VROW + ((c ^ ((r & 3) << Cfg<D>::VSH)) << 4);
 }
 
+// 16 bytes per lane from gbase + goff straight into LDS: lane l writes LDS bytes
+// [lds + 16 l, lds + 16 l + 16).  Issued as inline assembly so the compiler does
+// not order the ring's LDS reads behind these loads; completion is awaited
+// explicitly (s_waitcnt vmcnt + barrier) before a slot is read.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t goff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(goff), "s"(gbase), "s"(lds)
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// wait until at most `tiles` tiles of T loads each are still in flight
+template <int T>
+__device__ __forceinline__ void wait_tiles_in_flight(int tiles) {
+  if (tiles <= 0)
+    wait_vmcnt<0>();
+  else if (tiles == 1)
+    wait_vmcnt<T>();
+  else if (tiles == 2)
+    wait_vmcnt<2 * T>();
+  else
+    wait_vmcnt<3 * T>();
+}
+__device__ __forceinline__ void wait_lds_and_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// maxima are NaN-propagating (v_maximum3_f32): no operand canonicalisation
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float half_swap_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float half_swap_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ bf16x8 to_bf16x8(const float* a) {
-  f32x8 f = {a[0], a[1], a[2], a[3], a[4], a[5], a[6], a[7]};
-  return __builtin_convertvector(f, bf16x8);
+__device__ __forceinline__ float max16(const f32x16& s) {
+  const float a = vmax(vmax(s[0], s[1]), s[2]), b = vmax(vmax(s[3], s[4]), s[5]);
+  const float c = vmax(vmax(s[6], s[7]), s[8]), d = vmax(vmax(s[9], s[10]), s[11]);
+  const float e = vmax(vmax(s[12], s[13]), s[14]);
+  return vmax(vmax(vmax(a, b), c), vmax(vmax(d, e), s[15]));
 }
 
-// One softmax map's update for a 32-key block held as S^T in `s` (lane = query
-// row, 16 keys per lane half).  Produces the bf16 P^T operands of the two
-// 16-key PV steps and rescales `o` when the reference max moves.
-template <int NCB>
-__device__ __forceinline__ void online_softmax(const f32x16& s, float sc, float& m, float& l, f32x16 (&o)[NCB],
-                                               bf16x8& p0, bf16x8& p1) {
-  float mx = s[0];
+// Per-wavefront pipeline state (one softmax map).  Parity-indexed members
+// alternate between consecutive blocks (indices are compile-time constants).
+template <int D>
+struct St {
+  static constexpr int NCB = Cfg<D>::NCB, NKS = Cfg<D>::NKS;
+  f32x16 o[NCB];            // O^T accumulator
+  f32x16 s[2];              // S^T of block j (parity j) and j + 1
+  bf16x8 p[2][2];           // P^T operands: keys 0-15, 16-31
+  bf16x8 kf[NKS];           // K operands of the next score products
+  bf16x8 vf[NCB][2];        // V^T operands of the next P.V products
+  bf16x8 qf[NKS];
+  float m, l;
+};
+
+// Everything a pipeline step needs besides the state.
+struct Ctx {
+  const unsigned char* ring;
+  int koff;     // byte offset of this wavefront's map in a K tile (0 or KBYTES)
+  int l32, hh, vt_lane;
+  int kmax;     // last key this lane's query sees (causal: its row; else N - 1)
+  int jmask;    // first block that needs a mask for this wavefront
+  float sc;     // log2(e)/sqrt(d)
+};
+
+template <int D>
+__device__ __forceinline__ const unsigned char* slot_of(const Ctx& c, int tile) {
+  return c.ring + (tile % kSlots) * Cfg<D>::STAGE;
+}
+
+// K operands of block jj: A operand of S^T = K Q^T, lane (k, half) holds
+// K[k][16 s + 8 half + 0..7].
+template <int D>
+__device__ __forceinline__ void read_k(bf16x8 (&kf)[Cfg<D>::NKS], const Ctx& c, int jj) {
+  const unsigned char* t = slot_of<D>(c, jj >> 1) + c.koff;
+  const int kr = (jj & 1) * kKB + c.l32;
 #pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-  mx = half_swap_max(mx) * sc;
-  const bool need = mx > m + kRescaleSlack;
-  if (__builtin_amdgcn_ballot_w64(need)) {
-    const float mu = need ? mx : m;
-    const float alpha = __builtin_amdgcn_exp2f(m - mu);
-    m = mu;
-    l *= alpha;
+  for (int s = 0; s < Cfg<D>::NKS; ++s) kf[s] = *(const bf16x8*)(t + k_off<D>(kr, 2 * s + c.hh));
+}
+
+// V^T operands of block jj (32 channels x 16 keys per (cb, ks)): lane j of a
+// 16-lane group reads row (4 half + j/4) at channels c0 + 4 (j%4); the
+// transposing read hands lane i the 4 keys of channel c0 + i.
+template <int D>
+__device__ __forceinline__ void read_v(St<D>& st, const Ctx& c, int jj) {
+  using C = Cfg<D>;
+  const unsigned char* vs = slot_of<D>(c, jj >> 1) + 2 * C::KBYTES;
+  const int r0 = (jj & 1) * kKB + (c.vt_lane >> 8);
 #pragma unroll
-    for (int c = 0; c < NCB; ++c)
+  for (int cb = 0; cb < C::NCB; ++cb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[c][r] *= alpha;
-  }
+    for (int ks = 0; ks < 2; ++ks) {
+      const int row = r0 + ks * 16;
+      const int ch = cb * 32 + (c.vt_lane & 0xff);
+      const int cc = ch >> 3, within = (ch & 7) * 2;
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vs + v_off<D>(row, cc) + within));
+      const bf16x4 hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vs + v_off<D>(row + 8, cc) + within));
+      st.vf[cb][ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ f32x16 score_products(const bf16x8 (&kf)[Cfg<D>::NKS], const bf16x8 (&qf)[Cfg<D>::NKS]) {
+  f32x16 a = {};
+#pragma unroll
+  for (int s = 0; s < Cfg<D>::NKS; ++s) a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[s], a, 0, 0, 0);
+  return a;
+}
+
+template <int D, int PAR>
+__device__ __forceinline__ void pv_products(St<D>& st) {
+#pragma unroll
+  for (int cb = 0; cb < Cfg<D>::NCB; ++cb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      st.o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.vf[cb][ks], st.p[PAR][ks], st.o[cb], 0, 0, 0);
+}
+
+// S^T[r] of lane (q, half) is key k0 + 4 half + 8 (r/4) + r%4; keys past the
+// lane's last visible key are hidden
+__device__ __forceinline__ void mask_scores(f32x16& s, int k0, const Ctx& c) {
+  const int lim = c.kmax - k0 - 4 * c.hh;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = (8 * (r / 4) + (r & 3) > lim) ? -INFINITY : s[r];
+}
+
+// bf16 weights 2^(s sc - m) of a block as the P^T operands of its two 16-key
+// P.V steps; returns the sum of this lane's 16 bf16-rounded weights
+// (v_dot2_f32_bf16 against (1, 1)), i.e. exactly what the P.V product uses.
+__device__ __forceinline__ float block_weights(const f32x16& s, float sc, float m, bf16x8& p0, bf16x8& p1) {
   float pr[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sc, -m));
-  p0 = to_bf16x8(pr);
-  p1 = to_bf16x8(pr + 8);
-  // l accumulates the bf16-rounded weights the PV product uses, so each row of
-  // P/l sums to one up to fp32 rounding (v_dot2_f32_bf16 against (1, 1))
+  const f32x8 lo = {pr[0], pr[1], pr[2], pr[3], pr[4], pr[5], pr[6], pr[7]};
+  const f32x8 hi = {pr[8], pr[9], pr[10], pr[11], pr[12], pr[13], pr[14], pr[15]};
+  p0 = __builtin_convertvector(lo, bf16x8);
+  p1 = __builtin_convertvector(hi, bf16x8);
   const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-  float sum = 0.f;
-  sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p0, p0, 0, 1), one2, sum, false);
-  sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p0, p0, 2, 3), one2, sum, false);
-  sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p0, p0, 4, 5), one2, sum, false);
-  sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p0, p0, 6, 7), one2, sum, false);
-  sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p1, p1, 0, 1), one2, sum, false);
-  sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p1, p1, 2, 3), one2, sum, false);
-  sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p1, p1, 4, 5), one2, sum, false);
-  sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p1, p1, 6, 7), one2, sum, false);
-  l += sum;
+  float t0 = 0.f, t1 = 0.f;
+  t0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p0, p0, 0, 1), one2, t0, false);
+  t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p1, p1, 0, 1), one2, t1, false);
+  t0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p0, p0, 2, 3), one2, t0, false);
+  t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p1, p1, 2, 3), one2, t1, false);
+  t0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p0, p0, 4, 5), one2, t0, false);
+  t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p1, p1, 4, 5), one2, t1, false);
+  t0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p0, p0, 6, 7), one2, t0, false);
+  t1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p1, p1, 6, 7), one2, t1, false);
+  return t0 + t1;
 }
 
-// Per-wavefront state of the forward.
+// Interleave pattern of a step: each MFMA followed by VALU work and LDS operand
+// reads.
 template <int D>
-struct Wave {
-  static constexpr int DV = 2 * D, NCB = DV / 32, NKS = D / 16;
-  f32x16 o1[NCB], o2[NCB];
-  bf16x8 q1f[NKS], q2f[NKS];
-  float m1, m2, l1, l2;
-};
-
-// One 32-key block: rows kr0.. of the tile in LDS slot `stage`, absolute keys
-// k0..  MASK: hide keys past the causal diagonal (or past N when not causal).
-template <int D, bool MASK>
-__device__ __forceinline__ void block32(Wave<D>& w, const unsigned char* stage, int kr0, int k0, int qw0, int l32,
-                                        int hh, int vt_lane, const FwdParams& p) {
-  using C = Cfg<D>;
-  constexpr int NCB = Wave<D>::NCB, NKS = Wave<D>::NKS;
-  const unsigned char* K1s = stage;
-  const unsigned char* K2s = stage + C::KBYTES;
-  const unsigned char* Vs = stage + 2 * C::KBYTES;
-  f32x16 s1, s2;
+__device__ __forceinline__ void step_schedule() {
+  constexpr int NKS = Cfg<D>::NKS, NPV = 2 * Cfg<D>::NCB;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    s1[r] = 0.f;
-    s2[r] = 0.f;
+  for (int i = 0; i < NKS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (scores of block j + 1)
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU (softmax of block j)
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read (K of block j + 2)
   }
-  const int kr = kr0 + l32;  // this lane's key row within the tile (A operand row)
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    const bf16x8 a1 = *(const bf16x8*)(K1s + k_off<D>(kr, 2 * s + hh));
-    const bf16x8 a2 = *(const bf16x8*)(K2s + k_off<D>(kr, 2 * s + hh));
-    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, w.q1f[s], s1, 0, 0, 0);
-    s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, w.q2f[s], s2, 0, 0, 0);
-  }
-  if (MASK) {
-    // S^T[r] of lane (q, half): key k0 + 8 (r/4) + 4 half + r%4, query qw0 + q
-    const int q = qw0 + l32;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = k0 + 8 * (r / 4) + 4 * hh + (r & 3);
-      const bool hide = p.causal ? (key > q) : (key >= p.N);
-      s1[r] = hide ? -INFINITY : s1[r];
-      s2[r] = hide ? -INFINITY : s2[r];
-    }
-  }
-  bf16x8 pa0, pa1, pb0, pb1;
-  const float sc = p.sm_scale_log2;
-  online_softmax<NCB>(s1, sc, w.m1, w.l1, w.o1, pa0, pa1);
-  online_softmax<NCB>(s2, sc, w.m2, w.l2, w.o2, pb0, pb1);
-  // O^T += V^T P^T for both maps; each V^T fragment (32 channels x 16 keys) is read once.
-  // Lane j of a 16-lane group reads row (4 half + j/4) at channels c0 + 4 (j%4): the
-  // transposing read hands lane i the 4 keys of channel c0 + i.
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int row = kr0 + ks * 16 + (vt_lane >> 8);
-      const int ch = cb * 32 + (vt_lane & 0xff);
-      const int c = ch >> 3, within = (ch & 7) * 2;
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Vs + v_off<D>(row, c) + within));
-      const bf16x4 hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Vs + v_off<D>(row + 8, c) + within));
-      const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      w.o1[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ks ? pa1 : pa0, w.o1[cb], 0, 0, 0);
-      w.o2[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ks ? pb1 : pb0, w.o2[cb], 0, 0, 0);
-    }
+  for (int i = 0; i < NPV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (P.V of block j - 1)
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads (V of block j)
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
-  using C = Cfg<D>;
-  constexpr int DV = C::DV, NCB = DV / 32, NKS = D / 16;
-  // the two ring slots are separate objects, so the compiler can tell the DMA into one
-  // slot from the reads of the other (and need not wait for the DMA before reading)
-  __shared__ __attribute__((aligned(1024))) unsigned char slot0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char slot1[C::STAGE];
+// Pipeline iteration for block j (PAR = j mod 2): scores of block j + 1, P.V of
+// block j - 1, softmax of block j, LDS reads of K(j + 2) and V(j).  Past the
+// last block the score products and K reads work on stale ring data and their
+// results are never used; before the first block P(-1) and V(-1) are zero.
+template <int D, int PAR, bool MASK>
+__device__ __forceinline__ void step(St<D>& st, const Ctx& c, int j) {
+  constexpr int NCB = Cfg<D>::NCB;
+  st.s[PAR ^ 1] = score_products<D>(st.kf, st.qf);
+  read_k<D>(st.kf, c, j + 2);
+  pv_products<D, PAR ^ 1>(st);
+  f32x16 sj = st.s[PAR];
+  if (MASK) mask_scores(sj, j * kKB, c);
+  float sum = block_weights(sj, c.sc, st.m, st.p[PAR][0], st.p[PAR][1]);
+  read_v<D>(st, c, j);
+  step_schedule<D>();
+  // keep the weights in this block (they would otherwise sink past the branch below)
+  asm volatile("" ::"v"(st.p[PAR][0]), "v"(st.p[PAR][1]), "v"(sum));
+  // rare: some lane's weights sum past the limit or are not finite (the first
+  // block, where m = -1e30).  Recompute this block's scores (so they need not stay
+  // live), move m to the row's running max, rescale O (which already holds
+  // P(j-1) V(j-1)) and l, and form the weights again.
+  if (__builtin_amdgcn_ballot_w64(!(sum <= kSumLimit))) {
+    asm volatile("" ::: "memory");  // re-read the K operands from LDS
+    bf16x8 kj[Cfg<D>::NKS];
+    read_k<D>(kj, c, j);
+    f32x16 s = score_products<D>(kj, st.qf);
+    if (MASK) mask_scores(s, j * kKB, c);
+    const float mu = vmax(st.m, half_swap_max(max16(s)) * c.sc);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mu);
+    st.m = mu;
+    st.l *= alpha;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[cb][r] *= alpha;
+    sum = block_weights(s, c.sc, st.m, st.p[PAR][0], st.p[PAR][1]);
+  }
+  st.l += sum;
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
+  using C = Cfg<D>;
+  constexpr int DV = C::DV, NCB = C::NCB, NKS = C::NKS;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kSlots * C::STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave % kGroups, map = wave / kGroups;  // map 0: Q1/K1, map 1: Q2/K2
   const int l32 = lane & 31, hh = lane >> 5;
 
   // ---- work item: XCD-contiguous, (batch, noise group) major, longest q-block first
@@ -233,17 +345,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const int bid = blockIdx.x;
   const int xcd = bid & 7, q8 = total >> 3, r8 = total & 7;
   const int logical = xcd * q8 + min(xcd, r8) + (bid >> 3);
-  const int member = logical % p.g;
-  int t = logical / p.g;
-  const int qb = nq - 1 - t % nq;
-  t /= nq;
+  const int qb = nq - 1 - logical % nq;
+  int t = logical / nq;
+  const int member = t % p.g;
+  t /= p.g;
   const int n = t % p.Hn;
   const int b = t / p.Hn;
   const int h = __builtin_amdgcn_readfirstlane(p.members[n * p.g + member]);
   const int kh = __builtin_amdgcn_readfirstlane(p.kv[h]);
   const int q0 = qb * kQB;
-  const int qw0 = q0 + wave * kQW;
-  const bool wave_live = qw0 < p.N;
+  const int qw0 = q0 + grp * kQW;
 
   const __bf16* Q1 = (const __bf16*)p.q1 + b * p.sq1[0] + h * p.sq1[2];
   const __bf16* Q2 = (const __bf16*)p.q2 + b * p.sq2[0] + n * p.sq2[2];
@@ -251,127 +362,183 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const __bf16* K2 = (const __bf16*)p.k2 + b * p.sk2[0] + n * p.sk2[2];
   const __bf16* V = (const __bf16*)p.v + b * p.sv[0] + kh * p.sv[2];
 
-  const int q_end = min(q0 + kQB, p.N);
-  const int kend = p.causal ? q_end : p.N;
-  const int ntiles = (kend + kKT - 1) / kKT;
-  // tiles every wavefront sees whole: all keys <= every query of the block (causal),
-  // or all keys < N (not causal)
-  const int full_tiles = p.causal ? min(ntiles, q0 / kKT) : p.N / kKT;
+  const int kend = p.causal ? min(q0 + kQB, p.N) : p.N;
+  const int nb = (kend + kKB - 1) / kKB;      // 32-key blocks every wavefront walks
+  const int ntiles = (nb + 1) / 2;
 
-  // ---- DMA of one tile into a ring slot: each wave issues its share of 1-KiB
-  // loads; lane l of a load writes LDS bytes [16 l, 16 l + 16) of that KiB, so the
-  // global chunk a lane fetches implements the swizzle.  Rows past N re-read row
-  // N - 1 (in bounds); those keys are always masked (causal: beyond every valid
-  // query; otherwise: >= N).
-  // Addresses: a uniform base per tile (scalar registers) plus a 32-bit per-lane byte
-  // offset, recomputed per tile (rows are clamped to N - 1 on the last tile).
-  const uint32_t rk1 = (uint32_t)p.sk1[1] * 2u, rk2 = (uint32_t)p.sk2[1] * 2u, rv = (uint32_t)p.sv[1] * 2u;
-  auto issue_tile = [&](int tile, unsigned char* base) {
-    const int key0 = tile * kKT;
-    const int lim = p.N - 1 - key0;  // last valid row of this tile
-    const char* k1b = (const char*)(K1 + (int64_t)key0 * p.sk1[1]);
-    const char* k2b = (const char*)(K2 + (int64_t)key0 * p.sk2[1]);
-    const char* vb = (const char*)(V + (int64_t)key0 * p.sv[1]);
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_u8*)ring;
+
+  // ---- tile DMA.  Each wave loads TLOADS KiB of one tensor: waves 0-1 K1, 2-3 K2,
+  // 4-7 V.  Lane l of a 1-KiB load writes LDS bytes [16 l, 16 l + 16) of that KiB,
+  // so the global chunk a lane fetches implements the swizzle; within a KiB the
+  // row is row0 + l / (chunks per row) with row0 a multiple of 4 (V) or 8 (K), so
+  // the swizzle term and the per-lane source offset depend on the lane only.  On
+  // a tile that runs past N, rows past N re-read row N - 1 (in bounds): keys that
+  // are always masked (causal: beyond every valid query; otherwise: >= N).
+  const bool v_wave = wave >= 4;
+  const __bf16* tsrc = v_wave ? V : (wave < 2 ? K1 : K2);
+  const int64_t trow = v_wave ? p.sv[1] : (wave < 2 ? p.sk1[1] : p.sk2[1]);  // element stride of a row
+  const uint32_t trs = (uint32_t)trow * 2u;                                     // byte stride of a row
+  const int rpl = v_wave ? C::VRPL : C::KRPL;
+  const int tblk0 = v_wave ? (wave - 4) * C::TLOADS : (wave & 1) * C::TLOADS;  // first KiB of this wave's share
+  const uint32_t tdst = (v_wave ? 2 * C::KBYTES : (wave < 2 ? 0 : C::KBYTES)) + tblk0 * 1024;
+  const int lrow = v_wave ? lane / C::VCH : lane / C::KCH;
+  const uint32_t lchunk = v_wave ? (uint32_t)(((lane % C::VCH) ^ ((lrow & 3) << C::VSH)) << 4)
+                                 : (uint32_t)(((lane % C::KCH) ^ (lrow & C::KSW)) << 4);
+  const uint32_t loff = (uint32_t)lrow * trs + lchunk;
+  auto issue_tile = [&](int tile) {
+    const uint32_t dst = ring_lds + (tile % kSlots) * C::STAGE + tdst;
+    const int key0 = tile * kKT;  // < N for every tile issued
+    if (key0 + kKT <= p.N) {
+      const char* g = (const char*)(tsrc + (int64_t)(key0 + tblk0 * rpl) * trow);
 #pragma unroll
-    for (int i = 0; i < C::KLOADS; ++i) {
-      const int j = wave * C::KLOADS + i;                  // 1-KiB block of the K tile
-      const int r = j * (1024 / C::KROW) + lane / C::KCH;  // row this lane's 16 B land in
-      const uint32_t c16 = (uint32_t)(((lane % C::KCH) ^ (r & C::KSW)) << 4);  // global chunk for that slot
-      const uint32_t rr = (uint32_t)min(r, lim);
-      __builtin_amdgcn_global_load_lds((const void*)(k1b + (rr * rk1 + c16)), (lds_void*)(base + j * 1024), 16, 0,
-                                       0);
-      __builtin_amdgcn_global_load_lds((const void*)(k2b + (rr * rk2 + c16)),
-                                       (lds_void*)(base + C::KBYTES + j * 1024), 16, 0, 0);
-    }
+      for (int i = 0; i < C::TLOADS; ++i) dma16(g + (uint32_t)(i * rpl) * trs, loff, dst + i * 1024);
+    } else {
+      // rows relative to the tile start, clamped to the last valid row N - 1 - key0 >= 0
+      const char* g = (const char*)(tsrc + (int64_t)key0 * trow);
+      const int lim = p.N - 1 - key0;
 #pragma unroll
-    for (int i = 0; i < C::VLOADS; ++i) {
-      const int j = wave * C::VLOADS + i;
-      const int r = j * (1024 / C::VROW) + lane / C::VCH;
-      const uint32_t c16 = (uint32_t)(((lane % C::VCH) ^ ((r & 3) << C::VSH)) << 4);
-      const uint32_t rr = (uint32_t)min(r, lim);
-      __builtin_amdgcn_global_load_lds((const void*)(vb + (rr * rv + c16)),
-                                       (lds_void*)(base + 2 * C::KBYTES + j * 1024), 16, 0, 0);
+      for (int i = 0; i < C::TLOADS; ++i)
+        dma16(g, (uint32_t)min((tblk0 + i) * rpl + lrow, lim) * trs + lchunk, dst + i * 1024);
     }
   };
+  // before block 2t: blocks 2t and 2t + 1 read tiles t and t + 1.  Wait for this
+  // wave's loads of tile t + 1 (later tiles may stay in flight), then for every
+  // wave's; after the barrier the slot of tile t - 1 is no longer read and
+  // receives tile t + kSlots - 1.
+  static_assert(kSlots >= 4 && kSlots <= 6, "ring depth");
+  auto tile_sync = [&](int tt) {
+    if (tt + 1 >= ntiles) return;
+    wait_tiles_in_flight<C::TLOADS>(min(kSlots - 3, ntiles - tt - 2));
+    wait_lds_and_barrier();
+    if (tt + kSlots - 1 < ntiles) issue_tile(tt + kSlots - 1);
+  };
 
-  if (ntiles > 0) issue_tile(0, slot0);
-
-  Wave<D> w;
-#pragma unroll
-  for (int c = 0; c < NCB; ++c)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      w.o1[c][r] = 0.f;
-      w.o2[c][r] = 0.f;
-    }
-  w.m1 = w.m2 = -1e30f;
-  w.l1 = w.l2 = 0.f;
+  // ---- prologue: Q1 (waves 0-3) and Q2 (waves 4-7) of the workgroup into the last
+  // slot, tiles 0..kSlots-2 into the others
   {
-    // Q fragments: B operand of S^T = K Q^T; lane (q, half) holds Q[q][16s + 8 half + 0..7]
-    const int q = min(qw0 + l32, p.N - 1);  // rows past N: any valid row (results discarded)
+    const bool q2w = wave >= 4;
+    const __bf16* qsrc = q2w ? Q2 : Q1;
+    const int64_t qrow = q2w ? p.sq2[1] : p.sq1[1];
+    const uint32_t qrs = (uint32_t)qrow * 2u;
+    const int qblk0 = (wave & 3) * C::QLOADS;
+    const int kr_l = lane / C::KCH;
+    const uint32_t kc_l = (uint32_t)(((lane % C::KCH) ^ (kr_l & C::KSW)) << 4);
+    const uint32_t qdst = ring_lds + (kSlots - 1) * C::STAGE + (q2w ? C::QBYTES : 0) + qblk0 * 1024;
+    const int lim = p.N - 1 - q0;  // query rows past N re-read row N - 1 (never stored)
+    const char* g = (const char*)(qsrc + (int64_t)q0 * qrow);
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-      const u32x4 a = *(const u32x4*)(Q1 + (int64_t)q * p.sq1[1] + 16 * s + 8 * hh);
-      const u32x4 c = *(const u32x4*)(Q2 + (int64_t)q * p.sq2[1] + 16 * s + 8 * hh);
-      w.q1f[s] = __builtin_bit_cast(bf16x8, a);
-      w.q2f[s] = __builtin_bit_cast(bf16x8, c);
-    }
+    for (int i = 0; i < C::QLOADS; ++i)
+      dma16(g, (uint32_t)min((qblk0 + i) * C::KRPL + kr_l, lim) * qrs + kc_l, qdst + i * 1024);
   }
-  // lane's (row within a 16-key step) << 8 | channel offset within a 32-channel block
-  const int vt_lane = ((4 * hh + (lane & 15) / 4) << 8) | (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  for (int tt = 0; tt < min(ntiles, kSlots - 1); ++tt) issue_tile(tt);
+  wait_tiles_in_flight<C::TLOADS>(min(ntiles, kSlots - 1) - 1);  // the Q rows and tile 0 have landed
+  wait_lds_and_barrier();
 
-  // ---- tiles every wavefront sees whole: branch-free; unrolled by two so that each
-  // step reads one named slot while the DMA fills the other
-  auto full_step = [&](int tile, const unsigned char* cur, unsigned char* nxt) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's share of the tile (issued a step ago) has landed
-    __syncthreads();                // ... every wave's; and the other slot is no longer read
-    if (tile + 1 < ntiles) issue_tile(tile + 1, nxt);
-    block32<D, false>(w, cur, 0, tile * kKT, qw0, l32, hh, vt_lane, p);
-    block32<D, false>(w, cur, 32, tile * kKT + 32, qw0, l32, hh, vt_lane, p);
-  };
-  int tile = 0;
-  for (; tile + 1 < full_tiles; tile += 2) {
-    full_step(tile, slot0, slot1);
-    full_step(tile + 1, slot1, slot0);
-  }
-  if (tile < full_tiles) {
-    full_step(tile, slot0, slot1);
-    ++tile;
-  }
-  // ---- the diagonal tiles (causal) or the ragged last tile: per 32-key block,
-  // skip it (entirely above this wavefront's queries), mask it, or take it whole
-  for (; tile < ntiles; ++tile) {
-    unsigned char* cur = (tile & 1) ? slot1 : slot0;
-    unsigned char* nxt = (tile & 1) ? slot0 : slot1;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tile + 1 < ntiles) issue_tile(tile + 1, nxt);
+  Ctx c;
+  c.ring = ring;
+  c.koff = map * C::KBYTES;
+  c.l32 = l32;
+  c.hh = hh;
+  c.vt_lane = ((4 * hh + (lane & 15) / 4) << 8) | (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  c.kmax = p.causal ? qw0 + l32 : p.N - 1;
+  c.jmask = p.causal ? qw0 / kKB : p.N / kKB;
+  c.sc = p.sm_scale_log2;
+
+  St<D> st;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int k0 = tile * kKT + kb * 32;
-      if (!wave_live || k0 >= kend) continue;
-      if (p.causal && k0 > qw0 + kQW - 1) continue;
-      const bool mask = p.causal ? (k0 + 31 > qw0) : (k0 + 32 > p.N);
-      if (mask)
-        block32<D, true>(w, cur, kb * 32, k0, qw0, l32, hh, vt_lane, p);
-      else
-        block32<D, false>(w, cur, kb * 32, k0, qw0, l32, hh, vt_lane, p);
-    }
+  for (int cb = 0; cb < NCB; ++cb) st.o[cb] = f32x16{};
+  st.m = -1e30f;
+  st.l = 0.f;
+  {
+    // Q fragments: B operand of S^T = K Q^T; lane (q, half) holds Q[q][16 s + 8 half + 0..7]
+    const unsigned char* qs = ring + (kSlots - 1) * C::STAGE + map * C::QBYTES;
+    const int qr = grp * kQW + l32;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) st.qf[s] = *(const bf16x8*)(qs + k_off<D>(qr, 2 * s + hh));
   }
+  // P(-1) and V(-1) are zero: the first step's P.V adds nothing
+  st.p[1][0] = st.p[1][1] = bf16x8{};
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) st.vf[cb][0] = st.vf[cb][1] = bf16x8{};
+  read_k<D>(st.kf, c, 0);
+  st.s[0] = score_products<D>(st.kf, st.qf);
+  read_k<D>(st.kf, c, 1);
 
-  if (!wave_live) return;
+  // ---- the pipeline; tile t's sync precedes block 2t.  Blocks before this
+  // wavefront's first masked block run unmasked; every wavefront runs the same
+  // sequence of syncs.
+  const int jm = min(c.jmask, nb);
+  int j = 0;
+  for (; j + 1 < jm; j += 2) {
+    tile_sync(j >> 1);
+    step<D, 0, false>(st, c, j);
+    step<D, 1, false>(st, c, j + 1);
+  }
+  if (j < jm) {  // jm odd: one more unmasked (even) block
+    tile_sync(j >> 1);
+    step<D, 0, false>(st, c, j);
+    ++j;
+  }
+  // the masked blocks recompute the lane constants from an opaque lane index, so
+  // nothing derived for the loop above has to stay live across it
+  Ctx cm = c;
+  {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    cm.l32 = ln & 31;
+    cm.hh = ln >> 5;
+    cm.vt_lane = ((4 * cm.hh + (ln & 15) / 4) << 8) | (16 * ((ln >> 4) & 1) + 4 * (ln & 3));
+    cm.kmax = p.causal ? qw0 + cm.l32 : p.N - 1;
+  }
+  if ((j & 1) && j < nb) {  // first masked block is odd
+    step<D, 1, true>(st, cm, j);
+    ++j;
+  }
+  for (; j < nb; j += 2) {
+    tile_sync(j >> 1);
+    step<D, 0, true>(st, cm, j);
+    if (j + 1 < nb) step<D, 1, true>(st, cm, j + 1);
+  }
+  // drain: P(nb-1) V(nb-1)
+  if ((nb - 1) & 1)
+    pv_products<D, 1>(st);
+  else
+    pv_products<D, 0>(st);
 
-  // ---- epilogue: o = O1/l1 - lambda O2/l2, then the head RMS norm
-  const float l1 = half_swap_sum(w.l1), l2 = half_swap_sum(w.l2);
-  const float i1 = 1.0f / l1, i2 = 1.0f / l2;
+  // ---- epilogue.  The ring is free once every wave is past its last read (all
+  // tile loads were awaited before their tiles were read).
+  wait_lds_and_barrier();
+  const float lsum = half_swap_sum(st.l);
+  const float inv = 1.0f / lsum;
+  const int q = qw0 + l32;
+  if (p.lse && hh == 0 && q < p.N) {
+    const int64_t base = ((int64_t)b * p.Hs + h) * p.N + q;
+    constexpr float kLn2 = 0.69314718055994531f;
+    p.lse[(int64_t)map * p.B * p.Hs * p.N + base] = (st.m + __log2f(lsum)) * kLn2;
+  }
+  // hand-off of O2/l2 in the accumulator layout: register r of lane l of query
+  // group g at float index ((g NCB + cb) 16 + r) 64 + l
+  float* xo = (float*)ring;
+  if (map == 1) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[((grp * NCB + cb) * 16 + r) * 64 + lane] = __fmul_rn(st.o[cb][r], inv);
+  }
+  __syncthreads();
+  if (map == 1 || qw0 >= p.N) return;
+
+  // o = O1/l1 - lambda O2/l2, then the head RMS norm
   float ss = 0.f;
 #pragma unroll
-  for (int c = 0; c < NCB; ++c)
+  for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       // both maps take identical operations: identical maps with lambda = 1 give exact zeros
-      const float x = __builtin_fmaf(-p.lam, __fmul_rn(w.o2[c][r], i2), __fmul_rn(w.o1[c][r], i1));
-      w.o1[c][r] = x;
+      const float o2 = xo[((grp * NCB + cb) * 16 + r) * 64 + lane];
+      const float x = __builtin_fmaf(-p.lam, o2, __fmul_rn(st.o[cb][r], inv));
+      st.o[cb][r] = x;
       ss = __builtin_fmaf(x, x, ss);
     }
   float scale = 1.0f;
@@ -379,30 +546,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     ss = half_swap_sum(ss);
     scale = (1.0f - p.lam_init) / sqrtf(ss * (1.0f / DV) + p.eps);
   }
-  const int q = qw0 + l32;
   if (q < p.N) {
     __bf16* out = (__bf16*)p.out + b * p.so[0] + (int64_t)q * p.so[1] + h * p.so[2];
 #pragma unroll
-    for (int c = 0; c < NCB; ++c)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int ch = c * 32 + 8 * g4 + 4 * hh;  // channels ch..ch+3 live in o1[c][4 g4 .. 4 g4 + 3]
+        const int ch = cb * 32 + 8 * g4 + 4 * hh;  // channels ch..ch+3 live in o[cb][4 g4 .. 4 g4 + 3]
         f32x4 wv = {1.f, 1.f, 1.f, 1.f};
         if (p.normalize && p.norm_w) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) wv[e] = p.norm_w[ch + e];
         }
-        f32x4 y = {w.o1[c][4 * g4] * scale * wv[0], w.o1[c][4 * g4 + 1] * scale * wv[1],
-                   w.o1[c][4 * g4 + 2] * scale * wv[2], w.o1[c][4 * g4 + 3] * scale * wv[3]};
+        f32x4 y = {st.o[cb][4 * g4] * scale * wv[0], st.o[cb][4 * g4 + 1] * scale * wv[1],
+                   st.o[cb][4 * g4 + 2] * scale * wv[2], st.o[cb][4 * g4 + 3] * scale * wv[3]};
         *(bf16x4*)(out + ch) = __builtin_convertvector(y, bf16x4);
       }
-    if (p.lse && hh == 0) {
-      const int64_t base = ((int64_t)b * p.Hs + h) * p.N + q;
-      const int64_t plane = (int64_t)p.B * p.Hs * p.N;
-      constexpr float kLn2 = 0.69314718055994531f;
-      p.lse[base] = (w.m1 + __log2f(l1)) * kLn2;
-      p.lse[plane + base] = (w.m2 + __log2f(l2)) * kLn2;
-    }
   }
 }
 
