@@ -101,6 +101,34 @@ def test_large_logits_key_shift_invariance():
     assert_parity(as64(a), want, "bf16", "unshifted keys vs shifted oracle")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_scores_climbing_along_the_keys(causal):
+    # Scores that climb with the key position (map 1) or fall with it (map 2): a
+    # running max set early is exceeded by far again and again later in each row,
+    # so the kernels' lazy reference must move (and O, l be rescaled) many times.
+    # Keys k_j = r_j + (j / 2) e with e = 1/8 in every channel and queries
+    # q = r + e: q.k_j grows by about |e|^2 / 2 = 0.5 per key (raw units).
+    B, N, H, d = 1, 520, 2, 64
+    g = torch.Generator().manual_seed(41)
+    e = torch.full((d,), 0.125)
+    ramp = (torch.arange(N, dtype=torch.float32) / 2.0)[None, :, None, None] * e
+    q1 = (torch.randn(B, N, H, d, generator=g) + e).bfloat16()
+    k1 = (torch.randn(B, N, H, d, generator=g) + ramp).bfloat16()
+    q2 = (torch.randn(B, N, H, d, generator=g) + e).bfloat16()
+    k2 = (torch.randn(B, N, H, d, generator=g) - ramp).bfloat16()
+    v = torch.randn(B, N, H, 2 * d, generator=g).bfloat16()
+    inp = {"q1": q1, "q2": q2, "k1": k1, "k2": k2, "v": v}
+    # causal rows see ever larger logits: the first map's log-sum-exp of the last row
+    # exceeds that of the first block's rows by far (natural units)
+    lse = O.diff_attention_lse(q1, q2, k1, k2, rows=np.arange(N), causal=True)  # [2, B, N, H]
+    assert np.min(lse[0][:, -1, :]) - np.max(lse[0][:, :32, :]) > 20.0
+    for f in (torch.float32, torch.bfloat16):
+        x = {k: t.to(f) for k, t in inp.items()}
+        got = fwd(x, 0.6, 0.6, causal=causal)
+        want = O.diff_attention(q1, q2, k1, k2, v, 0.6, 0.6, causal=causal)
+        assert_parity(as64(got), want, "bf16" if f == torch.bfloat16 else "f32", f"climbing scores {f}")
+
+
 def test_bitwise_deterministic():
     inp = rand_inputs(B=2, N=700, hs=6, hn=2, hkv=6, d=64, dtype=torch.bfloat16, seed=37)
     d = to_dev(inp)
