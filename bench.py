@@ -22,6 +22,7 @@ bounded sample of the same workload on the host's cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -38,6 +39,37 @@ from differential_attention_diff_amd import workloads as W  # noqa: E402
 METRIC = "diff-attn fwd TFLOP/s (% bf16 MFMA peak) at seq 4096; decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+# HBM bytes per launch of the dominant kernel, from rocprofv3 FETCH_SIZE and WRITE_SIZE
+# passes (KiB per dispatch) scaled by what the same counters read for a plain 1 GiB
+# device copy in the same run (FETCH x 2.0, WRITE x 1.0); see
+# profiles/fwd_bf16_decode_hbm_counters.md.  Valid only for the kernel source the
+# counters were taken on (sha256 of the .hip file); reported as null otherwise.
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "differential_attention_diff_amd", "csrc")
+MEASURED_TRAFFIC = {
+    "fwd_bf16.hip": {
+        "sha256": "2c2394a183614507e23097d0ce97e02a470ef59278360203b090e2d1594be902",
+        "diff3b_bf16_n4096": 147783 * 1024 * 2.0 + 98304 * 1024 * 1.0,
+        "gda3to1_bf16_n4096": 97760 * 1024 * 2.0 + 73728 * 1024 * 1.0,
+    },
+    "decode_bf16.hip": {
+        "sha256": "e35c514fa96504b42227b4c515a18bcb446d58ea96aede928d37073be61a5b02",
+        "gda_decode_bf16_b64_l8192": 586361 * 1024 * 2.0 + 9679 * 1024 * 1.0,  # decode_partial_kernel
+    },
+}
+
+
+def measured_traffic(source: str, workload: str):
+    """Counter-derived HBM bytes per launch, or None if absent or the kernel source changed."""
+    entry = MEASURED_TRAFFIC.get(source)
+    if entry is None or workload not in entry:
+        return None
+    try:
+        with open(os.path.join(CSRC, source), "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    return entry[workload] if digest == entry["sha256"] else None
 
 
 # ---------------------------------------------------------------------------
@@ -160,7 +192,7 @@ def bench_prefill(w, steps, warmup, inp=None):
                    "dv": w.dv, "causal": w.causal, "entry": "diffattn_fwd" if plain else "gda_fwd",
                    "flop_convention": "F_alg"},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic("fwd_bf16.hip", w.name),
                      "flops_per_launch": fa, "kernel": "fwd_bf16_kernel<64>"},
         "roofline_exec": {"achieved": ache, "frac": ache / PEAK_BF16_TFLOPS, "flops_per_launch": fe},
         "algorithmic_bytes": prefill_bytes(w),
@@ -187,7 +219,8 @@ def bench_decode(w, steps, warmup):
                    "sum_seq_lens": int(inp["seq_lens"].sum()), "H_s": w.H_s, "H_n": w.H_n, "H_kv": w.H_kv,
                    "d": w.d, "dv": w.dv, "entry": "gda_decode"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": gbs / PEAK_HBM_GBS, "traffic": None, "bytes_per_launch": nb,
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("decode_bf16.hip", w.name),
+                     "bytes_per_launch": nb,
                      "kernel": "decode_partial_kernel + decode_combine_kernel (step time)"},
     }
 
