@@ -329,15 +329,40 @@ __global__ __launch_bounds__(kT) void decode_combine_kernel(DecodeParams p) {
   const float* base = p.ws + ((int64_t)b * p.Hn + n) * p.nchunks * cstride;
   const int c0 = 2 * lane;
   for (int o = wave; o < nout; o += kT / 64) {
+    // chunk maxima and sums: lane c holds chunk c (64 chunks per pass), all loads
+    // of a pass in flight together
     float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, base[c * cstride + o * (kDV + 2)]);
+    for (int cb = 0; cb < nch; cb += 64) {
+      const int c = cb + lane;
+      M = fmaxf(M, c < nch ? base[c * cstride + o * (kDV + 2)] : -INFINITY);
+    }
+    M = wave_max(M);
     float Ls = 0.f, a0 = 0.f, a1 = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const float* s = base + c * cstride + o * (kDV + 2);
-      const float f = __builtin_amdgcn_exp2f(s[0] - M);
-      Ls = __builtin_fmaf(s[1], f, Ls);
-      a0 = __builtin_fmaf(s[2 + c0], f, a0);
-      a1 = __builtin_fmaf(s[3 + c0], f, a1);
+    for (int cb = 0; cb < nch; cb += 64) {
+      const int c = cb + lane;
+      const float* sc = base + min(c, nch - 1) * cstride + o * (kDV + 2);
+      const float f = c < nch ? __builtin_amdgcn_exp2f(sc[0] - M) : 0.f;
+      Ls += wave_sum(sc[1] * f);
+      // channel pair c0, c0 + 1 of every chunk of the pass, weighted by its chunk's
+      // factor (broadcast from lane k); 8 chunks' loads in flight at a time.  Slots
+      // past the last chunk re-read the last chunk (in bounds) with factor 0.
+      const int n_pass = min(64, nch - cb);
+      for (int k0 = 0; k0 < n_pass; k0 += 8) {
+        float v0[8], v1[8], fk[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int k = k0 + u;  // <= 63
+          fk[u] = lane_f(f, k);
+          const float* sk = base + min(cb + k, nch - 1) * cstride + o * (kDV + 2);
+          v0[u] = sk[2 + c0];
+          v1[u] = sk[3 + c0];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          a0 = __builtin_fmaf(v0[u], fk[u], a0);
+          a1 = __builtin_fmaf(v1[u], fk[u], a1);
+        }
+      }
     }
     merged[o][2 + c0] = a0;
     merged[o][3 + c0] = a1;
