@@ -14,7 +14,8 @@ the C ABI).  One JSON line is printed; `value` is F_alg TFLOP/s (each product
 of the DiffAttn equation counted once, causal pairs only).  The same line
 carries the roofline of the kernel (against the 2.5 PFLOP/s dense bf16 MFMA
 peak), the F_exec view (F_alg plus the second P.V an exact one-pass kernel
-must issue), the grouped (3:1) prefill and the split-K decode (HBM GB/s
+must issue), the grouped (3:1) prefill, the packed variable-length prefill
+(8 sequences of 256..4096 tokens in one call) and the split-K decode (HBM GB/s
 against 8 TB/s) measured the same way, and the fp64 CPU oracle timed on a
 bounded sample of the same workload on the host's cores.
 """
@@ -199,6 +200,32 @@ def bench_prefill(w, steps, warmup, inp=None):
     }
 
 
+def bench_varlen(w, steps, warmup):
+    """Packed prefill: F_alg summed over the sequences' own causal pairs."""
+    import torch
+    from differential_attention_diff_amd import ops
+    inp = W.make_varlen_inputs(w)
+    d = {k: (v.cuda() if hasattr(v, "cuda") else v) for k, v in inp.items()}
+    T = d["q1"].shape[0]
+    out = torch.empty(T, w.H_s, w.dv, dtype=w.torch_dtype, device="cuda")
+    fn = lambda: ops.gda_fwd_varlen(d["q1"], d["q2"], d["k1"], d["k2"], d["v"], d["cu_seqlens"], d["max_seqlen"],
+                                    w.lam, w.lam_init, out=out, eps=w.eps)
+    ms = time_steps(fn, steps, warmup)
+    lengths = np.diff(inp["cu_seqlens"].numpy().astype(np.int64))
+    per_pair = w.H_s * 2 * w.d + w.H_n * 2 * w.d + w.H_s * 2 * w.dv
+    fa = int(np.sum(lengths * (lengths + 1) // 2)) * per_pair
+    ach = fa / (ms * 1e-3) / 1e12
+    return {
+        "workload": w.name, "value": ach, "unit": "TFLOP/s", "ms_per_step": ms,
+        "config": {"workload": w.name, "nseq": w.B, "lengths": lengths.tolist(), "tokens": T,
+                   "max_seqlen": d["max_seqlen"], "H_s": w.H_s, "H_n": w.H_n, "H_kv": w.H_kv, "d": w.d, "dv": w.dv,
+                   "causal": True, "entry": "gda_fwd_varlen", "flop_convention": "F_alg"},
+        "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic("fwd_bf16.hip", w.name),
+                     "flops_per_launch": fa, "kernel": "fwd_bf16_kernel<64>"},
+    }
+
+
 def bench_decode(w, steps, warmup):
     import torch
     from differential_attention_diff_amd import ops
@@ -243,8 +270,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="diff3b_bf16_n4096", choices=[k for k in W.ORDER if k != "tiny_diff_f32"])
-    ap.add_argument("--no-extra", action="store_true", help="skip the grouped prefill and decode lines")
+    ap.add_argument("--workload", default="diff3b_bf16_n4096",
+                    choices=[k for k in W.ORDER if k != "tiny_diff_f32"] + ["gda3to1_varlen_bf16_8x4096"])
+    ap.add_argument("--no-extra", action="store_true", help="skip the grouped, packed and decode lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed work, run 3 plain device copies of 1 GiB (reference dispatches that "
@@ -271,17 +299,19 @@ def main():
 
     import torch
     print(f"[bench] GPU {torch.cuda.get_device_name(0)}: timing {w.name}", file=sys.stderr, flush=True)
-    head = bench_prefill(w, args.steps, args.warmup, inp) if w.kind == "prefill" else \
-        bench_decode(w, args.steps, args.warmup)
+    if w.kind == "prefill":
+        head = bench_prefill(w, args.steps, args.warmup, inp)
+    else:
+        head = (bench_varlen if w.kind == "varlen" else bench_decode)(w, args.steps, args.warmup)
     extra = []
     if not args.no_extra:
-        for name in ("gda3to1_bf16_n4096", "gda_decode_bf16_b64_l8192"):
+        for name in ("gda3to1_bf16_n4096", "gda_decode_bf16_b64_l8192", "gda3to1_varlen_bf16_8x4096"):
             if name == w.name:
                 continue
             ew = W.WORKLOADS[name]
             print(f"[bench] timing {name}", file=sys.stderr, flush=True)
-            extra.append(bench_prefill(ew, args.steps, args.warmup) if ew.kind == "prefill"
-                         else bench_decode(ew, args.steps, args.warmup))
+            run = {"prefill": bench_prefill, "decode": bench_decode, "varlen": bench_varlen}[ew.kind]
+            extra.append(run(ew, args.steps, args.warmup))
 
     line = {
         "metric": METRIC,

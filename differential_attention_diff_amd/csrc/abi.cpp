@@ -108,11 +108,30 @@ da_status check_common_shapes(int64_t B, int64_t N, int64_t Hs, int64_t Hn, int6
   return DA_OK;
 }
 
-da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain) {
+// Packed sequences of the varlen entry point (cu == nullptr: fixed-length batch).
+struct Packing {
+  const int32_t* cu;
+  int64_t nseq, max_seqlen;
+};
+
+constexpr int kMaxGridYZ = 65535;  // grid y/z limit of the fp32 kernel's launch
+
+da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain, const Packing* pk = nullptr) {
   if (!a) return fail(DA_EINVAL, "args is NULL");
   da_status st = check_common_shapes(a->B, a->N, a->H_s, a->H_n, a->H_kv, a->d, a->dv, a->dtype, a->lambda,
                                      a->lambda_init, a->eps);
   if (st != DA_OK) return st;
+  if (pk) {
+    if (a->B != 1) return fail(DA_EINVAL, "packed sequences need B == 1 (got %lld)", (long long)a->B);
+    if (pk->nseq < 0 || pk->nseq > INT32_MAX) return fail(DA_EINVAL, "nseq = %lld out of range", (long long)pk->nseq);
+    if (pk->max_seqlen < 0 || pk->max_seqlen > a->N)
+      return fail(DA_EINVAL, "max_seqlen = %lld outside [0, N = %lld]", (long long)pk->max_seqlen, (long long)a->N);
+    if (pk->nseq > 0 && !pk->cu) return fail(DA_EINVAL, "cu_seqlens is NULL");
+    if (pk->cu && ((uintptr_t)pk->cu & 3u)) return fail(DA_EINVAL, "cu_seqlens is not 4-byte aligned");
+  }
+  const int64_t nseq = pk ? pk->nseq : a->B, max_seqlen = pk ? pk->max_seqlen : a->N;
+  if (a->dtype == DA_F32 && nseq > kMaxGridYZ)
+    return fail(DA_EUNSUPPORTED, "the fp32 kernel takes at most %d sequences per call", kMaxGridYZ);
   if (a->flags & ~(uint32_t)(DA_CAUSAL | DA_NO_NORM)) return fail(DA_EINVAL, "unknown flag bits 0x%x", a->flags);
   if (plain) {
     if (a->H_n != a->H_s || a->H_kv != a->H_s)
@@ -124,7 +143,8 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain) {
   if ((st = resolve_maps((int)a->H_s, (int)a->H_n, (int)a->H_kv, a->noise_of_signal, a->kv_of_signal, p.nz, p.kv,
                          p.members)) != DA_OK)
     return st;
-  if (a->B == 0 || a->N == 0) return DA_OK;  // empty: no pointer is touched (torch gives NULL for empty tensors)
+  if (a->B == 0 || a->N == 0 || nseq == 0 || max_seqlen == 0)
+    return DA_OK;  // empty: no pointer is touched (torch gives NULL for empty tensors)
 
   const int es = a->dtype == DA_BF16 ? 2 : 4;
   struct T {
@@ -168,6 +188,9 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain) {
   p.out = a->out;
   p.norm_w = a->norm_w;
   p.lse = a->lse;
+  p.cu_seqlens = pk ? pk->cu : nullptr;
+  p.nseq = (int)nseq;
+  p.max_seqlen = (int)max_seqlen;
   for (int i = 0; i < 3; ++i) {
     p.sq1[i] = a->s_q1[i];
     p.sq2[i] = a->s_q2[i];
@@ -315,6 +338,12 @@ extern "C" {
 da_status diffattn_fwd(const da_fwd_args* args, void* stream) { return fwd_impl(args, stream, true); }
 
 da_status gda_fwd(const da_fwd_args* args, void* stream) { return fwd_impl(args, stream, false); }
+
+da_status gda_fwd_varlen(const da_fwd_args* args, const int32_t* cu_seqlens, int64_t nseq, int64_t max_seqlen,
+                         void* stream) {
+  const Packing pk{cu_seqlens, nseq, max_seqlen};
+  return fwd_impl(args, stream, false, &pk);
+}
 
 size_t gda_decode_workspace_bytes(const da_decode_args* args) {
   da::DecodeParams p;

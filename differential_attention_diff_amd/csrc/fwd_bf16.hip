@@ -339,30 +339,51 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   const int grp = wave % kGroups, map = wave / kGroups;  // map 0: Q1/K1, map 1: Q2/K2
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // ---- work item: XCD-contiguous, (batch, noise group) major, longest q-block first
-  const int nq = (p.N + kQB - 1) / kQB;
-  const int total = p.B * p.Hs * nq;
+  // ---- work item: XCD-contiguous, query block fastest (longest first)
+  const int nq = (p.max_seqlen + kQB - 1) / kQB;
+  const int total = p.nseq * p.Hs * nq;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, q8 = total >> 3, r8 = total & 7;
   const int logical = xcd * q8 + min(xcd, r8) + (bid >> 3);
   const int qb = nq - 1 - logical % nq;
-  int t = logical / nq;
-  const int member = t % p.g;
-  t /= p.g;
-  const int n = t % p.Hn;
-  const int b = t / p.Hn;
+  int t = logical / nq, member, n, sq;  // sq: sequence
+  if (p.cu_seqlens) {
+    // packed sequences of unequal lengths: sequence fastest, so the contiguous
+    // range each XCD walks holds every sequence's share of the work
+    sq = t % p.nseq;
+    t /= p.nseq;
+    member = t % p.g;
+    n = t / p.g;
+  } else {
+    member = t % p.g;
+    t /= p.g;
+    n = t % p.Hn;
+    sq = t / p.Hn;
+  }
   const int h = __builtin_amdgcn_readfirstlane(p.members[n * p.g + member]);
   const int kh = __builtin_amdgcn_readfirstlane(p.kv[h]);
   const int q0 = qb * kQB;
   const int qw0 = q0 + grp * kQW;
 
-  const __bf16* Q1 = (const __bf16*)p.q1 + b * p.sq1[0] + h * p.sq1[2];
-  const __bf16* Q2 = (const __bf16*)p.q2 + b * p.sq2[0] + n * p.sq2[2];
-  const __bf16* K1 = (const __bf16*)p.k1 + b * p.sk1[0] + kh * p.sk1[2];
-  const __bf16* K2 = (const __bf16*)p.k2 + b * p.sk2[0] + n * p.sk2[2];
-  const __bf16* V = (const __bf16*)p.v + b * p.sv[0] + kh * p.sv[2];
+  // the sequence: batch b, tokens [tok0, tok0 + N).  Packed sequences live in
+  // batch 0 at the offsets cu_seqlens gives, clamped to the token axis.
+  int b = sq, tok0 = 0, N = p.N;
+  if (p.cu_seqlens) {
+    const int s0 = p.cu_seqlens[sq], s1 = p.cu_seqlens[sq + 1];
+    b = 0;
+    tok0 = min(max(s0, 0), p.N);
+    N = max(min(min(s1, p.N) - tok0, p.max_seqlen), 0);
+  }
+  if (q0 >= N) return;  // whole workgroup: no query row of this block exists
 
-  const int kend = p.causal ? min(q0 + kQB, p.N) : p.N;
+  const int64_t t0 = tok0;
+  const __bf16* Q1 = (const __bf16*)p.q1 + b * p.sq1[0] + t0 * p.sq1[1] + h * p.sq1[2];
+  const __bf16* Q2 = (const __bf16*)p.q2 + b * p.sq2[0] + t0 * p.sq2[1] + n * p.sq2[2];
+  const __bf16* K1 = (const __bf16*)p.k1 + b * p.sk1[0] + t0 * p.sk1[1] + kh * p.sk1[2];
+  const __bf16* K2 = (const __bf16*)p.k2 + b * p.sk2[0] + t0 * p.sk2[1] + n * p.sk2[2];
+  const __bf16* V = (const __bf16*)p.v + b * p.sv[0] + t0 * p.sv[1] + kh * p.sv[2];
+
+  const int kend = p.causal ? min(q0 + kQB, N) : N;
   const int nb = (kend + kKB - 1) / kKB;      // 32-key blocks every wavefront walks
   const int ntiles = (nb + 1) / 2;
 
@@ -389,14 +410,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   auto issue_tile = [&](int tile) {
     const uint32_t dst = ring_lds + (tile % kSlots) * C::STAGE + tdst;
     const int key0 = tile * kKT;  // < N for every tile issued
-    if (key0 + kKT <= p.N) {
+    if (key0 + kKT <= N) {
       const char* g = (const char*)(tsrc + (int64_t)(key0 + tblk0 * rpl) * trow);
 #pragma unroll
       for (int i = 0; i < C::TLOADS; ++i) dma16(g + (uint32_t)(i * rpl) * trs, loff, dst + i * 1024);
     } else {
       // rows relative to the tile start, clamped to the last valid row N - 1 - key0 >= 0
       const char* g = (const char*)(tsrc + (int64_t)key0 * trow);
-      const int lim = p.N - 1 - key0;
+      const int lim = N - 1 - key0;
 #pragma unroll
       for (int i = 0; i < C::TLOADS; ++i)
         dma16(g, (uint32_t)min((tblk0 + i) * rpl + lrow, lim) * trs + lchunk, dst + i * 1024);
@@ -425,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
     const int kr_l = lane / C::KCH;
     const uint32_t kc_l = (uint32_t)(((lane % C::KCH) ^ (kr_l & C::KSW)) << 4);
     const uint32_t qdst = ring_lds + (kSlots - 1) * C::STAGE + (q2w ? C::QBYTES : 0) + qblk0 * 1024;
-    const int lim = p.N - 1 - q0;  // query rows past N re-read row N - 1 (never stored)
+    const int lim = N - 1 - q0;  // query rows past N re-read row N - 1 (never stored)
     const char* g = (const char*)(qsrc + (int64_t)q0 * qrow);
 #pragma unroll
     for (int i = 0; i < C::QLOADS; ++i)
@@ -441,8 +462,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   c.l32 = l32;
   c.hh = hh;
   c.vt_lane = ((4 * hh + (lane & 15) / 4) << 8) | (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
-  c.kmax = p.causal ? qw0 + l32 : p.N - 1;
-  c.jmask = p.causal ? qw0 / kKB : p.N / kKB;
+  c.kmax = p.causal ? qw0 + l32 : N - 1;
+  c.jmask = p.causal ? qw0 / kKB : N / kKB;
   c.sc = p.sm_scale_log2;
 
   St<D> st;
@@ -489,7 +510,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
     cm.l32 = ln & 31;
     cm.hh = ln >> 5;
     cm.vt_lane = ((4 * cm.hh + (ln & 15) / 4) << 8) | (16 * ((ln >> 4) & 1) + 4 * (ln & 3));
-    cm.kmax = p.causal ? qw0 + cm.l32 : p.N - 1;
+    cm.kmax = p.causal ? qw0 + cm.l32 : N - 1;
   }
   if ((j & 1) && j < nb) {  // first masked block is odd
     step<D, 1, true>(st, cm, j);
@@ -512,8 +533,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   const float lsum = half_swap_sum(st.l);
   const float inv = 1.0f / lsum;
   const int q = qw0 + l32;
-  if (p.lse && hh == 0 && q < p.N) {
-    const int64_t base = ((int64_t)b * p.Hs + h) * p.N + q;
+  if (p.lse && hh == 0 && q < N) {
+    const int64_t base = ((int64_t)b * p.Hs + h) * p.N + tok0 + q;
     constexpr float kLn2 = 0.69314718055994531f;
     p.lse[(int64_t)map * p.B * p.Hs * p.N + base] = (st.m + __log2f(lsum)) * kLn2;
   }
@@ -527,7 +548,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
       for (int r = 0; r < 16; ++r) xo[((grp * NCB + cb) * 16 + r) * 64 + lane] = __fmul_rn(st.o[cb][r], inv);
   }
   __syncthreads();
-  if (map == 1 || qw0 >= p.N) return;
+  if (map == 1 || qw0 >= N) return;
 
   // o = O1/l1 - lambda O2/l2, then the head RMS norm
   float ss = 0.f;
@@ -546,8 +567,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
     ss = half_swap_sum(ss);
     scale = (1.0f - p.lam_init) / sqrtf(ss * (1.0f / DV) + p.eps);
   }
-  if (q < p.N) {
-    __bf16* out = (__bf16*)p.out + b * p.so[0] + (int64_t)q * p.so[1] + h * p.so[2];
+  if (q < N) {
+    __bf16* out = (__bf16*)p.out + b * p.so[0] + (t0 + q) * p.so[1] + h * p.so[2];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -568,8 +589,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s) {
-  const int64_t nq = (p.N + kQB - 1) / kQB;
-  const int64_t total = (int64_t)p.B * p.Hs * nq;
+  const int64_t nq = (p.max_seqlen + kQB - 1) / kQB;
+  const int64_t total = (int64_t)p.nseq * p.Hs * nq;
   if (total > INT32_MAX) return hipErrorInvalidValue;
   if (p.d == 64)
     hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((unsigned)total), dim3(kThreads), 0, s, p);

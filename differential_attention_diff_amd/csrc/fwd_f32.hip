@@ -7,7 +7,7 @@
 // Normalization" (head_bar_i equation); head grouping per "Grouped
 // Differential Attention" (mlsanity.com), "Abstract".
 //
-// One wavefront per (b, signal head, query row).  Keys are visited in chunks
+// One wavefront per (sequence, signal head, query row).  Keys are visited in chunks
 // of 64 (one per lane); each map keeps a running max and sum (online softmax,
 // natural-log units) and an unnormalised output, so the result equals the
 // full-row softmax up to rounding.  Output channels c and c+64 belong to lane c.
@@ -30,26 +30,36 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
-  const int i = p.N - 1 - (int)blockIdx.x;  // longest rows first
   const int h = blockIdx.y;
-  const int b = blockIdx.z;
+  // the sequence: batch b, tokens [tok0, tok0 + N); packed sequences live in
+  // batch 0 at the offsets cu_seqlens gives, clamped to the token axis
+  int b = blockIdx.z, tok0 = 0, N = p.N;
+  if (p.cu_seqlens) {
+    const int s0 = p.cu_seqlens[b], s1 = p.cu_seqlens[b + 1];
+    b = 0;
+    tok0 = min(max(s0, 0), p.N);
+    N = max(min(min(s1, p.N) - tok0, p.max_seqlen), 0);
+  }
+  const int i = N - 1 - (int)blockIdx.x;  // longest rows first
+  if (i < 0) return;                      // whole block: row past the sequence
   const int lane = threadIdx.x;
+  const int64_t t0 = tok0;
   const int n = p.nz[h], kh = p.kv[h];
   const int d = p.d, dv = p.dv;
 
   __shared__ float q1s[64], q2s[64], p1s[64], p2s[64];
-  const float* q1 = (const float*)p.q1 + b * p.sq1[0] + (int64_t)i * p.sq1[1] + h * p.sq1[2];
-  const float* q2 = (const float*)p.q2 + b * p.sq2[0] + (int64_t)i * p.sq2[1] + n * p.sq2[2];
-  const float* k1 = (const float*)p.k1 + b * p.sk1[0] + kh * p.sk1[2];
-  const float* k2 = (const float*)p.k2 + b * p.sk2[0] + n * p.sk2[2];
-  const float* v = (const float*)p.v + b * p.sv[0] + kh * p.sv[2];
+  const float* q1 = (const float*)p.q1 + b * p.sq1[0] + (t0 + i) * p.sq1[1] + h * p.sq1[2];
+  const float* q2 = (const float*)p.q2 + b * p.sq2[0] + (t0 + i) * p.sq2[1] + n * p.sq2[2];
+  const float* k1 = (const float*)p.k1 + b * p.sk1[0] + t0 * p.sk1[1] + kh * p.sk1[2];
+  const float* k2 = (const float*)p.k2 + b * p.sk2[0] + t0 * p.sk2[1] + n * p.sk2[2];
+  const float* v = (const float*)p.v + b * p.sv[0] + t0 * p.sv[1] + kh * p.sv[2];
   if (lane < d) {
     q1s[lane] = q1[lane];
     q2s[lane] = q2[lane];
   }
   __syncthreads();
 
-  const int last = p.causal ? i : p.N - 1;  // last visible key
+  const int last = p.causal ? i : N - 1;  // last visible key
   float m1 = -INFINITY, m2 = -INFINITY, l1 = 0.f, l2 = 0.f;
   float o1a = 0.f, o1b = 0.f, o2a = 0.f, o2b = 0.f;  // channels lane, lane + 64
   const int ca = lane, cb = lane + 64;
@@ -115,11 +125,11 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
     const float ms = wave_sum(oa * oa + ob * ob) / (float)dv;
     scale = (1.0f - p.lam_init) / sqrtf(ms + p.eps);
   }
-  float* out = (float*)p.out + b * p.so[0] + (int64_t)i * p.so[1] + h * p.so[2];
+  float* out = (float*)p.out + b * p.so[0] + (t0 + i) * p.so[1] + h * p.so[2];
   if (ca < dv) out[ca] = oa * scale * (p.normalize && p.norm_w ? p.norm_w[ca] : 1.0f);
   if (cb < dv) out[cb] = ob * scale * (p.normalize && p.norm_w ? p.norm_w[cb] : 1.0f);
   if (p.lse && lane == 0) {
-    const int64_t base = ((int64_t)b * p.Hs + h) * p.N + i;
+    const int64_t base = ((int64_t)b * p.Hs + h) * p.N + tok0 + i;
     const int64_t plane = (int64_t)p.B * p.Hs * p.N;
     p.lse[base] = m1 + logf(l1);
     p.lse[plane + base] = m2 + logf(l2);
@@ -129,7 +139,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
 }  // namespace
 
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s) {
-  dim3 grid((unsigned)p.N, (unsigned)p.Hs, (unsigned)p.B);
+  dim3 grid((unsigned)p.max_seqlen, (unsigned)p.Hs, (unsigned)p.nseq);
   hipLaunchKernelGGL(fwd_f32_kernel, grid, dim3(64), 0, s, p);
   return hipGetLastError();
 }

@@ -19,6 +19,10 @@ struct FwdParams {
   void* out;
   const float* norm_w;  // [dv] or nullptr
   float* lse;           // [2][B][H_s][N] or nullptr
+  // packed sequences: sequence s is tokens [cu_seqlens[s], cu_seqlens[s+1]) of
+  // batch 0; nullptr = nseq (= B) batches of max_seqlen (= N) tokens each
+  const int32_t* cu_seqlens;
+  int nseq, max_seqlen;
   int64_t sq1[3], sq2[3], sk1[3], sk2[3], sv[3], so[3];  // (b, n, head)
   int B, N, Hs, Hn, Hkv, d, dv;
   int g;                // signal heads per noise head

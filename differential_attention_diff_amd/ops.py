@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.diffattn_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
         L.gda_fwd.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p]
         L.diffattn_fwd.restype = L.gda_fwd.restype = ctypes.c_int
+        L.gda_fwd_varlen.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_void_p]
+        L.gda_fwd_varlen.restype = ctypes.c_int
         L.gda_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
         L.gda_decode_workspace_bytes.restype = ctypes.c_size_t
         L.gda_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
@@ -180,6 +183,29 @@ def diffattn_fwd(q1, q2, k1, k2, v, lam, lam_init, *, out=None, stream=None, **k
 def gda_fwd(q1, q2, k1, k2, v, lam, lam_init, *, out=None, stream=None, **kw):
     """Grouped differential attention forward; see include/diffattn.h."""
     return _fwd(lib().gda_fwd, q1, q2, k1, k2, v, lam, lam_init, out=out, stream=stream, **kw)
+
+
+def gda_fwd_varlen(q1, q2, k1, k2, v, cu_seqlens, max_seqlen, lam, lam_init, *, out=None, lse=None, stream=None,
+                   **kw):
+    """Packed variable-length GDA prefill; see include/diffattn.h.
+
+    q1 [T,H_s,d], q2/k2 [T,H_n,d], k1 [T,H_kv,d], v [T,H_kv,dv] hold the
+    sequences one after another; cu_seqlens is a device int32 tensor [nseq+1]
+    and max_seqlen a host int bounding the lengths.  lse, when given, is fp32
+    [2,H_s,T].  Tokens outside every sequence keep the value `out` held.
+    """
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of nseq + 1 offsets")
+    if cu_seqlens.device != q1.device or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous tensor on the device of q1")
+    if out is None:
+        out = torch.empty(q1.shape[:2] + (v.shape[2],), dtype=q1.dtype, device=q1.device)
+    t4 = [x.unsqueeze(0) for x in (q1, q2, k1, k2, v, out)]
+    a, keep = fwd_args(*t4[:5], t4[5], lam, lam_init, lse=lse, **kw)
+    _check(lib().gda_fwd_varlen(ctypes.byref(a), ctypes.c_void_p(cu_seqlens.data_ptr()),
+                                cu_seqlens.numel() - 1, int(max_seqlen), _stream(stream)))
+    del keep
+    return out
 
 
 def decode_args(q1, q2, k1c, k2c, vc, seq_lens, out, lam, lam_init, *, eps=1e-5, norm_weight=None, normalize=True,

@@ -10,7 +10,10 @@ Recipe: ``torch.Generator('cpu').manual_seed(seed)``; float32 ``randn`` draws
 in the order q1, q2, k1, k2, v (decode: q1, q2, k1_cache, k2_cache, v_cache,
 then the cache lengths), each scaled by its standard deviation and then
 rounded to the storage dtype (round-to-nearest-even for bf16).  Layout BSHD
-(last dim contiguous) for prefill; [B, H, Lmax, D] caches for decode.
+(last dim contiguous) for prefill; [B, H, Lmax, D] caches for decode.  A
+packed (varlen) prefill batch draws its B sequence lengths first (uniform
+integers in len_range), then q1, q2, k1, k2, v as [T, H, D] with T the sum of
+the lengths.
 """
 
 from __future__ import annotations
@@ -29,10 +32,10 @@ LAMBDA_INIT_L12 = 0.777870099559256
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "prefill" or "decode"
+    kind: str            # "prefill", "varlen" (packed prefill) or "decode"
     dtype: str           # "f32" or "bf16"
     B: int
-    N: int               # prefill: sequence length; decode: Lmax (cache capacity)
+    N: int               # prefill: sequence length; varlen: bound on lengths; decode: Lmax
     H_s: int
     H_n: int
     H_kv: int
@@ -45,7 +48,7 @@ class Workload:
     k_std: float = 1.0
     v_std: float = 1.0
     causal: bool = True
-    len_range: tuple = field(default=(0, 0))   # decode: inclusive [lo, hi] of L_b
+    len_range: tuple = field(default=(0, 0))   # decode / varlen: inclusive [lo, hi] of the lengths
     seed: int = 0
 
     @property
@@ -72,6 +75,10 @@ WORKLOADS = {
     "gda_decode_bf16_b64_l8192": Workload("gda_decode_bf16_b64_l8192", "decode", "bf16", B=64, N=8192, H_s=18,
                                           H_n=6, H_kv=6, d=64, dv=128, lam=0.75, lam_init=0.75,
                                           len_range=(4096, 8192), seed=1004),
+    # serving-side prefill: 8 GDA 3:1 sequences of 256..4096 tokens packed in one call
+    "gda3to1_varlen_bf16_8x4096": Workload("gda3to1_varlen_bf16_8x4096", "varlen", "bf16", B=8, N=4096, H_s=18,
+                                           H_n=6, H_kv=18, d=64, dv=128, lam=0.7, lam_init=0.7,
+                                           len_range=(256, 4096), seed=1005),
 }
 
 # workload order used by tests and docs (index = position in this list)
@@ -99,6 +106,30 @@ def make_prefill_inputs(w: Workload, *, seed: int | None = None, N: int | None =
         "k2": _draw(g, (B, N, w.H_n, w.d), w.k_std, dt),
         "v": _draw(g, (B, N, w.H_kv, w.dv), w.v_std, dt),
     }
+
+
+def make_varlen_inputs(w: Workload, *, seed: int | None = None, lengths=None):
+    """Seeded packed-prefill inputs on the CPU: the B sequence lengths (drawn
+    uniformly from len_range unless given), q1 [T,H_s,d], q2/k2 [T,H_n,d],
+    k1 [T,H_kv,d], v [T,H_kv,dv] in the storage dtype, int32 cu_seqlens [B+1]
+    and max_seqlen (the longest length, a host int)."""
+    g = torch.Generator("cpu").manual_seed(w.seed if seed is None else seed)
+    if lengths is None:
+        lo, hi = w.len_range
+        lengths = torch.randint(lo, hi + 1, (w.B,), generator=g, dtype=torch.int64)
+    lengths = torch.as_tensor(lengths, dtype=torch.int64).reshape(-1)
+    T = int(lengths.sum())
+    dt = w.torch_dtype
+    out = {
+        "q1": _draw(g, (T, w.H_s, w.d), w.q_std, dt),
+        "q2": _draw(g, (T, w.H_n, w.d), w.q_std, dt),
+        "k1": _draw(g, (T, w.H_kv, w.d), w.k_std, dt),
+        "k2": _draw(g, (T, w.H_n, w.d), w.k_std, dt),
+        "v": _draw(g, (T, w.H_kv, w.dv), w.v_std, dt),
+    }
+    out["cu_seqlens"] = torch.cat([torch.zeros(1, dtype=torch.int64), torch.cumsum(lengths, 0)]).to(torch.int32)
+    out["max_seqlen"] = int(lengths.max()) if lengths.numel() else 0
+    return out
 
 
 def make_decode_inputs(w: Workload, *, seed: int | None = None, B: int | None = None, Lmax: int | None = None,

@@ -112,6 +112,29 @@ da_status diffattn_fwd(const da_fwd_args* args, void* stream);
  * H_s % H_kv == 0.  With H_n == H_kv == H_s it equals diffattn_fwd. */
 da_status gda_fwd(const da_fwd_args* args, void* stream);
 
+/* Packed variable-length GDA prefill: the same operation as gda_fwd applied
+ * to each of `nseq` sequences packed one after another along the token axis
+ * (the serving-side prefill batch; [GDA] Abstract for the head grouping,
+ * [DA-blog] DiffAttn and head_bar_i per sequence).  Attention never crosses
+ * a sequence boundary; DA_CAUSAL applies within each sequence.
+ *   args: as for gda_fwd with B == 1 and N = the packed token count; every
+ *     tensor is [1, N, heads, width] (the batch stride is not used).
+ *   cu_seqlens: DEVICE int32[nseq + 1]; sequence s is tokens
+ *     [cu_seqlens[s], cu_seqlens[s+1]).  Caller contract: cu_seqlens[0] >= 0,
+ *     non-decreasing, cu_seqlens[nseq] <= N, every length <= max_seqlen.  The
+ *     kernels clamp starts to [0, N] and lengths to [0, min(max_seqlen, N -
+ *     start)], so a broken contract truncates sequences but never reads or
+ *     writes outside the tensors.  Tokens outside every sequence are not
+ *     written.
+ *   max_seqlen: HOST bound on the sequence lengths, 0 <= max_seqlen <= N
+ *     (sizes the launch grid).
+ *   lse (optional): fp32 [2][H_s][N], indexed by packed token.
+ * nseq == 0, max_seqlen == 0 or N == 0 is a no-op returning DA_OK.  Errors as
+ * for gda_fwd, plus DA_EINVAL for B != 1, nseq < 0, a NULL or misaligned
+ * cu_seqlens, or max_seqlen outside [0, N]. */
+da_status gda_fwd_varlen(const da_fwd_args* args, const int32_t* cu_seqlens, int64_t nseq, int64_t max_seqlen,
+                         void* stream);
+
 /* Decode arguments (gda_decode): one new query per sequence against caches
  * that already hold the current token, as in a serving step.
  *   q1 [B,H_s,d]  q2 [B,H_n,d]  out [B,H_s,dv]        strides of (b, head)

@@ -33,7 +33,10 @@ blocking over keys).  Readings taken where the pages are silent:
   optional per-channel weight;
 * in GDA each noise head owns both its Q2 and its K2; signal head h uses noise
   head noise_of_signal[h] (default h // (H_s / H_n)) and key/value head
-  kv_of_signal[h] (default h // (H_s / H_kv)).
+  kv_of_signal[h] (default h // (H_s / H_kv));
+* a packed batch of sequences (the serving-side prefill) is the same
+  forward applied to each sequence on its own: no query attends across a
+  sequence boundary, and causality counts positions from the sequence start.
 
 Every function here is pinned by the CPU tests against closed forms, library
 routines and brute force; none is "parity unpinned".
@@ -54,6 +57,8 @@ __all__ = [
     "diff_attention",
     "diff_attention_rows",
     "diff_attention_lse",
+    "diff_attention_packed",
+    "diff_attention_packed_lse",
     "gda_decode",
     "brute_diff_attention",
     "causal_pairs",
@@ -225,6 +230,56 @@ def diff_attention_lse(q1, q2, k1, k2, *, rows, causal: bool = True, noise_of_si
                     s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
                 m = np.max(s, axis=-1)
                 out[t, bi, :, hi] = m + np.log(np.sum(np.exp(s - m[:, None]), axis=-1))
+    return out
+
+
+def _packed_segments(cu_seqlens, T: int, tokens):
+    """(start, length, positions of ``tokens`` inside this sequence, their
+    indices in ``tokens``) per sequence of the packing ``cu_seqlens``."""
+    cu = np.asarray(cu_seqlens, np.int64).reshape(-1)
+    if cu.size < 1 or cu[0] < 0 or np.any(np.diff(cu) < 0) or cu[-1] > T:
+        raise ValueError("cu_seqlens must be non-decreasing offsets within [0, T]")
+    tokens = np.asarray(tokens, np.int64).reshape(-1)
+    segs = []
+    for s in range(cu.size - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        idx = np.nonzero((tokens >= a) & (tokens < b))[0]
+        if b > a and idx.size:
+            segs.append((a, b - a, tokens[idx] - a, idx))
+    return segs
+
+
+def diff_attention_packed(q1, q2, k1, k2, v, cu_seqlens, lam: float, lambda_init: float, *,
+                          tokens=None, **kw) -> np.ndarray:
+    """Packed variable-length forward: sequence s is tokens
+    [cu_seqlens[s], cu_seqlens[s+1]) of the packed tensors
+      q1 [T,H_s,d]  q2 [T,H_n,d]  k1 [T,H_kv,d]  k2 [T,H_n,d]  v [T,H_kv,dv]
+    and each sequence gets ``diff_attention_rows`` of its own slice (a batch
+    of one); keyword arguments are passed through.  Returns float64
+    [len(tokens), H_s, dv] for the packed token indices ``tokens`` (default:
+    all); a token outside every sequence gives NaN."""
+    q1, q2, k1, k2, v = (_as64(t) for t in (q1, q2, k1, k2, v))
+    T, h_s = q1.shape[0], q1.shape[1]
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens, np.int64).reshape(-1)
+    out = np.full((len(tokens), h_s, v.shape[2]), np.nan)
+    for a, n, rows, idx in _packed_segments(cu_seqlens, T, tokens):
+        sl = slice(a, a + n)
+        out[idx] = diff_attention_rows(q1[None, sl], q2[None, sl], k1[None, sl], k2[None, sl], v[None, sl],
+                                       lam, lambda_init, rows=rows, **kw)[0]
+    return out
+
+
+def diff_attention_packed_lse(q1, q2, k1, k2, cu_seqlens, *, tokens=None, **kw) -> np.ndarray:
+    """``diff_attention_lse`` per sequence of a packing: float64
+    [2, len(tokens), H_s], NaN for tokens outside every sequence."""
+    q1, q2, k1, k2 = (_as64(t) for t in (q1, q2, k1, k2))
+    T, h_s = q1.shape[0], q1.shape[1]
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens, np.int64).reshape(-1)
+    out = np.full((2, len(tokens), h_s), np.nan)
+    for a, n, rows, idx in _packed_segments(cu_seqlens, T, tokens):
+        sl = slice(a, a + n)
+        out[:, idx] = diff_attention_lse(q1[None, sl], q2[None, sl], k1[None, sl], k2[None, sl], rows=rows,
+                                         **kw)[:, 0]
     return out
 
 

@@ -25,8 +25,8 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = ops.header_functions()
-    assert set(names) >= {"diffattn_fwd", "gda_fwd", "gda_decode", "gda_decode_workspace_bytes", "da_status_str",
-                          "da_last_error", "da_abi_version"}
+    assert set(names) >= {"diffattn_fwd", "gda_fwd", "gda_fwd_varlen", "gda_decode", "gda_decode_workspace_bytes",
+                          "da_status_str", "da_last_error", "da_abi_version"}
     for n in names:
         assert hasattr(L, n), f"libdiffattn.so does not export {n}"
 
@@ -113,6 +113,45 @@ def test_plain_entry_requires_equal_heads(L):
 def test_empty_is_noop(L, B, N):
     a = base_fwd(B=B, N=N)
     st, err = call(L, a)
+    assert st == ops.DA_OK, err
+
+
+CU = FAKE + 40 * GIB  # fake device address of cu_seqlens
+
+
+def call_varlen(L, a, cu=CU, nseq=3, max_seqlen=40):
+    st = L.gda_fwd_varlen(ctypes.byref(a), None if cu is None else ctypes.c_void_p(cu), nseq, max_seqlen, None)
+    return st, ops.last_error()
+
+
+@pytest.mark.parametrize("kw,batch,status,msg", [
+    (dict(), 2, ops.DA_EINVAL, "B == 1"),
+    (dict(cu=None), 1, ops.DA_EINVAL, "cu_seqlens is NULL"),
+    (dict(cu=CU + 2), 1, ops.DA_EINVAL, "4-byte aligned"),
+    (dict(nseq=-1), 1, ops.DA_EINVAL, "nseq"),
+    (dict(max_seqlen=65), 1, ops.DA_EINVAL, "max_seqlen"),
+    (dict(max_seqlen=-1), 1, ops.DA_EINVAL, "max_seqlen"),
+])
+def test_varlen_validation(L, kw, batch, status, msg):
+    a = base_fwd(B=batch)
+    st, err = call_varlen(L, a, **kw)
+    assert st == status, err
+    assert msg in err
+
+
+def test_varlen_shared_checks_and_limits(L):
+    a = base_fwd(B=1)
+    a.s_k1[1] = 65  # the checks gda_fwd makes still apply
+    st, err = call_varlen(L, a)
+    assert st == ops.DA_EINVAL and "multiple of 16 bytes" in err
+    a = base_fwd(B=1, dtype=ops.DA_F32)
+    st, err = call_varlen(L, a, nseq=70000)
+    assert st == ops.DA_EUNSUPPORTED and "sequences" in err
+
+
+@pytest.mark.parametrize("kw", [dict(nseq=0, cu=None), dict(max_seqlen=0)])
+def test_varlen_empty_is_noop(L, kw):
+    st, err = call_varlen(L, base_fwd(B=1), **kw)
     assert st == ops.DA_OK, err
 
 

@@ -299,3 +299,70 @@ def test_lse_brute_and_softmax_identity():
     h, i = 3, 5
     a2 = np.exp(np.array([np.dot(q2[0, i, 1], k2[0, j, 1]) / math.sqrt(3) for j in range(i + 1)]) - lse[1, 0, i, h])
     np.testing.assert_allclose(a2 @ v[0, :i + 1, 1], (o0 - o1)[0, i, h], rtol=1e-12)
+
+
+# --- packed variable-length batches (the serving-side prefill) -----------------------------
+
+def packed_tiny(lengths, lead=0, tail=0, hs=4, hn=2, hkv=2, d=3, dv=6, seed=0):
+    T = lead + sum(lengths) + tail
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64) + lead
+    q1, q2, k1, k2, v = tiny(B=1, N=T, hs=hs, hn=hn, hkv=hkv, d=d, dv=dv, seed=seed)
+    return (q1[0], q2[0], k1[0], k2[0], v[0]), cu
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_packed_equals_brute_per_sequence(causal):
+    (q1, q2, k1, k2, v), cu = packed_tiny([3, 0, 5, 1, 4], lead=2, tail=1, seed=31)
+    got = O.diff_attention_packed(q1, q2, k1, k2, v, cu, 0.55, 0.25, causal=causal)
+    covered = np.zeros(q1.shape[0], bool)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        covered[a:b] = True
+        if b == a:
+            continue
+        sl = slice(a, b)
+        want = O.brute_diff_attention(q1[None, sl], q2[None, sl], k1[None, sl], k2[None, sl], v[None, sl],
+                                      0.55, 0.25, causal=causal)[0]
+        np.testing.assert_allclose(got[sl], want, rtol=1e-12, atol=1e-12)
+    assert np.all(np.isnan(got[~covered])) and not np.any(np.isnan(got[covered]))
+
+
+def test_packed_equal_lengths_is_the_batched_forward():
+    q1, q2, k1, k2, v = tiny(B=3, N=7, hs=6, hn=2, hkv=3, d=4, dv=8, seed=33)
+    batched = O.diff_attention(q1, q2, k1, k2, v, 0.8, 0.4)
+    flat = [x.reshape((21,) + x.shape[2:]) for x in (q1, q2, k1, k2, v)]
+    got = O.diff_attention_packed(*flat, [0, 7, 14, 21], 0.8, 0.4)
+    np.testing.assert_array_equal(got, batched.reshape(21, 6, 8))
+    sub = O.diff_attention_packed(*flat, [0, 7, 14, 21], 0.8, 0.4, tokens=[20, 0, 8])
+    np.testing.assert_allclose(sub, got[[20, 0, 8]], rtol=1e-12, atol=1e-14)
+
+
+def test_packed_sequences_are_isolated():
+    (q1, q2, k1, k2, v), cu = packed_tiny([4, 6, 3], seed=35)
+    base = O.diff_attention_packed(q1, q2, k1, k2, v, cu, 0.7, 0.3)
+    k1b, vb = k1.copy(), v.copy()
+    k1b[cu[0]:cu[1]] += rnd(k1b[cu[0]:cu[1]].shape, 36)  # perturb sequence 0 only
+    vb[cu[2]:cu[3]] *= -3.0      # and sequence 2
+    got = O.diff_attention_packed(q1, q2, k1b, k2, vb, cu, 0.7, 0.3)
+    np.testing.assert_array_equal(got[cu[1]:cu[2]], base[cu[1]:cu[2]])
+    assert not np.allclose(got[cu[0]:cu[1]], base[cu[0]:cu[1]])
+
+
+def test_packed_lse_per_sequence():
+    (q1, q2, k1, k2, v), cu = packed_tiny([2, 5], lead=1, seed=37)
+    lse = O.diff_attention_packed_lse(q1, q2, k1, k2, cu)
+    assert np.all(np.isnan(lse[:, 0]))
+    a = cu[1]  # second sequence, its position 3 sees its keys 0..3
+    i = 3
+    for h in range(4):
+        s1 = [float(np.dot(q1[a + i, h], k1[a + j, h // 2])) / math.sqrt(3) for j in range(i + 1)]
+        s2 = [float(np.dot(q2[a + i, h // 2], k2[a + j, h // 2])) / math.sqrt(3) for j in range(i + 1)]
+        assert lse[0, a + i, h] == pytest.approx(math.log(sum(math.exp(x) for x in s1)), rel=1e-12)
+        assert lse[1, a + i, h] == pytest.approx(math.log(sum(math.exp(x) for x in s2)), rel=1e-12)
+
+
+def test_packed_rejects_bad_offsets():
+    (q1, q2, k1, k2, v), _ = packed_tiny([3, 3], seed=39)
+    for cu in ([0, 4, 3], [-1, 3, 6], [0, 3, 7]):
+        with pytest.raises(ValueError):
+            O.diff_attention_packed(q1, q2, k1, k2, v, cu, 0.5, 0.5)
