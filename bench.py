@@ -49,13 +49,15 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "differential_attention_diff_amd", "csrc")
 MEASURED_TRAFFIC = {
     "fwd_bf16.hip": {
-        "sha256": "2c2394a183614507e23097d0ce97e02a470ef59278360203b090e2d1594be902",
-        "diff3b_bf16_n4096": 147783 * 1024 * 2.0 + 98304 * 1024 * 1.0,
-        "gda3to1_bf16_n4096": 97760 * 1024 * 2.0 + 73728 * 1024 * 1.0,
+        "sha256": "7f317fc5d633aba1b272810fd0a882e23d95568bf25620cd475f320cb1bc47d5",
+        "diff3b_bf16_n4096": 147766 * 1024 * 2.0 + 98304 * 1024 * 1.0,
+        "gda3to1_bf16_n4096": 97709 * 1024 * 2.0 + 73728 * 1024 * 1.0,
+        "gda3to1_varlen_bf16_8x4096": 152155 * 1024 * 2.0 + 101300 * 1024 * 1.0,
     },
     "decode_bf16.hip": {
-        "sha256": "e35c514fa96504b42227b4c515a18bcb446d58ea96aede928d37073be61a5b02",
-        "gda_decode_bf16_b64_l8192": 586361 * 1024 * 2.0 + 9679 * 1024 * 1.0,  # decode_partial_kernel
+        "sha256": "26a00461a84f5f191fb6441f605d2af4b2fe720c856883e852475b2df9c102d7",
+        # one step: decode_partial_kernel + decode_combine_kernel
+        "gda_decode_bf16_b64_l8192": (586379 + 4885) * 1024 * 2.0 + (9680 + 288) * 1024 * 1.0,
     },
 }
 
