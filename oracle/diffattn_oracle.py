@@ -34,6 +34,10 @@ blocking over keys).  Readings taken where the pages are silent:
 * in GDA each noise head owns both its Q2 and its K2; signal head h uses noise
   head noise_of_signal[h] (default h // (H_s / H_n)) and key/value head
   kv_of_signal[h] (default h // (H_s / H_kv));
+* the backward is the derivative of this forward (chain rule written out in
+  ``diff_attention_backward``): the pages state no training kernel, and the
+  gradient of a stated function has one value.  lambda_init is a per-layer
+  constant (its schedule), so it has no gradient;
 * a packed batch of sequences (the serving-side prefill) is the same
   forward applied to each sequence on its own: no query attends across a
   sequence boundary, and causality counts positions from the sequence start.
@@ -59,6 +63,8 @@ __all__ = [
     "diff_attention_lse",
     "diff_attention_packed",
     "diff_attention_packed_lse",
+    "diff_attention_maps",
+    "diff_attention_backward",
     "gda_decode",
     "brute_diff_attention",
     "causal_pairs",
@@ -317,6 +323,86 @@ def gda_decode(q1, q2, k1_cache, k2_cache, v_cache, seq_lens, lam: float, lambda
             o = a @ vc[b, kv[h], :L, :]
             out[bi, h, :] = head_rms_norm(o, lambda_init, eps, w) if normalize else o
     return out
+
+
+# ---------------------------------------------------------------------------
+# Gradients: the derivative of the forward above, by the chain rule
+# ---------------------------------------------------------------------------
+
+def diff_attention_maps(q1, q2, k1, k2, v, *, causal: bool = True, noise_of_signal=None, kv_of_signal=None):
+    """Each map's normalised output, o1 = A1 V and o2 = A2 V, per signal head:
+    float64 [2, B, N, H_s, dv] (index 0: the Q1 K1^T map, 1: the Q2 K2^T map).
+    The forward's raw output is o1 - lambda o2 ([DA-blog] DiffAttn equation)."""
+    one = diff_attention(q1, q2, k1, k2, v, 0.0, 0.0, causal=causal, noise_of_signal=noise_of_signal,
+                         kv_of_signal=kv_of_signal, normalize=False)
+    diff = diff_attention(q1, q2, k1, k2, v, 1.0, 0.0, causal=causal, noise_of_signal=noise_of_signal,
+                          kv_of_signal=kv_of_signal, normalize=False)
+    return np.stack([one, one - diff])
+
+
+def diff_attention_backward(q1, q2, k1, k2, v, dout, lam: float, lambda_init: float, *, eps: float = 1e-5,
+                            norm_weight=None, causal: bool = True, noise_of_signal=None, kv_of_signal=None,
+                            normalize: bool = True) -> dict:
+    """Gradients of L = sum(dout * out) for the forward ``diff_attention``
+    (same arguments; dout [B,N,H_s,dv]).  Returns float64 arrays dq1, dq2,
+    dk1, dk2, dv (shapes of the inputs), the scalar dlambda and, when a norm
+    weight is given, dnorm_weight [dv].
+
+    Steps, per batch b and signal head h (n = nz(h), k = kv(h)):
+      forward pieces: s1 = q1 k1^T / sqrt(d), s2 = q2 k2^T / sqrt(d), a1 =
+        softmax(s1), a2 = softmax(s2) (masked keys weigh 0), o1 = a1 v,
+        o2 = a2 v, o = o1 - lam o2 ([DA-blog] DiffAttn equation);
+      head norm ([DA-blog] head_bar_i): y = c w o / r, c = 1 - lambda_init,
+        r = sqrt(mean(o^2) + eps), so do = c w dy / r - o sum(c w dy o) / (dv r^3)
+        and dw = sum over rows of dy c o / r (do = dy without the norm);
+      lambda: do/dlam = -o2, so dlam = -sum(do . o2);
+      the difference: da1 = do v^T, da2 = -lam do v^T, dv += (a1 - lam a2)^T do;
+      softmax: ds = a (da - rowsum(a da)) for each map;
+      scores: dq1 += ds1 k1 / sqrt(d), dk1 += ds1^T q1 / sqrt(d), and the same
+        for the second map into dq2[n], dk2[n] (shared by the group's heads).
+    """
+    q1, q2, k1, k2, v, dy = (_as64(t) for t in (q1, q2, k1, k2, v, dout))
+    B, N, h_s, d = q1.shape
+    h_n, h_kv, dv_ = q2.shape[2], k1.shape[2], v.shape[3]
+    nz, kv = _maps(h_s, h_n, h_kv, noise_of_signal, kv_of_signal)
+    w = np.ones(dv_) if norm_weight is None else _as64(norm_weight).reshape(dv_)
+    c = 1.0 - lambda_init
+    scale = 1.0 / math.sqrt(d)
+    g = {k: np.zeros_like(x) for k, x in (("dq1", q1), ("dq2", q2), ("dk1", k1), ("dk2", k2), ("dv", v))}
+    dlam = 0.0
+    dw = np.zeros(dv_)
+    hidden = np.triu(np.ones((N, N), bool), 1) if causal else np.zeros((N, N), bool)
+    for b in range(B):
+        for h in range(h_s):
+            n, k = nz[h], kv[h]
+            s1 = np.where(hidden, -np.inf, (q1[b, :, h] @ k1[b, :, k].T) * scale)
+            s2 = np.where(hidden, -np.inf, (q2[b, :, n] @ k2[b, :, n].T) * scale)
+            a1, a2 = softmax_rows(s1), softmax_rows(s2)
+            vv = v[b, :, k]
+            o1, o2 = a1 @ vv, a2 @ vv
+            o = o1 - lam * o2
+            gy = dy[b, :, h]
+            if normalize:
+                r = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+                gw = c * w * gy
+                do = gw / r - o * np.sum(gw * o, axis=-1, keepdims=True) / (dv_ * r ** 3)
+                dw += np.sum(gy * c * o / r, axis=0)
+            else:
+                do = gy
+            dlam -= float(np.sum(do * o2))
+            dp = do @ vv.T
+            g["dv"][b, :, k] += (a1 - lam * a2).T @ do
+            ds1 = a1 * (dp - np.sum(a1 * dp, axis=-1, keepdims=True))
+            da2 = -lam * dp
+            ds2 = a2 * (da2 - np.sum(a2 * da2, axis=-1, keepdims=True))
+            g["dq1"][b, :, h] += ds1 @ k1[b, :, k] * scale
+            g["dk1"][b, :, k] += ds1.T @ q1[b, :, h] * scale
+            g["dq2"][b, :, n] += ds2 @ k2[b, :, n] * scale
+            g["dk2"][b, :, n] += ds2.T @ q2[b, :, n] * scale
+    g["dlambda"] = dlam
+    if norm_weight is not None and normalize:
+        g["dnorm_weight"] = dw
+    return g
 
 
 # ---------------------------------------------------------------------------

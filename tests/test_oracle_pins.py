@@ -366,3 +366,99 @@ def test_packed_rejects_bad_offsets():
     for cu in ([0, 4, 3], [-1, 3, 6], [0, 3, 7]):
         with pytest.raises(ValueError):
             O.diff_attention_packed(q1, q2, k1, k2, v, cu, 0.5, 0.5)
+
+
+# --- gradients of the forward (the backward pass) -------------------------------------------
+
+def loss(params, dout, lam, li, **kw):
+    return float(np.sum(dout * O.diff_attention(params["q1"], params["q2"], params["k1"], params["k2"],
+                                                params["v"], lam, li, **kw)))
+
+
+def grad_fd(params, dout, lam, li, key, h=1e-6, **kw):
+    x = params[key]
+    g = np.zeros_like(x)
+    for idx in np.ndindex(x.shape):
+        old = x[idx]
+        x[idx] = old + h
+        lp = loss(params, dout, lam, li, **kw)
+        x[idx] = old - h
+        lm = loss(params, dout, lam, li, **kw)
+        x[idx] = old
+        g[idx] = (lp - lm) / (2 * h)
+    return g
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("normalize", [True, False])
+@pytest.mark.parametrize("heads", [(4, 2, 2), (4, 1, 4), (2, 2, 1)])
+def test_backward_matches_finite_differences(causal, normalize, heads):
+    hs, hn, hkv = heads
+    q1, q2, k1, k2, v = tiny(B=1, N=5, hs=hs, hn=hn, hkv=hkv, d=3, dv=6, seed=51)
+    params = dict(q1=q1, q2=q2, k1=k1, k2=k2, v=v)
+    dout = rnd((1, 5, hs, 6), 52)
+    w = 0.5 + rnd((6,), 53) ** 2
+    lam, li = 0.6, 0.3
+    kw = dict(causal=causal, normalize=normalize, norm_weight=w)
+    g = O.diff_attention_backward(q1, q2, k1, k2, v, dout, lam, li, **kw)
+    for key in params:
+        np.testing.assert_allclose(g["d" + key], grad_fd(params, dout, lam, li, key, **kw), rtol=1e-6, atol=1e-8,
+                                   err_msg=key)
+    hl = 1e-6
+    dl = (loss(params, dout, lam + hl, li, **kw) - loss(params, dout, lam - hl, li, **kw)) / (2 * hl)
+    assert g["dlambda"] == pytest.approx(dl, rel=1e-6, abs=1e-8)
+    if normalize:
+        dw = np.zeros(6)
+        for c in range(6):
+            wp, wm = w.copy(), w.copy()
+            wp[c] += hl
+            wm[c] -= hl
+            dw[c] = (loss(params, dout, lam, li, **{**kw, "norm_weight": wp})
+                     - loss(params, dout, lam, li, **{**kw, "norm_weight": wm})) / (2 * hl)
+        np.testing.assert_allclose(g["dnorm_weight"], dw, rtol=1e-6, atol=1e-8)
+
+
+def test_backward_lambda_zero_is_sdpa_autograd():
+    q1, q2, k1, k2, v = tiny(B=2, N=9, hs=2, hn=2, hkv=2, d=4, dv=8, seed=55)
+    dout = rnd((2, 9, 2, 8), 56)
+    g = O.diff_attention_backward(q1, q2, k1, k2, v, dout, 0.0, 0.25)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(np.transpose(x, (0, 2, 1, 3)))).requires_grad_(True)
+    tq, tk, tv = t(q1), t(k1), t(v)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=0.5)
+    y = 0.75 * torch.nn.functional.rms_norm(o, (8,), eps=1e-5)
+    (y * t(dout).detach()).sum().backward()
+    back = lambda x: np.transpose(x.grad.numpy(), (0, 2, 1, 3))
+    np.testing.assert_allclose(g["dq1"], back(tq), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dk1"], back(tk), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(g["dv"], back(tv), rtol=1e-10, atol=1e-12)
+    assert np.all(g["dq2"] == 0) and np.all(g["dk2"] == 0)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_key_shift_invariance(causal):
+    # adding one vector to every key moves each score row by a constant: the keys' gradients sum to zero
+    q1, q2, k1, k2, v = tiny(B=2, N=11, hs=6, hn=2, hkv=3, d=4, dv=8, seed=57)
+    g = O.diff_attention_backward(q1, q2, k1, k2, v, rnd((2, 11, 6, 8), 58), 0.7, 0.2, causal=causal)
+    np.testing.assert_allclose(g["dk1"].sum(axis=1), 0.0, atol=1e-12)
+    np.testing.assert_allclose(g["dk2"].sum(axis=1), 0.0, atol=1e-12)
+
+
+def test_backward_gda_sums_the_repeated_plain_gradients():
+    q1, q2, k1, k2, v = tiny(B=1, N=8, hs=6, hn=2, hkv=6, d=4, dv=8, seed=59)
+    dout = rnd((1, 8, 6, 8), 60)
+    g = O.diff_attention_backward(q1, q2, k1, k2, v, dout, 0.55, 0.35)
+    rep = lambda x: np.repeat(x, 3, axis=2)
+    p = O.diff_attention_backward(q1, rep(q2), k1, rep(k2), v, dout, 0.55, 0.35)
+    summed = lambda x: x.reshape(1, 8, 2, 3, 4).sum(axis=3)
+    np.testing.assert_allclose(g["dq2"], summed(p["dq2"]), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(g["dk2"], summed(p["dk2"]), rtol=1e-12, atol=1e-13)
+    for key in ("dq1", "dk1", "dv"):
+        np.testing.assert_allclose(g[key], p[key], rtol=1e-12, atol=1e-13)
+    assert g["dlambda"] == pytest.approx(p["dlambda"], rel=1e-12)
+
+
+def test_maps_are_sdpa_of_each_stream():
+    q1, q2, k1, k2, v = tiny(B=1, N=10, hs=2, hn=2, hkv=2, d=4, dv=8, seed=61)
+    m = O.diff_attention_maps(q1, q2, k1, k2, v)
+    np.testing.assert_allclose(m[0], sdpa(q1, k1, v, True), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(m[1], sdpa(q2, k2, v, True), rtol=1e-10, atol=1e-12)
