@@ -159,6 +159,7 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain, const Packing
     if ((st = check_strides(t.name, t.p, t.s, 3, es)) != DA_OK) return st;
   if (a->norm_w && ((uintptr_t)a->norm_w & 3u)) return fail(DA_EINVAL, "norm_w is not 4-byte aligned");
   if (a->lse && ((uintptr_t)a->lse & 3u)) return fail(DA_EINVAL, "lse is not 4-byte aligned");
+  if (a->o_maps && !aligned16(a->o_maps)) return fail(DA_EINVAL, "o_maps is not 16-byte aligned");
 
   Extent eo;
   {
@@ -179,6 +180,18 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain, const Packing
         return fail(DA_EINVAL, "lse overlaps %s", ts[i].name);
     }
   }
+  if (a->o_maps) {
+    const uintptr_t lo = (uintptr_t)a->o_maps;
+    Extent em{lo, lo + (uintptr_t)(2 * a->B * a->N * a->H_s * a->dv * 4)};
+    if (overlaps(em, eo)) return fail(DA_EINVAL, "o_maps overlaps out");
+    if (a->lse && overlaps(em, Extent{(uintptr_t)a->lse, (uintptr_t)(a->lse + 2 * a->B * a->H_s * a->N)}))
+      return fail(DA_EINVAL, "o_maps overlaps lse");
+    for (int i = 0; i < 5; ++i) {
+      int64_t dims[3] = {a->B, a->N, ts[i].heads};
+      if (overlaps(em, extent(ts[i].p, dims, ts[i].s, 3, ts[i].last, es)))
+        return fail(DA_EINVAL, "o_maps overlaps %s", ts[i].name);
+    }
+  }
 
   p.q1 = a->q1;
   p.q2 = a->q2;
@@ -188,6 +201,7 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain, const Packing
   p.out = a->out;
   p.norm_w = a->norm_w;
   p.lse = a->lse;
+  p.o_maps = (float*)a->o_maps;
   p.cu_seqlens = pk ? pk->cu : nullptr;
   p.nseq = (int)nseq;
   p.max_seqlen = (int)max_seqlen;
@@ -331,6 +345,152 @@ size_t decode_ws_bytes(const da::DecodeParams& p) {
   return (size_t)p.B * p.Hn * p.nchunks * da::decode_ws_floats_per_chunk(p.slots, p.dv) * sizeof(float);
 }
 
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+  size_t dop, rowstat, partial, total;
+};
+
+BwdLayout bwd_layout(const da::BwdParams& p, int es) {
+  BwdLayout l;
+  l.dop = 0;
+  l.rowstat = round256((size_t)p.B * p.N * p.Hs * p.dv * es);
+  l.partial = l.rowstat + round256((size_t)p.B * p.Hs * p.N * 16);
+  l.total = l.partial + round256((size_t)p.nprep * (1 + p.dv) * 4);
+  return l;
+}
+
+da_status bwd_prepare(const da_bwd_args* a, da::BwdParams* p, bool check_pointers) {
+  memset(p, 0, sizeof *p);
+  if (!a) return fail(DA_EINVAL, "args is NULL");
+  da_status st = check_common_shapes(a->B, a->N, a->H_s, a->H_n, a->H_kv, a->d, a->dv, a->dtype, a->lambda,
+                                     a->lambda_init, a->eps);
+  if (st != DA_OK) return st;
+  if (a->flags & ~(uint32_t)(DA_CAUSAL | DA_NO_NORM)) return fail(DA_EINVAL, "unknown flag bits 0x%x", a->flags);
+  if (a->dtype == DA_F32 && a->B > kMaxGridYZ)
+    return fail(DA_EUNSUPPORTED, "the fp32 backward takes at most %d batches per call", kMaxGridYZ);
+  if ((st = resolve_maps((int)a->H_s, (int)a->H_n, (int)a->H_kv, a->noise_of_signal, a->kv_of_signal, p->nz, p->kv,
+                         p->members)) != DA_OK)
+    return st;
+  const int Hs = (int)a->H_s, Hn = (int)a->H_n, Hkv = (int)a->H_kv, g = Hs / Hn, gk = Hs / Hkv;
+  {
+    int fill[DA_MAX_HEADS] = {0};
+    for (int h = 0; h < Hs; ++h) p->kvmembers[p->kv[h] * gk + fill[p->kv[h]]++] = (int16_t)h;
+  }
+  if (a->dtype == DA_BF16) {
+    // each key/value head's signal heads form one run in one noise group's member order
+    int runs[DA_MAX_HEADS] = {0};
+    for (int n = 0; n < Hn; ++n)
+      for (int t = 0; t < g; ++t) {
+        const int k = p->kv[p->members[n * g + t]];
+        if (t == 0 || p->kv[p->members[n * g + t - 1]] != k) runs[k]++;
+      }
+    for (int k = 0; k < Hkv; ++k)
+      if (runs[k] != 1)
+        return fail(DA_EUNSUPPORTED,
+                    "bf16 backward: the signal heads of kv head %d are not one run inside one noise group", k);
+  }
+  const int64_t rows = a->B * a->N * a->H_s;
+  p->nprep = (int)std::max<int64_t>(1, std::min<int64_t>(da::kBwdPrepBlocks, (rows + 3) / 4));
+  p->B = (int)a->B;
+  p->N = (int)a->N;
+  p->Hs = Hs;
+  p->Hn = Hn;
+  p->Hkv = Hkv;
+  p->d = (int)a->d;
+  p->dv = (int)a->dv;
+  p->g = g;
+  p->gk = gk;
+  p->causal = (a->flags & DA_CAUSAL) ? 1 : 0;
+  p->normalize = (a->flags & DA_NO_NORM) ? 0 : 1;
+  p->lam = a->lambda;
+  p->lam_init = a->lambda_init;
+  p->eps = a->eps;
+  p->sm_scale = (float)(1.0 / sqrt((double)a->d));
+  p->sm_scale_log2 = (float)(1.4426950408889634 / sqrt((double)a->d));
+  if (!check_pointers) return DA_OK;
+
+  if (!a->dlambda) return fail(DA_EINVAL, "dlambda is NULL");
+  if ((uintptr_t)a->dlambda & 3u) return fail(DA_EINVAL, "dlambda is not 4-byte aligned");
+  if (a->dnorm_w) {
+    if ((uintptr_t)a->dnorm_w & 3u) return fail(DA_EINVAL, "dnorm_w is not 4-byte aligned");
+    if (!a->norm_w || !p->normalize) return fail(DA_EINVAL, "dnorm_w needs norm_w and the head norm");
+  }
+  if (a->norm_w && ((uintptr_t)a->norm_w & 3u)) return fail(DA_EINVAL, "norm_w is not 4-byte aligned");
+  p->dlambda = a->dlambda;
+  p->dnorm_w = a->dnorm_w;
+  p->norm_w = a->norm_w;
+  if (a->B == 0 || a->N == 0) return DA_OK;  // empty: only dlambda / dnorm_w are written (zeros)
+
+  const int es = a->dtype == DA_BF16 ? 2 : 4;
+  struct T {
+    const char* name;
+    const void* p;
+    const int64_t* s;
+    int64_t heads, last;
+  } ins[6] = {{"q1", a->q1, a->s_q1, a->H_s, a->d},       {"q2", a->q2, a->s_q2, a->H_n, a->d},
+              {"k1", a->k1, a->s_k1, a->H_kv, a->d},      {"k2", a->k2, a->s_k2, a->H_n, a->d},
+              {"v", a->v, a->s_v, a->H_kv, a->dv},        {"dout", a->dout, a->s_dout, a->H_s, a->dv}},
+    outs[5] = {{"grad_q1", a->grad_q1, a->s_gq1, a->H_s, a->d}, {"grad_q2", a->grad_q2, a->s_gq2, a->H_n, a->d},
+               {"grad_k1", a->grad_k1, a->s_gk1, a->H_kv, a->d}, {"grad_k2", a->grad_k2, a->s_gk2, a->H_n, a->d},
+               {"grad_v", a->grad_v, a->s_gv, a->H_kv, a->dv}};
+  for (auto& t : ins)
+    if ((st = check_strides(t.name, t.p, t.s, 3, es)) != DA_OK) return st;
+  for (auto& t : outs)
+    if ((st = check_strides(t.name, t.p, t.s, 3, es)) != DA_OK) return st;
+  if (!a->o_maps) return fail(DA_EINVAL, "o_maps is NULL");
+  if (!aligned16(a->o_maps)) return fail(DA_EINVAL, "o_maps is not 16-byte aligned");
+  if (!a->lse) return fail(DA_EINVAL, "lse is NULL");
+  if ((uintptr_t)a->lse & 3u) return fail(DA_EINVAL, "lse is not 4-byte aligned");
+  Extent ein[8], eout[5];
+  for (int i = 0; i < 6; ++i) {
+    int64_t dims[3] = {a->B, a->N, ins[i].heads};
+    ein[i] = extent(ins[i].p, dims, ins[i].s, 3, ins[i].last, es);
+  }
+  ein[6] = {(uintptr_t)a->o_maps, (uintptr_t)a->o_maps + (uintptr_t)(2 * a->B * a->N * a->H_s * a->dv * 4)};
+  ein[7] = {(uintptr_t)a->lse, (uintptr_t)(a->lse + 2 * a->B * a->H_s * a->N)};
+  const char* in_names[8] = {"q1", "q2", "k1", "k2", "v", "dout", "o_maps", "lse"};
+  for (int i = 0; i < 5; ++i) {
+    int64_t dims[3] = {a->B, a->N, outs[i].heads};
+    eout[i] = extent(outs[i].p, dims, outs[i].s, 3, outs[i].last, es);
+    for (int j = 0; j < 8; ++j)
+      if (overlaps(eout[i], ein[j])) return fail(DA_EINVAL, "%s overlaps %s", outs[i].name, in_names[j]);
+    for (int j = 0; j < i; ++j)
+      if (overlaps(eout[i], eout[j])) return fail(DA_EINVAL, "%s overlaps %s", outs[i].name, outs[j].name);
+  }
+  p->q1 = a->q1;
+  p->q2 = a->q2;
+  p->k1 = a->k1;
+  p->k2 = a->k2;
+  p->v = a->v;
+  p->o_maps = (const float*)a->o_maps;
+  p->lse = a->lse;
+  p->dout = a->dout;
+  p->gq1 = a->grad_q1;
+  p->gq2 = a->grad_q2;
+  p->gk1 = a->grad_k1;
+  p->gk2 = a->grad_k2;
+  p->gv = a->grad_v;
+  for (int i = 0; i < 3; ++i) {
+    p->sq1[i] = a->s_q1[i];
+    p->sq2[i] = a->s_q2[i];
+    p->sk1[i] = a->s_k1[i];
+    p->sk2[i] = a->s_k2[i];
+    p->sv[i] = a->s_v[i];
+    p->sdo[i] = a->s_dout[i];
+    p->sgq1[i] = a->s_gq1[i];
+    p->sgq2[i] = a->s_gq2[i];
+    p->sgk1[i] = a->s_gk1[i];
+    p->sgk2[i] = a->s_gk2[i];
+    p->sgv[i] = a->s_gv[i];
+  }
+  return DA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -363,6 +523,38 @@ da_status gda_decode(const da_decode_args* args, void* workspace, size_t workspa
   p.ws = (float*)workspace;
   hipError_t e = da::launch_decode(p, args->dtype, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return DA_OK;
+}
+
+size_t gda_bwd_workspace_bytes(const da_bwd_args* args) {
+  da::BwdParams p;
+  if (bwd_prepare(args, &p, /*check_pointers=*/false) != DA_OK) return 0;  // shapes only
+  if (p.B == 0 || p.N == 0) return 0;
+  return bwd_layout(p, args->dtype == DA_BF16 ? 2 : 4).total;
+}
+
+da_status gda_bwd(const da_bwd_args* args, void* workspace, size_t workspace_bytes, void* stream) {
+  da::BwdParams p;
+  da_status st = bwd_prepare(args, &p, /*check_pointers=*/true);
+  if (st != DA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (p.B == 0 || p.N == 0) {
+    if ((e = da::launch_bwd_zero(p, s)) != hipSuccess) return hip_fail(e, "backward launch");
+    return DA_OK;
+  }
+  const BwdLayout l = bwd_layout(p, args->dtype == DA_BF16 ? 2 : 4);
+  if (!workspace || workspace_bytes < l.total)
+    return fail(DA_EWORKSPACE, "workspace needs %zu bytes, got %zu", l.total, workspace ? workspace_bytes : (size_t)0);
+  if ((uintptr_t)workspace & 15u) return fail(DA_EINVAL, "workspace is not 16-byte aligned");
+  unsigned char* ws = (unsigned char*)workspace;
+  p.dop = ws + l.dop;
+  p.rowstat = (float*)(ws + l.rowstat);
+  p.partial = (float*)(ws + l.partial);
+  if ((e = da::launch_bwd_prep(p, args->dtype, s)) != hipSuccess) return hip_fail(e, "backward row pass");
+  e = args->dtype == DA_BF16 ? da::launch_bwd_bf16(p, s) : da::launch_bwd_f32(p, s);
+  if (e != hipSuccess) return hip_fail(e, "backward score passes");
+  if ((e = da::launch_bwd_finalize(p, s)) != hipSuccess) return hip_fail(e, "backward reduction");
   return DA_OK;
 }
 

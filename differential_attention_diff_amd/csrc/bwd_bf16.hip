@@ -1,0 +1,416 @@
+// bf16 backward score passes for gfx950 (MFMA): dQ1/dQ2 query-major, then
+// dK1/dK2/dV key-major, both recomputing scores and weights from the saved
+// log-sum-exps.
+//
+// Gradients of "Differential Attention in Large Language Models: How
+// Denoising Subtraction Eliminates Attention Noise and Outlier Activations"
+// (llms.blog), "Differential Attention Architecture", DiffAttn equation, with
+// the noise heads of "Grouped Differential Attention" (mlsanity.com),
+// "Abstract".  With do and the row statistics of the prep pass (lse1', lse2'
+// in log2 units, D1 = do . o1, D2 = do . o2), per query i, visible key j:
+//   p1 = 2^(s1 sc - lse1'), p2 = 2^(s2 sc - lse2'), dp = do_i . v_j
+//   ds1 = p1 (dp - D1),  ds2 = -lambda p2 (dp - D2)
+//   dQ1 = dS1 K1 / sqrt(d), dK1 = dS1^T Q1 / sqrt(d), dV = (P1 - lambda P2)^T do,
+//   dQ2 = dS2 K2 / sqrt(d), dK2 = dS2^T Q2 / sqrt(d)
+// One dp = do V^T product serves both maps (both use the head's V).
+//
+// Both passes: a workgroup of 4 wavefronts owns 128 rows (32 per wavefront)
+// of one (batch, noise group) and walks the group's signal heads in turn, so
+// the noise head's sums (dQ2, dK2) stay in registers and every gradient row is
+// written once; the other operand side is staged through LDS in 64-row tiles,
+// double-buffered (the next tile's global loads are in flight during the
+// current tile's products; one barrier per tile).  v_mfma_f32_32x32x16_bf16
+// throughout; operands that must be transposed are read with
+// ds_read_b64_tr_b16.  A product's B operand taken from another product's
+// accumulator uses that accumulator's row order as its k order, and the A
+// operand read from LDS follows the same order.
+//   dQ pass: S^T = K Q^T (lane = query), so the weights of a lane's query are
+//     in its own registers and dS^T is the B operand of dQ^T = K^T dS^T.
+//   dKV pass: S = Q K^T (lane = key), so dS and P1 - lambda P2 are the B
+//     operands of dK^T = Q^T dS and dV^T = do^T (P1 - lambda P2); the per-query
+//     statistics are LDS broadcasts.
+// In the dKV pass the signal heads of a key/value head must be consecutive in
+// the group (checked on the host): dK1/dV accumulate over that run and are
+// stored when the key/value head changes.
+#include <math.h>
+
+#include "kernels.h"
+
+namespace da {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRW = 32;               // rows per wavefront
+constexpr int kRB = kWaves * kRW;     // rows per workgroup
+constexpr int kTR = 64;               // rows per LDS tile
+
+template <int D>
+struct BC {
+  static constexpr int DV = 2 * D;
+  static constexpr int NKS = D / 16, NVS = DV / 16;   // 16-wide k steps over d, dv
+  static constexpr int NDT = D / 32, NVT = DV / 32;   // 32-row output tiles over d, dv
+  static constexpr int KCH = 2 * D / 16, VCH = 2 * DV / 16;  // 16-B chunks per row
+  static constexpr int KT = kTR * 2 * D, VT = kTR * 2 * DV;  // tile bytes
+  static constexpr int KL = kTR * KCH / kThreads, VL = kTR * VCH / kThreads;  // 16-B loads per thread
+  static_assert(KL >= 1 && VL >= 1, "tile split over threads");
+};
+
+// LDS byte offset of 16-B chunk c of row r in a tile with `ch` chunks per row.
+// The XOR term takes 16 distinct values over 16 consecutive rows (row-wise
+// 16-B operand reads spread over the banks) and 4 values, 2 bits apart, over
+// the 4 rows a transposing read touches.
+__device__ __forceinline__ int swz(int r, int c, int ch) {
+  const int f = ch >= 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ch == 8 ? (((r & 3) << 1) | ((r >> 2) & 1)) : (r & 3);
+  return r * ch * 16 + ((c ^ f) << 4);
+}
+
+// Rows [r0, r0 + 64) of a tensor (element row stride rs), rows past `last`
+// re-read row `last`; thread t handles chunks t, t + 256, ...
+template <int L, int CH>
+__device__ __forceinline__ void tile_load(u32x4 (&reg)[L], const __bf16* base, int64_t rs, int r0, int last) {
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    const int idx = (int)threadIdx.x + kThreads * k, r = idx / CH, c = idx % CH;
+    reg[k] = *(const u32x4*)(base + (int64_t)min(r0 + r, last) * rs + c * 8);
+  }
+}
+template <int L, int CH>
+__device__ __forceinline__ void tile_store(unsigned char* t, const u32x4 (&reg)[L]) {
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    const int idx = (int)threadIdx.x + kThreads * k, r = idx / CH, c = idx % CH;
+    *(u32x4*)(t + swz(r, c, CH)) = reg[k];
+  }
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row-wise A operand: lane (r, half) holds row rb + r, elements 16 s + 8 half .. + 7.
+__device__ __forceinline__ bf16x8 rd_rows(const unsigned char* t, int rb, int s, int ch, int l32, int hh) {
+  return *(const bf16x8*)(t + swz(rb + l32, 2 * s + hh, ch));
+}
+
+// Transposed A operand of a 32 x 16 step: rows rb + 16 ks + {4 half + 0..3,
+// 8 + 4 half + 0..3} (the accumulator row order), column block ct (32 columns).
+// Lane j of a 16-lane group reads row 4 half + j / 4 at columns 16 g + 4 (j % 4);
+// the transposing read hands lane i the 4 rows of column 16 g + i.
+__device__ __forceinline__ bf16x8 rd_tr(const unsigned char* t, int rb, int ks, int ct, int ch, int lane) {
+  const int hh = lane >> 5, row = rb + 16 * ks + 4 * hh + (lane & 15) / 4;
+  const int col = ct * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int cc = col >> 3, within = (col & 7) * 2;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + swz(row, cc, ch) + within));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + swz(row + 8, cc, ch) + within));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// accumulator registers 0-7 / 8-15 as bf16 B operands (k = accumulator rows)
+__device__ __forceinline__ void to_b(const float (&x)[16], bf16x8& b0, bf16x8& b1) {
+  const f32x8 lo = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  const f32x8 hi = {x[8], x[9], x[10], x[11], x[12], x[13], x[14], x[15]};
+  b0 = __builtin_convertvector(lo, bf16x8);
+  b1 = __builtin_convertvector(hi, bf16x8);
+}
+
+// store a 32-column accumulator tile (rows = columns of the gradient row `lane`)
+// as bf16: register 4 g4 + e is column 32 ct + 8 g4 + 4 half + e
+template <int NT>
+__device__ __forceinline__ void store_rows(__bf16* row, const f32x16 (&acc)[NT], float scale, int hh) {
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 y = {acc[ct][4 * g4] * scale, acc[ct][4 * g4 + 1] * scale, acc[ct][4 * g4 + 2] * scale,
+                       acc[ct][4 * g4 + 3] * scale};
+      *(bf16x4*)(row + ct * 32 + 8 * g4 + 4 * hh) = __builtin_convertvector(y, bf16x4);
+    }
+}
+
+__device__ __forceinline__ int xcd_logical(int bid, int total) {
+  const int xcd = bid & 7, q8 = total >> 3, r8 = total & 7;
+  return xcd * q8 + min(xcd, r8) + (bid >> 3);
+}
+
+// ---------------------------------------------------------------------------
+// dQ pass: workgroup = (b, noise group n, 128 queries)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
+  using C = BC<D>;
+  constexpr int STAGE = 2 * C::KT + C::VT;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  const int nq = (p.N + kRB - 1) / kRB;
+  const int logical = xcd_logical(blockIdx.x, (int)gridDim.x);
+  const int qb = nq - 1 - logical % nq;  // longest causal range first
+  const int t0 = logical / nq;
+  const int n = t0 % p.Hn, b = t0 / p.Hn;
+  const int q0 = qb * kRB, qw = q0 + wave * kRW, q = qw + l32, qc = min(q, p.N - 1);
+  const int kend = p.causal ? min(q0 + kRB, p.N) : p.N;
+  const int ntile = (kend + kTR - 1) / kTR;
+  const int klast = p.causal ? min(qw + kRW - 1, p.N - 1) : p.N - 1;  // last key this wavefront sees
+  const int kvis = p.causal ? min(q, p.N - 1) : p.N - 1;              // last key this lane sees
+
+  const __bf16* K2 = (const __bf16*)p.k2 + b * p.sk2[0] + n * p.sk2[2];
+  bf16x8 q2f[C::NKS];
+  {
+    const __bf16* Q2 = (const __bf16*)p.q2 + b * p.sq2[0] + (int64_t)qc * p.sq2[1] + n * p.sq2[2];
+#pragma unroll
+    for (int s = 0; s < C::NKS; ++s) q2f[s] = *(const bf16x8*)(Q2 + 16 * s + 8 * hh);
+  }
+  f32x16 dq2[C::NDT];
+#pragma unroll
+  for (int ct = 0; ct < C::NDT; ++ct) dq2[ct] = f32x16{};
+
+  for (int mem = 0; mem < p.g; ++mem) {
+    const int h = __builtin_amdgcn_readfirstlane(p.members[n * p.g + mem]);
+    const int kh = __builtin_amdgcn_readfirstlane(p.kv[h]);
+    const __bf16* K1 = (const __bf16*)p.k1 + b * p.sk1[0] + kh * p.sk1[2];
+    const __bf16* V = (const __bf16*)p.v + b * p.sv[0] + kh * p.sv[2];
+    bf16x8 q1f[C::NKS], dof[C::NVS];
+    {
+      const __bf16* Q1 = (const __bf16*)p.q1 + b * p.sq1[0] + (int64_t)qc * p.sq1[1] + h * p.sq1[2];
+      const __bf16* DO = (const __bf16*)p.dop + (((int64_t)b * p.N + qc) * p.Hs + h) * C::DV;
+#pragma unroll
+      for (int s = 0; s < C::NKS; ++s) q1f[s] = *(const bf16x8*)(Q1 + 16 * s + 8 * hh);
+#pragma unroll
+      for (int s = 0; s < C::NVS; ++s) dof[s] = *(const bf16x8*)(DO + 16 * s + 8 * hh);
+    }
+    const float4 rs = *(const float4*)(p.rowstat + 4 * (((int64_t)b * p.Hs + h) * p.N + qc));
+    f32x16 dq1[C::NDT];
+#pragma unroll
+    for (int ct = 0; ct < C::NDT; ++ct) dq1[ct] = f32x16{};
+
+    u32x4 r1[C::KL], r2[C::KL], rv[C::VL];
+    tile_load<C::KL, C::KCH>(r1, K1, p.sk1[1], 0, p.N - 1);
+    tile_load<C::KL, C::KCH>(r2, K2, p.sk2[1], 0, p.N - 1);
+    tile_load<C::VL, C::VCH>(rv, V, p.sv[1], 0, p.N - 1);
+    tile_store<C::KL, C::KCH>(lds, r1);
+    tile_store<C::KL, C::KCH>(lds + C::KT, r2);
+    tile_store<C::VL, C::VCH>(lds + 2 * C::KT, rv);
+    __syncthreads();
+    for (int tile = 0; tile < ntile; ++tile) {
+      if (tile + 1 < ntile) {
+        const int r0 = (tile + 1) * kTR;
+        tile_load<C::KL, C::KCH>(r1, K1, p.sk1[1], r0, p.N - 1);
+        tile_load<C::KL, C::KCH>(r2, K2, p.sk2[1], r0, p.N - 1);
+        tile_load<C::VL, C::VCH>(rv, V, p.sv[1], r0, p.N - 1);
+      }
+      const unsigned char* tk1 = lds + (tile & 1) * STAGE;
+      const unsigned char* tk2 = tk1 + C::KT;
+      const unsigned char* tv = tk1 + 2 * C::KT;
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const int key0 = tile * kTR + jb * 32;
+        if (key0 > klast) continue;  // wavefront-uniform: every key of the block is hidden
+        f32x16 s1 = {}, s2 = {}, dp = {};
+#pragma unroll
+        for (int s = 0; s < C::NKS; ++s) {
+          s1 = mfma(rd_rows(tk1, jb * 32, s, C::KCH, l32, hh), q1f[s], s1);
+          s2 = mfma(rd_rows(tk2, jb * 32, s, C::KCH, l32, hh), q2f[s], s2);
+        }
+#pragma unroll
+        for (int s = 0; s < C::NVS; ++s) dp = mfma(rd_rows(tv, jb * 32, s, C::VCH, l32, hh), dof[s], dp);
+        float d1[16], d2[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 4 * hh + 8 * (r / 4) + (r & 3);
+          const bool vis = key <= kvis;
+          const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.sm_scale_log2, -rs.x)) : 0.f;
+          const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[r], p.sm_scale_log2, -rs.y)) : 0.f;
+          d1[r] = p1 * (dp[r] - rs.z);
+          d2[r] = -p.lam * p2 * (dp[r] - rs.w);
+        }
+        bf16x8 b1[2], b2[2];
+        to_b(d1, b1[0], b1[1]);
+        to_b(d2, b2[0], b2[1]);
+#pragma unroll
+        for (int ct = 0; ct < C::NDT; ++ct)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            dq1[ct] = mfma(rd_tr(tk1, jb * 32, ks, ct, C::KCH, lane), b1[ks], dq1[ct]);
+            dq2[ct] = mfma(rd_tr(tk2, jb * 32, ks, ct, C::KCH, lane), b2[ks], dq2[ct]);
+          }
+      }
+      if (tile + 1 < ntile) {
+        unsigned char* nt = lds + ((tile + 1) & 1) * STAGE;
+        tile_store<C::KL, C::KCH>(nt, r1);
+        tile_store<C::KL, C::KCH>(nt + C::KT, r2);
+        tile_store<C::VL, C::VCH>(nt + 2 * C::KT, rv);
+      }
+      __syncthreads();
+    }
+    if (q < p.N)
+      store_rows<C::NDT>((__bf16*)p.gq1 + b * p.sgq1[0] + (int64_t)q * p.sgq1[1] + h * p.sgq1[2], dq1, p.sm_scale, hh);
+  }
+  if (q < p.N)
+    store_rows<C::NDT>((__bf16*)p.gq2 + b * p.sgq2[0] + (int64_t)q * p.sgq2[1] + n * p.sgq2[2], dq2, p.sm_scale, hh);
+}
+
+// ---------------------------------------------------------------------------
+// dKV pass: workgroup = (b, noise group n, 128 keys)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
+  using C = BC<D>;
+  constexpr int RS = kTR * 16;  // row statistics of a tile (float4 per query)
+  constexpr int STAGE = 2 * C::KT + C::VT + RS;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int nk = (p.N + kRB - 1) / kRB;
+  const int logical = xcd_logical(blockIdx.x, (int)gridDim.x);
+  const int kb = p.causal ? logical % nk : nk - 1 - logical % nk;  // causal: most queries first
+  const int t0 = logical / nk;
+  const int n = t0 % p.Hn, b = t0 / p.Hn;
+  const int k0 = kb * kRB, kw = k0 + wave * kRW, key = kw + l32, kc = min(key, p.N - 1);
+  const int qt0 = p.causal ? k0 / kTR : 0;
+  const int ntile = (p.N + kTR - 1) / kTR;
+
+  const __bf16* Q2 = (const __bf16*)p.q2 + b * p.sq2[0] + n * p.sq2[2];
+  bf16x8 kf2[C::NKS];
+  {
+    const __bf16* K2 = (const __bf16*)p.k2 + b * p.sk2[0] + (int64_t)kc * p.sk2[1] + n * p.sk2[2];
+#pragma unroll
+    for (int s = 0; s < C::NKS; ++s) kf2[s] = *(const bf16x8*)(K2 + 16 * s + 8 * hh);
+  }
+  f32x16 dk2[C::NDT], dk1[C::NDT], dv[C::NVT];
+#pragma unroll
+  for (int ct = 0; ct < C::NDT; ++ct) dk2[ct] = dk1[ct] = f32x16{};
+#pragma unroll
+  for (int vt = 0; vt < C::NVT; ++vt) dv[vt] = f32x16{};
+  bf16x8 kf1[C::NKS], vf[C::NVS];
+  int cur = -1;  // key/value head of the accumulating run
+
+  for (int mem = 0; mem < p.g; ++mem) {
+    const int h = __builtin_amdgcn_readfirstlane(p.members[n * p.g + mem]);
+    const int kh = __builtin_amdgcn_readfirstlane(p.kv[h]);
+    if (kh != cur) {
+      if (cur >= 0 && key < p.N) {
+        store_rows<C::NDT>((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)key * p.sgk1[1] + cur * p.sgk1[2], dk1,
+                           p.sm_scale, hh);
+        store_rows<C::NVT>((__bf16*)p.gv + b * p.sgv[0] + (int64_t)key * p.sgv[1] + cur * p.sgv[2], dv, 1.0f, hh);
+      }
+#pragma unroll
+      for (int ct = 0; ct < C::NDT; ++ct) dk1[ct] = f32x16{};
+#pragma unroll
+      for (int vt = 0; vt < C::NVT; ++vt) dv[vt] = f32x16{};
+      cur = kh;
+      const __bf16* K1 = (const __bf16*)p.k1 + b * p.sk1[0] + (int64_t)kc * p.sk1[1] + kh * p.sk1[2];
+      const __bf16* V = (const __bf16*)p.v + b * p.sv[0] + (int64_t)kc * p.sv[1] + kh * p.sv[2];
+#pragma unroll
+      for (int s = 0; s < C::NKS; ++s) kf1[s] = *(const bf16x8*)(K1 + 16 * s + 8 * hh);
+#pragma unroll
+      for (int s = 0; s < C::NVS; ++s) vf[s] = *(const bf16x8*)(V + 16 * s + 8 * hh);
+    }
+    const __bf16* Q1 = (const __bf16*)p.q1 + b * p.sq1[0] + h * p.sq1[2];
+    const __bf16* DO = (const __bf16*)p.dop + ((int64_t)b * p.N * p.Hs + h) * C::DV;  // row i at + i Hs dv
+    const float* RSB = p.rowstat + 4 * ((int64_t)b * p.Hs + h) * p.N;
+    const int64_t dors = (int64_t)p.Hs * C::DV;
+
+    u32x4 r1[C::KL], r2[C::KL], rv[C::VL], rr;
+    auto load_all = [&](int qt) {
+      const int r0 = qt * kTR;
+      tile_load<C::KL, C::KCH>(r1, Q1, p.sq1[1], r0, p.N - 1);
+      tile_load<C::KL, C::KCH>(r2, Q2, p.sq2[1], r0, p.N - 1);
+      tile_load<C::VL, C::VCH>(rv, DO, dors, r0, p.N - 1);
+      if (tid < kTR) rr = *(const u32x4*)(RSB + 4 * (int64_t)min(r0 + tid, p.N - 1));
+    };
+    auto store_all = [&](unsigned char* t) {
+      tile_store<C::KL, C::KCH>(t, r1);
+      tile_store<C::KL, C::KCH>(t + C::KT, r2);
+      tile_store<C::VL, C::VCH>(t + 2 * C::KT, rv);
+      if (tid < kTR) *(u32x4*)(t + 2 * C::KT + C::VT + 16 * tid) = rr;
+    };
+    load_all(qt0);
+    store_all(lds);
+    __syncthreads();
+    for (int qt = qt0; qt < ntile; ++qt) {
+      if (qt + 1 < ntile) load_all(qt + 1);
+      const unsigned char* tq1 = lds + ((qt - qt0) & 1) * STAGE;
+      const unsigned char* tq2 = tq1 + C::KT;
+      const unsigned char* tdo = tq1 + 2 * C::KT;
+      const float* trs = (const float*)(tq1 + 2 * C::KT + C::VT);
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const int qs0 = qt * kTR + sb * 32;
+        if (qs0 >= p.N || (p.causal && qs0 + 31 < kw)) continue;  // wavefront-uniform: nothing visible
+        f32x16 s1 = {}, s2 = {}, dp = {};
+#pragma unroll
+        for (int s = 0; s < C::NKS; ++s) {
+          s1 = mfma(rd_rows(tq1, sb * 32, s, C::KCH, l32, hh), kf1[s], s1);
+          s2 = mfma(rd_rows(tq2, sb * 32, s, C::KCH, l32, hh), kf2[s], s2);
+        }
+#pragma unroll
+        for (int s = 0; s < C::NVS; ++s) dp = mfma(rd_rows(tdo, sb * 32, s, C::VCH, l32, hh), vf[s], dp);
+        float pc[16], d1[16], d2[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = sb * 32 + 4 * hh + 8 * (r / 4) + (r & 3);  // query row in the tile
+          const int qg = qt * kTR + qi;
+          const bool vis = qg < p.N && (!p.causal || qg >= key);
+          const float4 st = *(const float4*)(trs + 4 * qi);
+          const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.sm_scale_log2, -st.x)) : 0.f;
+          const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[r], p.sm_scale_log2, -st.y)) : 0.f;
+          pc[r] = __builtin_fmaf(-p.lam, p2, p1);
+          d1[r] = p1 * (dp[r] - st.z);
+          d2[r] = -p.lam * p2 * (dp[r] - st.w);
+        }
+        bf16x8 bc[2], b1[2], b2[2];
+        to_b(pc, bc[0], bc[1]);
+        to_b(d1, b1[0], b1[1]);
+        to_b(d2, b2[0], b2[1]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int vt = 0; vt < C::NVT; ++vt) dv[vt] = mfma(rd_tr(tdo, sb * 32, ks, vt, C::VCH, lane), bc[ks], dv[vt]);
+#pragma unroll
+          for (int ct = 0; ct < C::NDT; ++ct) {
+            dk1[ct] = mfma(rd_tr(tq1, sb * 32, ks, ct, C::KCH, lane), b1[ks], dk1[ct]);
+            dk2[ct] = mfma(rd_tr(tq2, sb * 32, ks, ct, C::KCH, lane), b2[ks], dk2[ct]);
+          }
+        }
+      }
+      if (qt + 1 < ntile) store_all(lds + ((qt + 1 - qt0) & 1) * STAGE);
+      __syncthreads();
+    }
+  }
+  if (key < p.N) {
+    store_rows<C::NDT>((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)key * p.sgk1[1] + cur * p.sgk1[2], dk1, p.sm_scale,
+                       hh);
+    store_rows<C::NVT>((__bf16*)p.gv + b * p.sgv[0] + (int64_t)key * p.sgv[1] + cur * p.sgv[2], dv, 1.0f, hh);
+    store_rows<C::NDT>((__bf16*)p.gk2 + b * p.sgk2[0] + (int64_t)key * p.sgk2[1] + n * p.sgk2[2], dk2, p.sm_scale,
+                       hh);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
+  const int64_t nblk = (p.N + kRB - 1) / kRB;
+  const int64_t grid = (int64_t)p.B * p.Hn * nblk;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  if (p.d == 64) {
+    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(bwd_dkv_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(bwd_dq_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(bwd_dkv_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace da

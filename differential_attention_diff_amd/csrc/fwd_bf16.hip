@@ -550,6 +550,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   __syncthreads();
   if (map == 1 || qw0 >= N) return;
 
+  if (p.o_maps && q < N) {  // each map's own output, A1 V and A2 V, in fp32
+    float* om1 = p.o_maps + ((((int64_t)b * p.N + tok0 + q) * p.Hs + h) * DV);
+    float* om2 = om1 + (int64_t)p.B * p.N * p.Hs * DV;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int ch = cb * 32 + 8 * g4 + 4 * hh;
+        f32x4 a, z;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = __fmul_rn(st.o[cb][4 * g4 + e], inv);
+          z[e] = xo[((grp * NCB + cb) * 16 + 4 * g4 + e) * 64 + lane];
+        }
+        *(f32x4*)(om1 + ch) = a;
+        *(f32x4*)(om2 + ch) = z;
+      }
+  }
+
   // o = O1/l1 - lambda O2/l2, then the head RMS norm
   float ss = 0.f;
 #pragma unroll

@@ -19,6 +19,7 @@ struct FwdParams {
   void* out;
   const float* norm_w;  // [dv] or nullptr
   float* lse;           // [2][B][H_s][N] or nullptr
+  float* o_maps;        // fp32 [2][B][N][H_s][dv] dense or nullptr: A1 V and A2 V
   // packed sequences: sequence s is tokens [cu_seqlens[s], cu_seqlens[s+1]) of
   // batch 0; nullptr = nseq (= B) batches of max_seqlen (= N) tokens each
   const int32_t* cu_seqlens;
@@ -60,9 +61,57 @@ struct DecodeParams {
   int16_t uidx[DA_MAX_HEADS];      // signal head -> index of its kv head in its group's ukv list
 };
 
+// Backward.  Workspace sections (offsets in bytes, each 256-aligned):
+//   dop     [B][N][H_s][dv] dense, the gradient at o (head norm undone), in
+//           the storage dtype (the MFMA operand of the bf16 passes)
+//   rowstat [B][H_s][N] x float4 {lse1 log2(e), lse2 log2(e), D1, D2} with
+//           D1 = dop . o1 and D2 = dop . o2 per row
+//   partial [prep workgroups][1 + dv] fp32: per-workgroup sums of -D2 (for
+//           dlambda) and of dy c o / r per channel (for dw)
+struct BwdParams {
+  const void* q1;
+  const void* q2;
+  const void* k1;
+  const void* k2;
+  const void* v;
+  const float* o_maps;
+  const float* lse;
+  const void* dout;
+  void* gq1;
+  void* gq2;
+  void* gk1;
+  void* gk2;
+  void* gv;
+  float* dlambda;
+  float* dnorm_w;
+  const float* norm_w;
+  void* dop;
+  float* rowstat;
+  float* partial;
+  int nprep;            // prep workgroups (rows of `partial`)
+  int64_t sq1[3], sq2[3], sk1[3], sk2[3], sv[3], sdo[3];
+  int64_t sgq1[3], sgq2[3], sgk1[3], sgk2[3], sgv[3];
+  int B, N, Hs, Hn, Hkv, d, dv;
+  int g, gk;            // signal heads per noise head, per key/value head
+  int causal, normalize;
+  float lam, lam_init, eps;
+  float sm_scale, sm_scale_log2;
+  int16_t nz[DA_MAX_HEADS];
+  int16_t kv[DA_MAX_HEADS];
+  int16_t members[DA_MAX_HEADS];   // noise group n's signal heads at [n*g, n*g+g)
+  int16_t kvmembers[DA_MAX_HEADS]; // key/value head k's signal heads at [k*gk, k*gk+gk)
+};
+
+constexpr int kBwdPrepBlocks = 1024;  // upper bound of BwdParams::nprep
+
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t s);
+hipError_t launch_bwd_prep(const BwdParams& p, int dtype, hipStream_t s);
+hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_finalize(const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_zero(const BwdParams& p, hipStream_t s);  // empty input: dlambda = 0, dw = 0
 
 // workspace floats per (b, group, chunk) for decode
 inline int64_t decode_ws_floats_per_chunk(int slots, int dv) { return (int64_t)slots * (dv + 2); }

@@ -3,8 +3,10 @@
 Every step of the computation runs in the library's HIP kernels; this module
 turns torch tensors into device pointers, element strides and the current HIP
 stream, and raises if the library is missing or returns an error.  Entry
-points mirror the C ABI: ``diffattn_fwd``, ``gda_fwd``, ``gda_decode`` (plus
-``gda_decode_workspace_bytes``).
+points mirror the C ABI: ``diffattn_fwd``, ``gda_fwd``, ``gda_fwd_varlen``,
+``gda_bwd`` (plus ``gda_bwd_workspace_bytes``), ``gda_decode`` (plus
+``gda_decode_workspace_bytes``); ``diff_attention`` wraps the forward and the
+backward as a torch autograd function.
 """
 
 from __future__ import annotations
@@ -38,6 +40,26 @@ class FwdArgs(ctypes.Structure):
         ("noise_of_signal", ctypes.POINTER(ctypes.c_int32)), ("kv_of_signal", ctypes.POINTER(ctypes.c_int32)),
         ("lambda_", ctypes.c_float), ("lambda_init", ctypes.c_float), ("eps", ctypes.c_float),
         ("norm_w", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("o_maps", ctypes.c_void_p),
+    ]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("q1", ctypes.c_void_p), ("q2", ctypes.c_void_p), ("k1", ctypes.c_void_p), ("k2", ctypes.c_void_p),
+        ("v", ctypes.c_void_p), ("o_maps", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("dout", ctypes.c_void_p),
+        ("grad_q1", ctypes.c_void_p), ("grad_q2", ctypes.c_void_p), ("grad_k1", ctypes.c_void_p),
+        ("grad_k2", ctypes.c_void_p), ("grad_v", ctypes.c_void_p),
+        ("dlambda", ctypes.c_void_p), ("dnorm_w", ctypes.c_void_p),
+        ("B", ctypes.c_int64), ("N", ctypes.c_int64), ("H_s", ctypes.c_int64), ("H_n", ctypes.c_int64),
+        ("H_kv", ctypes.c_int64), ("d", ctypes.c_int64), ("dv", ctypes.c_int64),
+        ("s_q1", _i64x3), ("s_q2", _i64x3), ("s_k1", _i64x3), ("s_k2", _i64x3), ("s_v", _i64x3),
+        ("s_dout", _i64x3),
+        ("s_gq1", _i64x3), ("s_gq2", _i64x3), ("s_gk1", _i64x3), ("s_gk2", _i64x3), ("s_gv", _i64x3),
+        ("noise_of_signal", ctypes.POINTER(ctypes.c_int32)), ("kv_of_signal", ctypes.POINTER(ctypes.c_int32)),
+        ("lambda_", ctypes.c_float), ("lambda_init", ctypes.c_float), ("eps", ctypes.c_float),
+        ("norm_w", ctypes.c_void_p),
         ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
     ]
 
@@ -80,6 +102,10 @@ def lib() -> ctypes.CDLL:
         L.gda_fwd_varlen.argtypes = [ctypes.POINTER(FwdArgs), ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                      ctypes.c_void_p]
         L.gda_fwd_varlen.restype = ctypes.c_int
+        L.gda_bwd_workspace_bytes.argtypes = [ctypes.POINTER(BwdArgs)]
+        L.gda_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.gda_bwd.argtypes = [ctypes.POINTER(BwdArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        L.gda_bwd.restype = ctypes.c_int
         L.gda_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
         L.gda_decode_workspace_bytes.restype = ctypes.c_size_t
         L.gda_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
@@ -147,7 +173,7 @@ def _lead(t: torch.Tensor, k: int):
 
 
 def fwd_args(q1, q2, k1, k2, v, out, lam, lam_init, *, eps=1e-5, norm_weight=None, causal=True, normalize=True,
-             noise_of_signal=None, kv_of_signal=None, lse=None):
+             noise_of_signal=None, kv_of_signal=None, lse=None, o_maps=None):
     """Fill the C argument struct from BSHD tensors (returns (args, keepalive))."""
     B, N, hs, d = q1.shape
     a = FwdArgs()
@@ -161,6 +187,7 @@ def fwd_args(q1, q2, k1, k2, v, out, lam, lam_init, *, eps=1e-5, norm_weight=Non
     a.lambda_, a.lambda_init, a.eps = float(lam), float(lam_init), float(eps)
     a.norm_w = None if norm_weight is None else norm_weight.data_ptr()
     a.lse = None if lse is None else lse.data_ptr()
+    a.o_maps = None if o_maps is None else o_maps.data_ptr()
     a.dtype = _dtype_code(q1)
     a.flags = (DA_CAUSAL if causal else 0) | (0 if normalize else DA_NO_NORM)
     return a, (nz_keep, kv_keep)
@@ -206,6 +233,83 @@ def gda_fwd_varlen(q1, q2, k1, k2, v, cu_seqlens, max_seqlen, lam, lam_init, *, 
                                 cu_seqlens.numel() - 1, int(max_seqlen), _stream(stream)))
     del keep
     return out
+
+
+def bwd_args(q1, q2, k1, k2, v, o_maps, lse, dout, grads, dlambda, lam, lam_init, *, eps=1e-5, norm_weight=None,
+             dnorm_weight=None, causal=True, normalize=True, noise_of_signal=None, kv_of_signal=None):
+    """Fill the backward struct; grads = (dq1, dq2, dk1, dk2, dv) shaped like the inputs."""
+    B, N, hs, d = q1.shape
+    a = BwdArgs()
+    a.q1, a.q2, a.k1, a.k2, a.v = (t.data_ptr() for t in (q1, q2, k1, k2, v))
+    a.o_maps, a.lse, a.dout = o_maps.data_ptr(), lse.data_ptr(), dout.data_ptr()
+    a.grad_q1, a.grad_q2, a.grad_k1, a.grad_k2, a.grad_v = (t.data_ptr() for t in grads)
+    a.dlambda = dlambda.data_ptr()
+    a.dnorm_w = None if dnorm_weight is None else dnorm_weight.data_ptr()
+    a.B, a.N, a.H_s, a.H_n, a.H_kv, a.d, a.dv = B, N, hs, q2.shape[2], k1.shape[2], d, v.shape[3]
+    a.s_q1[:], a.s_q2[:], a.s_k1[:] = _lead(q1, 3), _lead(q2, 3), _lead(k1, 3)
+    a.s_k2[:], a.s_v[:], a.s_dout[:] = _lead(k2, 3), _lead(v, 3), _lead(dout, 3)
+    a.s_gq1[:], a.s_gq2[:], a.s_gk1[:], a.s_gk2[:], a.s_gv[:] = (_lead(t, 3) for t in grads)
+    nz, nz_keep = _map(noise_of_signal, hs)
+    kv, kv_keep = _map(kv_of_signal, hs)
+    a.noise_of_signal, a.kv_of_signal = nz, kv
+    a.lambda_, a.lambda_init, a.eps = float(lam), float(lam_init), float(eps)
+    a.norm_w = None if norm_weight is None else norm_weight.data_ptr()
+    a.dtype = _dtype_code(q1)
+    a.flags = (DA_CAUSAL if causal else 0) | (0 if normalize else DA_NO_NORM)
+    return a, (nz_keep, kv_keep)
+
+
+def gda_bwd(q1, q2, k1, k2, v, o_maps, lse, dout, lam, lam_init, *, grads=None, dnorm_weight=None, workspace=None,
+            stream=None, **kw):
+    """Backward of gda_fwd; o_maps and lse as stored by the forward; see include/diffattn.h.
+    Returns (dq1, dq2, dk1, dk2, dv, dlambda [1] fp32)."""
+    if grads is None:
+        grads = tuple(torch.empty_like(t, memory_format=torch.contiguous_format) for t in (q1, q2, k1, k2, v))
+    dlambda = torch.empty(1, dtype=torch.float32, device=q1.device)
+    a, keep = bwd_args(q1, q2, k1, k2, v, o_maps, lse, dout, grads, dlambda, lam, lam_init,
+                       dnorm_weight=dnorm_weight, **kw)
+    need = int(lib().gda_bwd_workspace_bytes(ctypes.byref(a)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q1.device)
+    _check(lib().gda_bwd(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                         _stream(stream)))
+    del keep
+    return tuple(grads) + (dlambda,)
+
+
+class _DiffAttnFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q1, q2, k1, k2, v, lam, norm_weight, lam_init, eps, causal, normalize, nz, kvm):
+        lam_f = float(lam.detach().reshape(-1)[0].item()) if torch.is_tensor(lam) else float(lam)
+        B, N, hs, _ = q1.shape
+        lse = torch.empty(2, B, hs, N, dtype=torch.float32, device=q1.device)
+        o_maps = torch.empty(2, B, N, hs, v.shape[3], dtype=torch.float32, device=q1.device)
+        out = gda_fwd(q1, q2, k1, k2, v, lam_f, lam_init, eps=eps, norm_weight=norm_weight, causal=causal,
+                      normalize=normalize, noise_of_signal=nz, kv_of_signal=kvm, lse=lse, o_maps=o_maps)
+        ctx.save_for_backward(q1, q2, k1, k2, v, o_maps, lse, norm_weight)
+        ctx.cfg = (lam_f, lam.shape if torch.is_tensor(lam) else None, lam_init, eps, causal, normalize, nz, kvm)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q1, q2, k1, k2, v, o_maps, lse, w = ctx.saved_tensors
+        lam_f, lam_shape, lam_init, eps, causal, normalize, nz, kvm = ctx.cfg
+        want_w = w is not None and ctx.needs_input_grad[6] and normalize
+        dw = torch.empty(v.shape[3], dtype=torch.float32, device=q1.device) if want_w else None
+        dq1, dq2, dk1, dk2, dvv, dlam = gda_bwd(q1, q2, k1, k2, v, o_maps, lse, dout.contiguous(), lam_f, lam_init,
+                                                dnorm_weight=dw, eps=eps, norm_weight=w, causal=causal,
+                                                normalize=normalize, noise_of_signal=nz, kv_of_signal=kvm)
+        return (dq1, dq2, dk1, dk2, dvv, None if lam_shape is None else dlam.reshape(lam_shape), dw,
+                None, None, None, None, None, None)
+
+
+def diff_attention(q1, q2, k1, k2, v, lam, lam_init, *, norm_weight=None, eps=1e-5, causal=True, normalize=True,
+                   noise_of_signal=None, kv_of_signal=None):
+    """Differentiable (grouped) differential attention: gda_fwd forward, gda_bwd backward.
+    lam may be a float or a 0-d tensor (then it receives dL/dlambda); norm_weight an fp32
+    [dv] tensor (receives dL/dw when it requires grad)."""
+    return _DiffAttnFn.apply(q1, q2, k1, k2, v, lam, norm_weight, lam_init, eps, causal, normalize,
+                             noise_of_signal, kv_of_signal)
 
 
 def decode_args(q1, q2, k1c, k2c, vc, seq_lens, out, lam, lam_init, *, eps=1e-5, norm_weight=None, normalize=True,

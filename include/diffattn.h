@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define DA_ABI_VERSION 1
+#define DA_ABI_VERSION 2
 #define DA_MAX_HEADS 256
 
 typedef enum {
@@ -84,7 +84,11 @@ enum {
  *     mean of squares.  norm_w: device fp32 [dv] or NULL (unit weight).
  *   lse: device fp32 [2][B][H_s][N] or NULL.  When given, receives the natural
  *     log-sum-exp of each map's scaled logits per (b, h, i): lse[0] for A1,
- *     lse[1] for A2 (what a backward pass re-uses). */
+ *     lse[1] for A2 (what a backward pass re-uses).
+ *   o_maps: device fp32 [2][B][N][H_s][dv] (dense, any dtype) or NULL.  When
+ *     given, receives each map's own output A1 V and A2 V per (b, i, h), the
+ *     two terms of the DiffAttn difference (what gda_bwd needs besides lse;
+ *     fp32 because the head norm's backward differences them). */
 typedef struct da_fwd_args {
   const void* q1;
   const void* q2;
@@ -101,6 +105,7 @@ typedef struct da_fwd_args {
   float* lse;
   int32_t dtype;    /* da_dtype */
   uint32_t flags;   /* DA_CAUSAL | DA_NO_NORM */
+  void* o_maps;
 } da_fwd_args;
 
 /* Plain differential attention ([DA-blog] DiffAttn + head_bar_i): requires
@@ -134,6 +139,67 @@ da_status gda_fwd(const da_fwd_args* args, void* stream);
  * cu_seqlens, or max_seqlen outside [0, N]. */
 da_status gda_fwd_varlen(const da_fwd_args* args, const int32_t* cu_seqlens, int64_t nseq, int64_t max_seqlen,
                          void* stream);
+
+/* Backward arguments (gda_bwd): gradients of L = sum(dout * out) for the
+ * forward of the same arguments (the derivative of [DA-blog] DiffAttn and
+ * head_bar_i; [GDA] Abstract for the sums over shared heads).
+ *   q1, q2, k1, k2, v: the forward's inputs, layouts and strides as in
+ *     da_fwd_args.
+ *   o_maps: fp32 [2][B][N][H_s][dv] dense, lse: fp32 [2][B][H_s][N]: what
+ *     the forward stored through its o_maps and lse arguments.
+ *   dout [B,N,H_s,dv]: the incoming gradient (dtype `dtype`).
+ *   grad_q1 .. grad_v: the gradients, shapes of q1 .. v, written in full
+ *     (never accumulated into); strides s_g*.  A noise head's dQ2/dK2 sum its
+ *     signal heads' contributions, a key/value head's dK1/dV its heads'.
+ *   dlambda: device fp32 [1], receives dL/dlambda.  dnorm_w: device fp32 [dv]
+ *     or NULL; receives dL/dw when the head norm is on and norm_w is given.
+ *     lambda_init is a per-layer constant ([DA-blog] lambda_init schedule):
+ *     no gradient.
+ *   Everything else as in da_fwd_args; DA_CAUSAL and DA_NO_NORM must match the
+ *     forward.  With dtype DA_BF16 the key/value map must keep the heads that
+ *     share a key/value head together: every key/value head's signal heads
+ *     lie in one noise group (true for consecutive maps with H_kv >= H_n);
+ *     otherwise DA_EUNSUPPORTED. */
+typedef struct da_bwd_args {
+  const void* q1;
+  const void* q2;
+  const void* k1;
+  const void* k2;
+  const void* v;
+  const void* o_maps;
+  const float* lse;
+  const void* dout;
+  void* grad_q1;
+  void* grad_q2;
+  void* grad_k1;
+  void* grad_k2;
+  void* grad_v;
+  float* dlambda;
+  float* dnorm_w;
+  int64_t B, N, H_s, H_n, H_kv, d, dv;
+  int64_t s_q1[3], s_q2[3], s_k1[3], s_k2[3], s_v[3], s_dout[3];
+  int64_t s_gq1[3], s_gq2[3], s_gk1[3], s_gk2[3], s_gv[3];
+  const int32_t* noise_of_signal;
+  const int32_t* kv_of_signal;
+  float lambda, lambda_init, eps;
+  const float* norm_w;
+  int32_t dtype;
+  uint32_t flags;
+} da_bwd_args;
+
+/* Bytes of device workspace gda_bwd needs (shapes and dtype only; pointers
+ * may be NULL).  0 for empty inputs and on invalid shapes (then
+ * da_last_error() says why). */
+size_t gda_bwd_workspace_bytes(const da_bwd_args* args);
+
+/* Backward of gda_fwd / diffattn_fwd (plain differential attention is H_n ==
+ * H_kv == H_s).  Kernels: a row pass (head-norm backward, the per-row dot
+ * products dout' . o1 and dout' . o2, partial sums of dlambda and dw), a
+ * query-major pass (dQ1, dQ2), a key-major pass (dK1, dK2, dV) and a final
+ * reduction (dlambda, dw); scores and weights are recomputed from lse.
+ * workspace: device, caller-owned, 16-byte aligned, >= gda_bwd_workspace_bytes
+ * (DA_EWORKSPACE otherwise).  Outputs must not overlap inputs or each other. */
+da_status gda_bwd(const da_bwd_args* args, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Decode arguments (gda_decode): one new query per sequence against caches
  * that already hold the current token, as in a serving step.

@@ -25,14 +25,15 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = ops.header_functions()
-    assert set(names) >= {"diffattn_fwd", "gda_fwd", "gda_fwd_varlen", "gda_decode", "gda_decode_workspace_bytes",
-                          "da_status_str", "da_last_error", "da_abi_version"}
+    assert set(names) >= {"diffattn_fwd", "gda_fwd", "gda_fwd_varlen", "gda_bwd", "gda_bwd_workspace_bytes",
+                          "gda_decode", "gda_decode_workspace_bytes", "da_status_str", "da_last_error",
+                          "da_abi_version"}
     for n in names:
         assert hasattr(L, n), f"libdiffattn.so does not export {n}"
 
 
 def test_version_and_status_strings(L):
-    assert L.da_abi_version() == 1
+    assert L.da_abi_version() == 2
     for s in range(5):
         assert ops.status_str(s).startswith("DA_")
     assert ops.status_str(99) == "unknown status"
@@ -78,6 +79,8 @@ def call(L, a, entry="gda_fwd"):
     (lambda a: setattr(a, "dtype", 7), ops.DA_EINVAL, "dtype"),
     (lambda a: setattr(a, "out", a.v), ops.DA_EINVAL, "overlaps v"),
     (lambda a: setattr(a, "out", FAKE + 4 * GIB + 1024), ops.DA_EINVAL, "overlaps v"),
+    (lambda a: setattr(a, "o_maps", FAKE + 6 * GIB + 8), ops.DA_EINVAL, "o_maps is not 16-byte aligned"),
+    (lambda a: setattr(a, "o_maps", FAKE + 5 * GIB - 64), ops.DA_EINVAL, "o_maps overlaps out"),
 ])
 def test_fwd_validation(L, mutate, status, msg):
     a = base_fwd()
@@ -153,6 +156,70 @@ def test_varlen_shared_checks_and_limits(L):
 def test_varlen_empty_is_noop(L, kw):
     st, err = call_varlen(L, base_fwd(B=1), **kw)
     assert st == ops.DA_OK, err
+
+
+def base_bwd(B=2, N=64, hs=6, hn=2, hkv=6, d=64, dtype=ops.DA_BF16):
+    a = ops.BwdArgs()
+    dv = 2 * d
+    (a.q1, a.q2, a.k1, a.k2, a.v, a.o_maps, a.lse, a.dout, a.grad_q1, a.grad_q2, a.grad_k1, a.grad_k2,
+     a.grad_v, a.dlambda) = (FAKE + i * GIB for i in range(14))
+    a.B, a.N, a.H_s, a.H_n, a.H_kv, a.d, a.dv = B, N, hs, hn, hkv, d, dv
+    lead = lambda h, w: [N * h * w, h * w, w]
+    a.s_q1[:], a.s_gq1[:] = lead(hs, d), lead(hs, d)
+    a.s_q2[:], a.s_gq2[:] = lead(hn, d), lead(hn, d)
+    a.s_k1[:], a.s_gk1[:] = lead(hkv, d), lead(hkv, d)
+    a.s_k2[:], a.s_gk2[:] = lead(hn, d), lead(hn, d)
+    a.s_v[:], a.s_gv[:] = lead(hkv, dv), lead(hkv, dv)
+    a.s_dout[:] = lead(hs, dv)
+    a.lambda_, a.lambda_init, a.eps = 0.7, 0.7, 1e-5
+    a.dtype = dtype
+    a.flags = ops.DA_CAUSAL
+    return a
+
+
+def test_bwd_workspace_bytes(L):
+    a = base_bwd()
+    rows = 2 * 64 * 6
+    r256 = lambda x: (x + 255) // 256 * 256
+    want = r256(rows * 128 * 2) + r256(rows * 16) + r256(((rows + 3) // 4) * 129 * 4)
+    assert L.gda_bwd_workspace_bytes(ctypes.byref(a)) == want
+    a = base_bwd(dtype=ops.DA_F32)
+    assert L.gda_bwd_workspace_bytes(ctypes.byref(a)) == r256(rows * 128 * 4) + r256(rows * 16) + r256(
+        ((rows + 3) // 4) * 129 * 4)
+    assert L.gda_bwd_workspace_bytes(ctypes.byref(base_bwd(B=0))) == 0
+
+
+@pytest.mark.parametrize("mutate,status,msg", [
+    (lambda a: setattr(a, "dlambda", None), ops.DA_EINVAL, "dlambda is NULL"),
+    (lambda a: setattr(a, "o_maps", None), ops.DA_EINVAL, "o_maps is NULL"),
+    (lambda a: setattr(a, "lse", None), ops.DA_EINVAL, "lse is NULL"),
+    (lambda a: setattr(a, "dnorm_w", FAKE + 20 * GIB), ops.DA_EINVAL, "dnorm_w needs norm_w"),
+    (lambda a: setattr(a, "grad_v", None), ops.DA_EINVAL, "grad_v is NULL"),
+    (lambda a: setattr(a, "grad_k1", a.q1), ops.DA_EINVAL, "grad_k1 overlaps q1"),
+    (lambda a: setattr(a, "grad_k2", a.grad_q2), ops.DA_EINVAL, "grad_k2 overlaps grad_q2"),
+    (lambda a: setattr(a, "grad_q1", FAKE + 6 * GIB), ops.DA_EINVAL, "grad_q1 overlaps lse"),
+    (lambda a: a.s_gv.__setitem__(1, 100), ops.DA_EINVAL, "multiple of 16 bytes"),
+    (lambda a: setattr(a, "flags", 4), ops.DA_EINVAL, "flag"),
+    (lambda a: (setattr(a, "H_kv", 1)), ops.DA_EUNSUPPORTED, "not one run"),
+])
+def test_bwd_validation(L, mutate, status, msg):
+    a = base_bwd()
+    mutate(a)
+    st = L.gda_bwd(ctypes.byref(a), None, 0, None)
+    assert st == status, ops.last_error()
+    assert msg in ops.last_error()
+
+
+def test_bwd_workspace_required(L):
+    a = base_bwd()
+    assert L.gda_bwd(ctypes.byref(a), None, 0, None) == ops.DA_EWORKSPACE
+    assert L.gda_bwd(ctypes.byref(a), ctypes.c_void_p(FAKE + 30 * GIB), 1024, None) == ops.DA_EWORKSPACE
+    a = base_bwd(hs=8, hn=2, hkv=4, dtype=ops.DA_BF16)  # consecutive GQA inside each group: supported
+    a.s_q1[:], a.s_gq1[:] = [64 * 8 * 64, 8 * 64, 64], [64 * 8 * 64, 8 * 64, 64]
+    a.s_dout[:] = [64 * 8 * 128, 8 * 128, 128]
+    a.s_k1[:], a.s_gk1[:] = [64 * 4 * 64, 4 * 64, 64], [64 * 4 * 64, 4 * 64, 64]
+    a.s_v[:], a.s_gv[:] = [64 * 4 * 128, 4 * 128, 128], [64 * 4 * 128, 4 * 128, 128]
+    assert L.gda_bwd(ctypes.byref(a), None, 0, None) == ops.DA_EWORKSPACE, ops.last_error()
 
 
 def base_dec(B=64, L_=8192, hs=18, hn=6, hkv=6, d=64, chunk=0):

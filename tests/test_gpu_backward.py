@@ -1,0 +1,179 @@
+"""GPU parity of the backward (gda_bwd, and the autograd wrapper) against the
+fp64 oracle's gradients, through the C ABI.
+
+Small cases compare every element of every gradient (several 128-row blocks
+and 64-row tiles with ragged tails; plain, grouped, grouped + GQA, d = 32 and
+64; causal and not; with and without the head norm).  The 3B-scale layers run
+at full size in the benchmark's configuration and are compared on one batch
+and one noise group (the oracle's gradients of that slice are exact for it:
+the slice holds every head those gradients sum over).
+
+Bars (the forward's bars do not transfer to gradients, whose scale varies
+with the shape): fp32 max-abs <= 1e-5 max(1, max|ref|); bf16 relative L2
+<= 1e-2 and max-abs <= 4e-2 max|ref| per gradient; a gradient that is exactly
+zero (one visible key) within 1e-5.  The bf16 passes round
+three operands to bf16 on the way to each gradient (do, the weights and dS,
+relative error <= 2^-9 each) on top of bf16 inputs; the relative errors of
+such sums stay near 2^-8.  dlambda, one sum over every row, within 1e-2
+relative (fp32: 1e-5)."""
+
+import numpy as np
+import pytest
+import torch
+
+from differential_attention_diff_amd import ops
+from differential_attention_diff_amd import workloads as W
+from oracle import diffattn_oracle as O
+from tests.helpers import as64, rand_inputs
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq1", "dq2", "dk1", "dk2", "dv")
+
+
+def check_grad(got, want, dtype, what):
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    diff = got - want
+    scale = float(np.max(np.abs(want))) if want.size else 0.0
+    maxabs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    rel = float(np.linalg.norm(diff)) / max(float(np.linalg.norm(want)), 1e-30)
+    if scale == 0.0:  # an exact zero (e.g. one visible key: dS = 0): only rounding may remain
+        assert maxabs <= 1e-5, f"{what}: {maxabs:.3e} where the gradient is exactly zero"
+        return maxabs, 0.0
+    if dtype == "f32":
+        assert maxabs <= 1e-5 * max(1.0, scale), f"{what}: fp32 max-abs {maxabs:.3e} (scale {scale:.3e})"
+    else:
+        assert rel <= 1e-2 and maxabs <= 4e-2 * scale, \
+            f"{what}: bf16 rel-L2 {rel:.3e}, max-abs {maxabs:.3e} (scale {scale:.3e})"
+    return maxabs, rel
+
+
+def run_fwd_bwd(inp, dout, lam, li, norm_weight=None, want_dw=False, **kw):
+    d = {k: v.cuda() for k, v in inp.items()}
+    B, N, hs, _ = d["q1"].shape
+    dv = d["v"].shape[3]
+    lse = torch.empty(2, B, hs, N, device="cuda")
+    om = torch.empty(2, B, N, hs, dv, dtype=torch.float32, device="cuda")
+    out = ops.gda_fwd(d["q1"], d["q2"], d["k1"], d["k2"], d["v"], lam, li, lse=lse, o_maps=om,
+                      norm_weight=norm_weight, **kw)
+    dw = torch.empty(dv, device="cuda") if want_dw else None
+    grads = ops.gda_bwd(d["q1"], d["q2"], d["k1"], d["k2"], d["v"], om, lse, dout.cuda(), lam, li,
+                        norm_weight=norm_weight, dnorm_weight=dw, **kw)
+    torch.cuda.synchronize()
+    return out, grads, dw
+
+
+def dout_like(B, N, hs, dv, dtype, seed):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randn(B, N, hs, dv, generator=g).to(dtype)
+
+
+SMALL = [
+    ("f32", dict(B=1, N=77, hs=4, hn=2, hkv=2, d=32)),
+    ("f32", dict(B=2, N=130, hs=6, hn=2, hkv=3, d=64)),
+    ("bf16", dict(B=2, N=300, hs=4, hn=4, hkv=4, d=64)),   # plain, ragged tail
+    ("bf16", dict(B=1, N=257, hs=6, hn=2, hkv=6, d=64)),   # GDA 3:1
+    ("bf16", dict(B=1, N=200, hs=8, hn=2, hkv=4, d=64)),   # GDA 4:1 + GQA
+    ("bf16", dict(B=2, N=190, hs=4, hn=2, hkv=2, d=32)),   # d = 32
+    ("bf16", dict(B=1, N=1, hs=2, hn=2, hkv=2, d=64)),     # one token
+    ("bf16", dict(B=1, N=33, hs=3, hn=1, hkv=3, d=64)),    # one noise head for all
+]
+
+
+@pytest.mark.parametrize("dtype,shape", SMALL, ids=[f"{t}-{s['N']}-{s['hs']}-{s['hn']}-{s['hkv']}-{s['d']}"
+                                                     for t, s in SMALL])
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_small_every_element(dtype, shape, causal):
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    inp = rand_inputs(**shape, dtype=tdt, seed=71)
+    dout = dout_like(shape["B"], shape["N"], shape["hs"], 2 * shape["d"], tdt, 72)
+    lam, li = 0.65, 0.3
+    w = torch.linspace(0.5, 1.5, 2 * shape["d"], device="cuda")
+    print(f"[bwd {dtype} {shape} causal={causal}]", flush=True)
+    _, grads, dw = run_fwd_bwd(inp, dout, lam, li, norm_weight=w, want_dw=True, causal=causal)
+    want = O.diff_attention_backward(inp["q1"], inp["q2"], inp["k1"], inp["k2"], inp["v"], dout, lam, li,
+                                     norm_weight=as64(w), causal=causal)
+    for name, g in zip(NAMES, grads[:5]):
+        check_grad(as64(g), want[name], dtype, f"{name} {dtype} {shape} causal={causal}")
+    dl = float(grads[5].cpu()[0])
+    assert abs(dl - want["dlambda"]) <= (1e-5 if dtype == "f32" else 1e-2) * max(1.0, abs(want["dlambda"]))
+    check_grad(as64(dw), want["dnorm_weight"], dtype, "dnorm_w")
+
+
+def test_backward_without_norm_and_explicit_maps():
+    inp = rand_inputs(B=1, N=150, hs=4, hn=2, hkv=2, d=64, dtype=torch.bfloat16, seed=73)
+    dout = dout_like(1, 150, 4, 128, torch.bfloat16, 74)
+    nz, kv = [1, 0, 0, 1], [1, 0, 0, 1]  # each kv head's heads: one run in one group
+    _, grads, _ = run_fwd_bwd(inp, dout, 0.8, 0.2, normalize=False, noise_of_signal=nz, kv_of_signal=kv)
+    want = O.diff_attention_backward(inp["q1"], inp["q2"], inp["k1"], inp["k2"], inp["v"], dout, 0.8, 0.2,
+                                     normalize=False, noise_of_signal=nz, kv_of_signal=kv)
+    for name, g in zip(NAMES, grads[:5]):
+        check_grad(as64(g), want[name], "bf16", f"{name} raw, explicit maps")
+
+
+# fp32 takes any head maps; bf16 needs each key/value head's heads inside one noise group
+@pytest.mark.parametrize("dtype,hkv", [(torch.float32, 3), (torch.bfloat16, 2)])
+def test_autograd_function(dtype, hkv):
+    inp = rand_inputs(B=1, N=96, hs=6, hn=2, hkv=hkv, d=64, dtype=dtype, seed=75)
+    d = {k: v.cuda().requires_grad_(True) for k, v in inp.items()}
+    lam = torch.tensor(0.7, device="cuda", requires_grad=True)
+    w = torch.linspace(0.8, 1.2, 128, device="cuda").requires_grad_(True)
+    out = ops.diff_attention(d["q1"], d["q2"], d["k1"], d["k2"], d["v"], lam, 0.4, norm_weight=w)
+    dout = dout_like(1, 96, 6, 128, dtype, 76).cuda()
+    (out.float() * dout.float()).sum().backward()
+    want = O.diff_attention_backward(inp["q1"], inp["q2"], inp["k1"], inp["k2"], inp["v"], dout.cpu(), 0.7, 0.4,
+                                     norm_weight=as64(w))
+    tag = "f32" if dtype == torch.float32 else "bf16"
+    for name, key in zip(NAMES, ("q1", "q2", "k1", "k2", "v")):
+        check_grad(as64(d[key].grad), want[name], tag, f"autograd {name}")
+    assert abs(float(lam.grad) - want["dlambda"]) <= (1e-5 if tag == "f32" else 1e-2) * max(1, abs(want["dlambda"]))
+    check_grad(as64(w.grad), want["dnorm_weight"], tag, "autograd dw")
+
+
+def test_backward_empty_writes_zero_dlambda():
+    inp = rand_inputs(B=0, N=16, hs=2, hn=2, hkv=2, d=64, dtype=torch.bfloat16, seed=1)
+    d = {k: v.cuda() for k, v in inp.items()}
+    om = torch.empty(2, 0, 16, 2, 128, dtype=torch.float32, device="cuda")
+    lse = torch.empty(2, 0, 2, 16, device="cuda")
+    dout = torch.empty(0, 16, 2, 128, dtype=torch.bfloat16, device="cuda")
+    grads = ops.gda_bwd(d["q1"], d["q2"], d["k1"], d["k2"], d["v"], om, lse, dout, 0.5, 0.5)
+    torch.cuda.synchronize()
+    assert float(grads[5].cpu()[0]) == 0.0
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_key_gradients_sum_to_zero(causal):
+    # one vector added to every key moves each score row by a constant: sum_j dK_j = 0
+    inp = rand_inputs(B=1, N=260, hs=6, hn=2, hkv=2, d=64, dtype=torch.bfloat16, seed=77)
+    dout = dout_like(1, 260, 6, 128, torch.bfloat16, 78)
+    _, grads, _ = run_fwd_bwd(inp, dout, 0.6, 0.3, causal=causal)
+    for g in (grads[2], grads[3]):
+        x = as64(g)
+        assert np.max(np.abs(x.sum(axis=1))) <= 2e-2 * np.sqrt(260) * np.max(np.abs(x))
+
+
+def slice_group(inp, b, members, n, kvs):
+    return {"q1": inp["q1"][b:b + 1, :, members], "q2": inp["q2"][b:b + 1, :, n:n + 1],
+            "k1": inp["k1"][b:b + 1, :, kvs], "k2": inp["k2"][b:b + 1, :, n:n + 1], "v": inp["v"][b:b + 1, :, kvs]}
+
+
+@pytest.mark.parametrize("name", ["diff3b_bf16_n4096", "gda3to1_bf16_n4096"])
+def test_backward_full_workload_one_group(name):
+    w = W.WORKLOADS[name]
+    inp = W.make_prefill_inputs(w)
+    dout = dout_like(w.B, w.N, w.H_s, w.dv, torch.bfloat16, w.seed + 100)
+    print(f"[{name}] backward at full size", flush=True)
+    _, grads, _ = run_fwd_bwd(inp, dout, w.lam, w.lam_init, eps=w.eps)
+    g = w.H_s // w.H_n
+    b, n = 1, w.H_n - 1
+    members = list(range(n * g, n * g + g))
+    kvs = members if w.H_kv == w.H_s else sorted({h // (w.H_s // w.H_kv) for h in members})
+    sl = slice_group(inp, b, members, n, kvs)
+    want = O.diff_attention_backward(sl["q1"], sl["q2"], sl["k1"], sl["k2"], sl["v"], dout[b:b + 1, :, members],
+                                     w.lam, w.lam_init, eps=w.eps)
+    got = {"dq1": grads[0][b:b + 1, :, members], "dq2": grads[1][b:b + 1, :, n:n + 1],
+           "dk1": grads[2][b:b + 1, :, kvs], "dk2": grads[3][b:b + 1, :, n:n + 1], "dv": grads[4][b:b + 1, :, kvs]}
+    for k in NAMES:
+        ma, rel = check_grad(as64(got[k]), want[k], "bf16", f"{name} {k}")
+        print(f"[{name}] {k}: max-abs {ma:.3e} rel-L2 {rel:.3e}", flush=True)
