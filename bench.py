@@ -15,8 +15,9 @@ of the DiffAttn equation counted once, causal pairs only).  The same line
 carries the roofline of the kernel (against the 2.5 PFLOP/s dense bf16 MFMA
 peak), the F_exec view (F_alg plus the second P.V an exact one-pass kernel
 must issue), the grouped (3:1) prefill, the packed variable-length prefill
-(8 sequences of 256..4096 tokens in one call) and the split-K decode (HBM GB/s
-against 8 TB/s) measured the same way, and the fp64 CPU oracle timed on a
+(8 sequences of 256..4096 tokens in one call), the split-K decode (HBM GB/s
+against 8 TB/s) and the backward of the two 4096-token layers (gda_bwd) measured
+the same way, and the fp64 CPU oracle timed on a
 bounded sample of the same workload on the host's cores.
 """
 
@@ -93,6 +94,13 @@ def f_exec(w):
     g, gk = w.H_s // w.H_n, w.H_s // w.H_kv
     distinct = len({(h // g, h // gk) for h in range(w.H_s)})
     return f_alg(w) + pairs(w) * distinct * 2 * w.dv
+
+
+def f_alg_bwd(w):
+    """Products the gradient of the DiffAttn equation needs, each counted once per causal pair:
+    per signal head the recomputed Q1K1^T (2d), dP = dO V^T (2dv), dV (2dv), dQ1 and dK1 (2d each);
+    per noise head the recomputed Q2K2^T, dQ2 and dK2 (2d each; dS2 summed over the group first)."""
+    return pairs(w) * (w.H_s * (3 * 2 * w.d + 2 * 2 * w.dv) + w.H_n * 3 * 2 * w.d)
 
 
 def prefill_bytes(w):
@@ -228,6 +236,35 @@ def bench_varlen(w, steps, warmup):
     }
 
 
+def bench_backward(w, steps, warmup):
+    """gda_bwd on the prefill workload (row pass, dQ pass, dK/dV pass, reduction), with the forward's
+    lse and per-map outputs and a seeded dout resident in HBM."""
+    import torch
+    from differential_attention_diff_amd import ops
+    d = {k: v.cuda() for k, v in W.make_prefill_inputs(w).items()}
+    g = torch.Generator("cpu").manual_seed(w.seed + 100)
+    dout = torch.randn(w.B, w.N, w.H_s, w.dv, generator=g).to(w.torch_dtype).cuda()
+    lse = torch.empty(2, w.B, w.H_s, w.N, device="cuda")
+    om = torch.empty(2, w.B, w.N, w.H_s, w.dv, device="cuda")
+    ops.gda_fwd(d["q1"], d["q2"], d["k1"], d["k2"], d["v"], w.lam, w.lam_init, eps=w.eps, lse=lse, o_maps=om)
+    grads = tuple(torch.empty_like(d[k]) for k in ("q1", "q2", "k1", "k2", "v"))
+    nbytes = ops.gda_bwd_workspace_bytes(d["q1"], d["q2"], d["k1"], d["k2"], d["v"], om, lse, dout)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    fn = lambda: ops.gda_bwd(d["q1"], d["q2"], d["k1"], d["k2"], d["v"], om, lse, dout, w.lam, w.lam_init,
+                             grads=grads, workspace=ws, eps=w.eps)
+    ms = time_steps(fn, steps, warmup)
+    fb = f_alg_bwd(w)
+    ach = fb / (ms * 1e-3) / 1e12
+    return {
+        "workload": w.name + " backward", "value": ach, "unit": "TFLOP/s", "ms_per_step": ms,
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "H_s": w.H_s, "H_n": w.H_n, "H_kv": w.H_kv, "d": w.d,
+                   "dv": w.dv, "causal": w.causal, "entry": "gda_bwd", "flop_convention": "F_alg backward"},
+        "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "flops_per_launch": fb,
+                     "kernel": "bwd_prep + bwd_dq_kernel<64> + bwd_dkv_kernel<64> + bwd_finalize (step time)"},
+    }
+
+
 def bench_decode(w, steps, warmup):
     import torch
     from differential_attention_diff_amd import ops
@@ -314,6 +351,9 @@ def main():
             print(f"[bench] timing {name}", file=sys.stderr, flush=True)
             run = {"prefill": bench_prefill, "decode": bench_decode, "varlen": bench_varlen}[ew.kind]
             extra.append(run(ew, args.steps, args.warmup))
+        for name in ("diff3b_bf16_n4096", "gda3to1_bf16_n4096"):
+            print(f"[bench] timing {name} backward", file=sys.stderr, flush=True)
+            extra.append(bench_backward(W.WORKLOADS[name], args.steps, args.warmup))
 
     line = {
         "metric": METRIC,

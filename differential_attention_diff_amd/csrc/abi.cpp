@@ -360,7 +360,7 @@ BwdLayout bwd_layout(const da::BwdParams& p, int es) {
   l.dop = 0;
   l.rowstat = round256((size_t)p.B * p.N * p.Hs * p.dv * es);
   l.partial = l.rowstat + round256((size_t)p.B * p.Hs * p.N * 16);
-  l.total = l.partial + round256((size_t)p.nprep * (1 + p.dv) * 4);
+  l.total = l.partial + round256((size_t)p.nprep * (1 + p.dv) * 8);
   return l;
 }
 
@@ -550,7 +550,7 @@ da_status gda_bwd(const da_bwd_args* args, void* workspace, size_t workspace_byt
   unsigned char* ws = (unsigned char*)workspace;
   p.dop = ws + l.dop;
   p.rowstat = (float*)(ws + l.rowstat);
-  p.partial = (float*)(ws + l.partial);
+  p.partial = (double*)(ws + l.partial);
   if ((e = da::launch_bwd_prep(p, args->dtype, s)) != hipSuccess) return hip_fail(e, "backward row pass");
   e = args->dtype == DA_BF16 ? da::launch_bwd_bf16(p, s) : da::launch_bwd_f32(p, s);
   if (e != hipSuccess) return hip_fail(e, "backward score passes");

@@ -24,89 +24,160 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ float wave_sum(float x) {
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 8 consecutive values as floats
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  for (int e = 0; e < 4; ++e) {
+    x[e] = a[e];
+    x[4 + e] = b[e];
+  }
+}
+__device__ __forceinline__ void load8(const __bf16* p, float (&x)[8]) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  const bf16x8 a = *(const bf16x8*)p;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
+}
+__device__ __forceinline__ void store8(float* p, const float (&x)[8], float (&r)[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = r[e] = x[e];
+    b[e] = r[4 + e] = x[4 + e];
+  }
+  *(f32x4*)p = a;
+  *(f32x4*)(p + 4) = b;
+}
+__device__ __forceinline__ void store8(__bf16* p, const float (&x)[8], float (&r)[8]) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  bf16x8 a;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)x[e];
+    r[e] = (float)a[e];
+  }
+  *(bf16x8*)p = a;
+}
+
+// sum over the L lanes of a row group (L a power of two, groups aligned)
+template <int L>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int o = L / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
 }
 
-template <typename T>
-__device__ __forceinline__ float ld(const T* p) {
-  return (float)p[0];
-}
-
-// One wavefront per row, grid-stride over rows; channels lane and lane + 64.
-template <typename T>
+// Each row's dv channels are spread over L = dv / 8 lanes, 8 channels per lane
+// (16-byte loads); a wavefront holds 64 / L rows at a time and walks the rows
+// grid-stride.
+template <typename T, int DV>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+  constexpr int L = DV / 8, RPW = 64 / L;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int dv = p.dv;
+  const int sub = lane % L, c0 = sub * 8;
   const int64_t rows = (int64_t)p.B * p.N * p.Hs;
-  const int64_t plane = rows * dv;  // one map of o_maps
+  const int64_t plane = rows * DV;  // one map of o_maps
   const float cst = 1.0f - p.lam_init;
-  float lam_part = 0.f, dw0 = 0.f, dw1 = 0.f;
-  const int c0 = lane, c1 = lane + 64;
-  const bool v0 = c0 < dv, v1 = c1 < dv;
-  float w0 = 1.f, w1 = 1.f;
-  if (p.normalize && p.norm_w) {
-    if (v0) w0 = p.norm_w[c0];
-    if (v1) w1 = p.norm_w[c1];
-  }
-  for (int64_t row = (int64_t)blockIdx.x * 4 + wave; row < rows; row += (int64_t)gridDim.x * 4) {
-    const int h = (int)(row % p.Hs);
-    const int64_t t = row / p.Hs;
+  double lam_part = 0.0, dw[8] = {};  // sums over many rows: fp64
+  float w[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] = (p.normalize && p.norm_w) ? p.norm_w[c0 + e] : 1.0f;
+  const int64_t step = (int64_t)gridDim.x * 4 * RPW;
+  for (int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * RPW; row0 < rows; row0 += step) {
+    const int64_t row = row0 + lane / L;
+    const bool valid = row < rows;
+    const int64_t rr = valid ? row : rows - 1;
+    const int h = (int)(rr % p.Hs);
+    const int64_t t = rr / p.Hs;
     const int i = (int)(t % p.N);
     const int b = (int)(t / p.N);
-    const T* dy = (const T*)p.dout + b * p.sdo[0] + (int64_t)i * p.sdo[1] + h * p.sdo[2];
-    const float* o1 = p.o_maps + row * dv;
-    const float* o2 = o1 + plane;
-    const float y0 = v0 ? ld(dy + c0) : 0.f, y1 = v1 ? ld(dy + c1) : 0.f;
-    const float a0 = v0 ? ld(o1 + c0) : 0.f, a1 = v1 ? ld(o1 + c1) : 0.f;
-    const float z0 = v0 ? ld(o2 + c0) : 0.f, z1 = v1 ? ld(o2 + c1) : 0.f;
-    const float o0 = __builtin_fmaf(-p.lam, z0, a0), oo1 = __builtin_fmaf(-p.lam, z1, a1);
-    float d0 = y0, d1 = y1;
-    if (p.normalize) {
-      const float r = sqrtf(wave_sum(o0 * o0 + oo1 * oo1) / dv + p.eps);
-      const float ir = 1.0f / r;
-      const float g0 = cst * w0 * y0, g1 = cst * w1 * y1;
-      const float tt = wave_sum(g0 * o0 + g1 * oo1) * ir * ir * ir / dv;
-      d0 = g0 * ir - o0 * tt;
-      d1 = g1 * ir - oo1 * tt;
-      dw0 += y0 * cst * o0 * ir;
-      dw1 += y1 * cst * oo1 * ir;
+    float y[8], a[8], z[8], o[8], dd[8], e8[8];
+    load8((const T*)p.dout + b * p.sdo[0] + (int64_t)i * p.sdo[1] + h * p.sdo[2] + c0, y);
+    load8(p.o_maps + rr * DV + c0, a);
+    load8(p.o_maps + plane + rr * DV + c0, z);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (!valid) y[e] = a[e] = z[e] = 0.f;
+      o[e] = __builtin_fmaf(-p.lam, z[e], a[e]);
+      ss = __builtin_fmaf(o[e], o[e], ss);
+      dd[e] = y[e];
     }
-    lam_part -= wave_sum(d0 * z0 + d1 * z1);
-    const T r0 = (T)d0, r1 = (T)d1;
-    T* dop = (T*)p.dop + row * dv;
-    if (v0) dop[c0] = r0;
-    if (v1) dop[c1] = r1;
-    const float e0 = (float)r0, e1 = (float)r1;
-    const float D1 = wave_sum(e0 * a0 + e1 * a1), D2 = wave_sum(e0 * z0 + e1 * z1);
-    if (lane == 0) {
+    if (p.normalize) {
+      const float r = sqrtf(group_sum<L>(ss) / DV + p.eps);
+      const float ir = 1.0f / r;
+      float g[8], gt = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        g[e] = cst * w[e] * y[e];
+        gt = __builtin_fmaf(g[e], o[e], gt);
+      }
+      const float tt = group_sum<L>(gt) * ir * ir * ir / DV;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dd[e] = g[e] * ir - o[e] * tt;
+        dw[e] += (double)(y[e] * cst * o[e] * ir);
+      }
+    }
+    float lp = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lp = __builtin_fmaf(dd[e], z[e], lp);
+    lam_part -= (double)lp;
+    if (valid) store8((T*)p.dop + rr * DV + c0, dd, e8);
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (!valid) e8[e] = (float)(T)dd[e];
+      s1 = __builtin_fmaf(e8[e], a[e], s1);
+      s2 = __builtin_fmaf(e8[e], z[e], s2);
+    }
+    const float D1 = group_sum<L>(s1), D2 = group_sum<L>(s2);
+    if (valid && sub == 0) {
       const int64_t li = ((int64_t)b * p.Hs + h) * p.N + i;
       const float l1 = p.lse[li], l2 = p.lse[(int64_t)p.B * p.Hs * p.N + li];
       *(float4*)(p.rowstat + 4 * li) = make_float4(l1 * kLog2e, l2 * kLog2e, D1, D2);
     }
   }
-  // workgroup sums into this workgroup's row of `partial`
-  __shared__ float red[4][129];
-  red[wave][0] = lam_part;  // identical in every lane (wave sums)
-  if (v0) red[wave][1 + c0] = dw0;
-  if (v1) red[wave][1 + c1] = dw1;
+  // sums over the wavefront's row slots, then over the 4 wavefronts, into this
+  // workgroup's row of `partial`
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lam_part += __shfl_xor(lam_part, o, 64);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int o = L; o < 64; o <<= 1) dw[e] += __shfl_xor(dw[e], o, 64);
+  __shared__ double red[4][1 + DV];
+  if (lane == 0) red[wave][0] = lam_part;
+  if (lane < L)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wave][1 + c0 + e] = dw[e];
   __syncthreads();
-  for (int k = threadIdx.x; k < 1 + dv; k += blockDim.x)
-    p.partial[(int64_t)blockIdx.x * (1 + dv) + k] = red[0][k] + red[1][k] + red[2][k] + red[3][k];
+  for (int k = threadIdx.x; k < 1 + DV; k += blockDim.x)
+    p.partial[(int64_t)blockIdx.x * (1 + DV) + k] = red[0][k] + red[1][k] + red[2][k] + red[3][k];
 }
 
-// One workgroup: sums the per-workgroup partials in a fixed order.
+// One workgroup per column of `partial` (dlambda, then dw channel by channel):
+// thread t sums rows t, t + 256, ..., then a fixed-order tree over the threads.
 __global__ __launch_bounds__(256) void bwd_finalize_kernel(BwdParams p) {
-  const int dv = p.dv;
-  for (int k = threadIdx.x; k < 1 + dv; k += blockDim.x) {
-    float s = 0.f;
-    for (int w = 0; w < p.nprep; ++w) s += p.partial[(int64_t)w * (1 + dv) + k];
+  const int k = blockIdx.x, dv = p.dv;
+  if (k > 0 && !p.dnorm_w) return;  // whole workgroup
+  double s = 0.0;
+  for (int w = threadIdx.x; w < p.nprep; w += 256) s += p.partial[(int64_t)w * (1 + dv) + k];
+  __shared__ double red[256];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
     if (k == 0)
-      p.dlambda[0] = s;
-    else if (p.dnorm_w)
-      p.dnorm_w[k - 1] = s;
+      p.dlambda[0] = (float)red[0];
+    else
+      p.dnorm_w[k - 1] = (float)red[0];
   }
 }
 
@@ -122,15 +193,22 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(BwdParams p) {
 }  // namespace
 
 hipError_t launch_bwd_prep(const BwdParams& p, int dtype, hipStream_t s) {
-  if (dtype == DA_BF16)
-    hipLaunchKernelGGL(bwd_prep_kernel<__bf16>, dim3(p.nprep), dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(bwd_prep_kernel<float>, dim3(p.nprep), dim3(256), 0, s, p);
+  if (dtype == DA_BF16) {
+    if (p.dv == 128)
+      hipLaunchKernelGGL((bwd_prep_kernel<__bf16, 128>), dim3(p.nprep), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((bwd_prep_kernel<__bf16, 64>), dim3(p.nprep), dim3(256), 0, s, p);
+  } else {
+    if (p.dv == 128)
+      hipLaunchKernelGGL((bwd_prep_kernel<float, 128>), dim3(p.nprep), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((bwd_prep_kernel<float, 64>), dim3(p.nprep), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_finalize(const BwdParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_finalize_kernel, dim3(1), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(bwd_finalize_kernel, dim3(1 + p.dv), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

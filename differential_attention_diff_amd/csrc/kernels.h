@@ -66,7 +66,7 @@ struct DecodeParams {
 //           the storage dtype (the MFMA operand of the bf16 passes)
 //   rowstat [B][H_s][N] x float4 {lse1 log2(e), lse2 log2(e), D1, D2} with
 //           D1 = dop . o1 and D2 = dop . o2 per row
-//   partial [prep workgroups][1 + dv] fp32: per-workgroup sums of -D2 (for
+//   partial [prep workgroups][1 + dv] fp64: per-workgroup sums of -D2 (for
 //           dlambda) and of dy c o / r per channel (for dw)
 struct BwdParams {
   const void* q1;
@@ -87,7 +87,7 @@ struct BwdParams {
   const float* norm_w;
   void* dop;
   float* rowstat;
-  float* partial;
+  double* partial;
   int nprep;            // prep workgroups (rows of `partial`)
   int64_t sq1[3], sq2[3], sk1[3], sk2[3], sv[3], sdo[3];
   int64_t sgq1[3], sgq2[3], sgk1[3], sgk2[3], sgv[3];
@@ -102,7 +102,7 @@ struct BwdParams {
   int16_t kvmembers[DA_MAX_HEADS]; // key/value head k's signal heads at [k*gk, k*gk+gk)
 };
 
-constexpr int kBwdPrepBlocks = 1024;  // upper bound of BwdParams::nprep
+constexpr int kBwdPrepBlocks = 8192;  // upper bound of BwdParams::nprep
 
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s);

@@ -259,6 +259,14 @@ def bwd_args(q1, q2, k1, k2, v, o_maps, lse, dout, grads, dlambda, lam, lam_init
     return a, (nz_keep, kv_keep)
 
 
+def gda_bwd_workspace_bytes(q1, q2, k1, k2, v, o_maps, lse, dout, **kw) -> int:
+    """Workspace bytes gda_bwd needs for these tensors (shapes and dtype only)."""
+    grads = (q1, q2, k1, k2, v)  # shapes and strides only: nothing is written
+    a, keep = bwd_args(q1, q2, k1, k2, v, o_maps, lse, dout, grads, lse, 0.0, 0.0,
+                       **{k: x for k, x in kw.items() if k not in ("lam", "lam_init")})
+    return int(lib().gda_bwd_workspace_bytes(ctypes.byref(a)))
+
+
 def gda_bwd(q1, q2, k1, k2, v, o_maps, lse, dout, lam, lam_init, *, grads=None, dnorm_weight=None, workspace=None,
             stream=None, **kw):
     """Backward of gda_fwd; o_maps and lse as stored by the forward; see include/diffattn.h.

@@ -181,11 +181,11 @@ def test_bwd_workspace_bytes(L):
     a = base_bwd()
     rows = 2 * 64 * 6
     r256 = lambda x: (x + 255) // 256 * 256
-    want = r256(rows * 128 * 2) + r256(rows * 16) + r256(((rows + 3) // 4) * 129 * 4)
+    want = r256(rows * 128 * 2) + r256(rows * 16) + r256(((rows + 3) // 4) * 129 * 8)
     assert L.gda_bwd_workspace_bytes(ctypes.byref(a)) == want
     a = base_bwd(dtype=ops.DA_F32)
     assert L.gda_bwd_workspace_bytes(ctypes.byref(a)) == r256(rows * 128 * 4) + r256(rows * 16) + r256(
-        ((rows + 3) // 4) * 129 * 4)
+        ((rows + 3) // 4) * 129 * 8)
     assert L.gda_bwd_workspace_bytes(ctypes.byref(base_bwd(B=0))) == 0
 
 

@@ -14,8 +14,9 @@ with the shape): fp32 max-abs <= 1e-5 max(1, max|ref|); bf16 relative L2
 zero (one visible key) within 1e-5.  The bf16 passes round
 three operands to bf16 on the way to each gradient (do, the weights and dS,
 relative error <= 2^-9 each) on top of bf16 inputs; the relative errors of
-such sums stay near 2^-8.  dlambda, one sum over every row, within 1e-2
-relative (fp32: 1e-5)."""
+such sums stay near 2^-8.  dlambda is one sum over every row whose terms
+cancel (each row's do . o2 carries the rounding of o = o1 - lambda o2 and of
+the norm's backward): within 1e-2 relative (fp32: 1e-4)."""
 
 import numpy as np
 import pytest
@@ -97,7 +98,7 @@ def test_backward_small_every_element(dtype, shape, causal):
     for name, g in zip(NAMES, grads[:5]):
         check_grad(as64(g), want[name], dtype, f"{name} {dtype} {shape} causal={causal}")
     dl = float(grads[5].cpu()[0])
-    assert abs(dl - want["dlambda"]) <= (1e-5 if dtype == "f32" else 1e-2) * max(1.0, abs(want["dlambda"]))
+    assert abs(dl - want["dlambda"]) <= (1e-4 if dtype == "f32" else 1e-2) * max(1.0, abs(want["dlambda"]))
     check_grad(as64(dw), want["dnorm_weight"], dtype, "dnorm_w")
 
 
@@ -127,7 +128,7 @@ def test_autograd_function(dtype, hkv):
     tag = "f32" if dtype == torch.float32 else "bf16"
     for name, key in zip(NAMES, ("q1", "q2", "k1", "k2", "v")):
         check_grad(as64(d[key].grad), want[name], tag, f"autograd {name}")
-    assert abs(float(lam.grad) - want["dlambda"]) <= (1e-5 if tag == "f32" else 1e-2) * max(1, abs(want["dlambda"]))
+    assert abs(float(lam.grad) - want["dlambda"]) <= (1e-4 if tag == "f32" else 1e-2) * max(1, abs(want["dlambda"]))
     check_grad(as64(w.grad), want["dnorm_weight"], tag, "autograd dw")
 
 
