@@ -202,6 +202,7 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain, const Packing
   p.norm_w = a->norm_w;
   p.lse = a->lse;
   p.o_maps = (float*)a->o_maps;
+  p.lam_dev = a->lambda_dev;
   p.cu_seqlens = pk ? pk->cu : nullptr;
   p.nseq = (int)nseq;
   p.max_seqlen = (int)max_seqlen;
@@ -313,6 +314,7 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool chec
   p->k2 = a->k2_cache;
   p->v = a->v_cache;
   p->seq_lens = a->seq_lens;
+  p->lam_dev = a->lambda_dev;
   p->out = a->out;
   p->norm_w = a->norm_w;
   for (int i = 0; i < 2; ++i) {
@@ -468,6 +470,7 @@ da_status bwd_prepare(const da_bwd_args* a, da::BwdParams* p, bool check_pointer
   p->k2 = a->k2;
   p->v = a->v;
   p->o_maps = (const float*)a->o_maps;
+  p->lam_dev = a->lambda_dev;
   p->lse = a->lse;
   p->dout = a->dout;
   p->gq1 = a->grad_q1;
@@ -488,6 +491,12 @@ da_status bwd_prepare(const da_bwd_args* a, da::BwdParams* p, bool check_pointer
     p->sgk2[i] = a->s_gk2[i];
     p->sgv[i] = a->s_gv[i];
   }
+  return DA_OK;
+}
+
+da_status check_vec(const char* name, const float* p) {
+  if (!p) return fail(DA_EINVAL, "%s is NULL", name);
+  if ((uintptr_t)p & 3u) return fail(DA_EINVAL, "%s is not 4-byte aligned", name);
   return DA_OK;
 }
 
@@ -555,6 +564,46 @@ da_status gda_bwd(const da_bwd_args* args, void* workspace, size_t workspace_byt
   e = args->dtype == DA_BF16 ? da::launch_bwd_bf16(p, s) : da::launch_bwd_f32(p, s);
   if (e != hipSuccess) return hip_fail(e, "backward score passes");
   if ((e = da::launch_bwd_finalize(p, s)) != hipSuccess) return hip_fail(e, "backward reduction");
+  return DA_OK;
+}
+
+da_status da_lambda_reparam(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int64_t dim,
+                            float lambda_init, float* lambda_out, void* stream) {
+  if (dim < 1 || dim > 65536) return fail(DA_EINVAL, "dim = %lld outside [1, 65536]", (long long)dim);
+  if (!isfinite(lambda_init)) return fail(DA_EINVAL, "lambda_init must be finite");
+  const char* names[5] = {"lq1", "lk1", "lq2", "lk2", "lambda_out"};
+  const float* ptrs[5] = {lq1, lk1, lq2, lk2, lambda_out};
+  da_status st;
+  for (int i = 0; i < 5; ++i)
+    if ((st = check_vec(names[i], ptrs[i])) != DA_OK) return st;
+  const Extent eo{(uintptr_t)lambda_out, (uintptr_t)(lambda_out + 1)};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(eo, Extent{(uintptr_t)ptrs[i], (uintptr_t)(ptrs[i] + dim)}))
+      return fail(DA_EINVAL, "lambda_out overlaps %s", names[i]);
+  hipError_t e = da::launch_lambda_reparam(lq1, lk1, lq2, lk2, (int)dim, lambda_init, lambda_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "lambda launch");
+  return DA_OK;
+}
+
+da_status da_lambda_reparam_bwd(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int64_t dim,
+                                const float* dlambda, float* dlq1, float* dlk1, float* dlq2, float* dlk2,
+                                void* stream) {
+  if (dim < 1 || dim > 65536) return fail(DA_EINVAL, "dim = %lld outside [1, 65536]", (long long)dim);
+  const char* names[9] = {"lq1", "lk1", "lq2", "lk2", "dlambda", "dlq1", "dlk1", "dlq2", "dlk2"};
+  const float* ptrs[9] = {lq1, lk1, lq2, lk2, dlambda, dlq1, dlk1, dlq2, dlk2};
+  da_status st;
+  for (int i = 0; i < 9; ++i)
+    if ((st = check_vec(names[i], ptrs[i])) != DA_OK) return st;
+  for (int i = 5; i < 9; ++i) {
+    const Extent eo{(uintptr_t)ptrs[i], (uintptr_t)(ptrs[i] + dim)};
+    for (int j = 0; j < i; ++j) {
+      const Extent ej{(uintptr_t)ptrs[j], (uintptr_t)(ptrs[j] + (j == 4 ? 1 : dim))};
+      if (overlaps(eo, ej)) return fail(DA_EINVAL, "%s overlaps %s", names[i], names[j]);
+    }
+  }
+  hipError_t e = da::launch_lambda_reparam_bwd(lq1, lk1, lq2, lk2, (int)dim, dlambda, dlq1, dlk1, dlq2, dlk2,
+                                               (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "lambda backward launch");
   return DA_OK;
 }
 

@@ -158,6 +158,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const int t0 = logical / nq;
   const int n = t0 % p.Hn, b = t0 / p.Hn;
   const int q0 = qb * kRB, qw = q0 + wave * kRW, q = qw + l32, qc = min(q, p.N - 1);
+  const float lam = lambda_of(p.lam_dev, p.lam);
   const int kend = p.causal ? min(q0 + kRB, p.N) : p.N;
   const int ntile = (kend + kTR - 1) / kTR;
   const int klast = p.causal ? min(qw + kRW - 1, p.N - 1) : p.N - 1;  // last key this wavefront sees
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
           const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.sm_scale_log2, -rs.x)) : 0.f;
           const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[r], p.sm_scale_log2, -rs.y)) : 0.f;
           d1[r] = p1 * (dp[r] - rs.z);
-          d2[r] = -p.lam * p2 * (dp[r] - rs.w);
+          d2[r] = -lam * p2 * (dp[r] - rs.w);
         }
         bf16x8 b1[2], b2[2];
         to_b(d1, b1[0], b1[1]);
@@ -277,6 +278,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const int t0 = logical / nk;
   const int n = t0 % p.Hn, b = t0 / p.Hn;
   const int k0 = kb * kRB, kw = k0 + wave * kRW, key = kw + l32, kc = min(key, p.N - 1);
+  const float lam = lambda_of(p.lam_dev, p.lam);
   const int qt0 = p.causal ? k0 / kTR : 0;
   const int ntile = (p.N + kTR - 1) / kTR;
 
@@ -365,9 +367,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
           const float4 st = *(const float4*)(trs + 4 * qi);
           const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.sm_scale_log2, -st.x)) : 0.f;
           const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[r], p.sm_scale_log2, -st.y)) : 0.f;
-          pc[r] = __builtin_fmaf(-p.lam, p2, p1);
+          pc[r] = __builtin_fmaf(-lam, p2, p1);
           d1[r] = p1 * (dp[r] - st.z);
-          d2[r] = -p.lam * p2 * (dp[r] - st.w);
+          d2[r] = -lam * p2 * (dp[r] - st.w);
         }
         bf16x8 bc[2], b1[2], b2[2];
         to_b(pc, bc[0], bc[1]);

@@ -81,6 +81,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   const int64_t rows = (int64_t)p.B * p.N * p.Hs;
   const int64_t plane = rows * DV;  // one map of o_maps
   const float cst = 1.0f - p.lam_init;
+  const float lam = lambda_of(p.lam_dev, p.lam);
   double lam_part = 0.0, dw[8] = {};  // sums over many rows: fp64
   float w[8];
 #pragma unroll
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       if (!valid) y[e] = a[e] = z[e] = 0.f;
-      o[e] = __builtin_fmaf(-p.lam, z[e], a[e]);
+      o[e] = __builtin_fmaf(-lam, z[e], a[e]);
       ss = __builtin_fmaf(o[e], o[e], ss);
       dd[e] = y[e];
     }

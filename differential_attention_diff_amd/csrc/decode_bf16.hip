@@ -328,6 +328,7 @@ __global__ __launch_bounds__(kT) void decode_combine_kernel(DecodeParams p) {
   const int64_t cstride = (int64_t)p.slots * (kDV + 2);
   const float* base = p.ws + ((int64_t)b * p.Hn + n) * p.nchunks * cstride;
   const int c0 = 2 * lane;
+  const float lam = lambda_of(p.lam_dev, p.lam);
   for (int o = wave; o < nout; o += kT / 64) {
     // chunk maxima and sums: lane c holds chunk c (64 chunks per pass), all loads
     // of a pass in flight together
@@ -380,8 +381,8 @@ __global__ __launch_bounds__(kT) void decode_combine_kernel(DecodeParams p) {
     const int s2 = g + p.uidx[h];
     const float i1 = 1.0f / merged[j][1], i2 = 1.0f / merged[s2][1];
     // identical operations on both maps: identical maps with lambda = 1 give exact zeros
-    const float o0 = __builtin_fmaf(-p.lam, __fmul_rn(merged[s2][2 + c0], i2), __fmul_rn(merged[j][2 + c0], i1));
-    const float o1 = __builtin_fmaf(-p.lam, __fmul_rn(merged[s2][3 + c0], i2), __fmul_rn(merged[j][3 + c0], i1));
+    const float o0 = __builtin_fmaf(-lam, __fmul_rn(merged[s2][2 + c0], i2), __fmul_rn(merged[j][2 + c0], i1));
+    const float o1 = __builtin_fmaf(-lam, __fmul_rn(merged[s2][3 + c0], i2), __fmul_rn(merged[j][3 + c0], i1));
     float scale = 1.0f, w0 = 1.0f, w1 = 1.0f;
     if (p.normalize) {
       const float ms = wave_sum(o0 * o0 + o1 * o1) * (1.0f / kDV);

@@ -570,6 +570,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   }
 
   // o = O1/l1 - lambda O2/l2, then the head RMS norm
+  const float lam = lambda_of(p.lam_dev, p.lam);
   float ss = 0.f;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
     for (int r = 0; r < 16; ++r) {
       // both maps take identical operations: identical maps with lambda = 1 give exact zeros
       const float o2 = xo[((grp * NCB + cb) * 16 + r) * 64 + lane];
-      const float x = __builtin_fmaf(-p.lam, o2, __fmul_rn(st.o[cb][r], inv));
+      const float x = __builtin_fmaf(-lam, o2, __fmul_rn(st.o[cb][r], inv));
       st.o[cb][r] = x;
       ss = __builtin_fmaf(x, x, ss);
     }

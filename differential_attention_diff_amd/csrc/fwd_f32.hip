@@ -116,6 +116,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
   // o = O1/l1 - lambda O2/l2.  Both maps go through identical operations, so
   // identical maps with lambda = 1 cancel to exactly zero.
   const float r1 = 1.0f / l1, r2 = 1.0f / l2;
+  const float lam = lambda_of(p.lam_dev, p.lam);
   if (p.o_maps) {  // each map's own output, A1 V and A2 V
     float* om1 = p.o_maps + ((((int64_t)b * p.N + tok0 + i) * p.Hs + h) * dv);
     float* om2 = om1 + (int64_t)p.B * p.N * p.Hs * dv;
@@ -128,8 +129,8 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdParams p) {
       om2[cb] = __fmul_rn(o2b, r2);
     }
   }
-  float oa = fmaf(-p.lam, __fmul_rn(o2a, r2), __fmul_rn(o1a, r1));
-  float ob = fmaf(-p.lam, __fmul_rn(o2b, r2), __fmul_rn(o1b, r1));
+  float oa = fmaf(-lam, __fmul_rn(o2a, r2), __fmul_rn(o1a, r1));
+  float ob = fmaf(-lam, __fmul_rn(o2b, r2), __fmul_rn(o1b, r1));
   if (ca >= dv) oa = 0.f;
   if (cb >= dv) ob = 0.f;
   float scale = 1.0f;

@@ -20,6 +20,7 @@ struct FwdParams {
   const float* norm_w;  // [dv] or nullptr
   float* lse;           // [2][B][H_s][N] or nullptr
   float* o_maps;        // fp32 [2][B][N][H_s][dv] dense or nullptr: A1 V and A2 V
+  const float* lam_dev; // device lambda or nullptr (then lam)
   // packed sequences: sequence s is tokens [cu_seqlens[s], cu_seqlens[s+1]) of
   // batch 0; nullptr = nseq (= B) batches of max_seqlen (= N) tokens each
   const int32_t* cu_seqlens;
@@ -45,6 +46,7 @@ struct DecodeParams {
   const int32_t* seq_lens;
   void* out;
   float* ws;            // partials, see decode_bf16.hip
+  const float* lam_dev; // device lambda or nullptr (then lam)
   const float* norm_w;
   int64_t sq1[2], sq2[2], so[2];
   int64_t sk1[3], sk2[3], sv[3];
@@ -75,6 +77,7 @@ struct BwdParams {
   const void* k2;
   const void* v;
   const float* o_maps;
+  const float* lam_dev;  // device lambda or nullptr (then lam)
   const float* lse;
   const void* dout;
   void* gq1;
@@ -112,6 +115,14 @@ hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_finalize(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_zero(const BwdParams& p, hipStream_t s);  // empty input: dlambda = 0, dw = 0
+hipError_t launch_lambda_reparam(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int dim,
+                                 float lambda_init, float* out, hipStream_t s);
+hipError_t launch_lambda_reparam_bwd(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int dim,
+                                     const float* dlambda, float* dlq1, float* dlk1, float* dlq2, float* dlk2,
+                                     hipStream_t s);
+
+// lambda as the kernels use it: the device value when one is given
+__device__ __forceinline__ float lambda_of(const float* dev, float host) { return dev ? *dev : host; }
 
 // workspace floats per (b, group, chunk) for decode
 inline int64_t decode_ws_floats_per_chunk(int slots, int dv) { return (int64_t)slots * (dv + 2); }

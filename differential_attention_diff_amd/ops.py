@@ -5,8 +5,10 @@ turns torch tensors into device pointers, element strides and the current HIP
 stream, and raises if the library is missing or returns an error.  Entry
 points mirror the C ABI: ``diffattn_fwd``, ``gda_fwd``, ``gda_fwd_varlen``,
 ``gda_bwd`` (plus ``gda_bwd_workspace_bytes``), ``gda_decode`` (plus
-``gda_decode_workspace_bytes``); ``diff_attention`` wraps the forward and the
-backward as a torch autograd function.
+``gda_decode_workspace_bytes``), ``lambda_reparam`` / ``lambda_reparam_bwd``;
+``diff_attention`` wraps the forward and the backward as a torch autograd
+function and ``lambda_from_params`` the lambda re-parameterisation.  lambda may
+be a float or a device fp32 tensor (read by the kernels, no host round trip).
 """
 
 from __future__ import annotations
@@ -41,7 +43,7 @@ class FwdArgs(ctypes.Structure):
         ("lambda_", ctypes.c_float), ("lambda_init", ctypes.c_float), ("eps", ctypes.c_float),
         ("norm_w", ctypes.c_void_p), ("lse", ctypes.c_void_p),
         ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
-        ("o_maps", ctypes.c_void_p),
+        ("o_maps", ctypes.c_void_p), ("lambda_dev", ctypes.c_void_p),
     ]
 
 
@@ -61,6 +63,7 @@ class BwdArgs(ctypes.Structure):
         ("lambda_", ctypes.c_float), ("lambda_init", ctypes.c_float), ("eps", ctypes.c_float),
         ("norm_w", ctypes.c_void_p),
         ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("lambda_dev", ctypes.c_void_p),
     ]
 
 
@@ -77,6 +80,7 @@ class DecodeArgs(ctypes.Structure):
         ("lambda_", ctypes.c_float), ("lambda_init", ctypes.c_float), ("eps", ctypes.c_float),
         ("norm_w", ctypes.c_void_p),
         ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("lambda_dev", ctypes.c_void_p),
     ]
 
 
@@ -110,6 +114,11 @@ def lib() -> ctypes.CDLL:
         L.gda_decode_workspace_bytes.restype = ctypes.c_size_t
         L.gda_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.gda_decode.restype = ctypes.c_int
+        _fp = ctypes.c_void_p
+        L.da_lambda_reparam.argtypes = [_fp, _fp, _fp, _fp, ctypes.c_int64, ctypes.c_float, _fp, _fp]
+        L.da_lambda_reparam.restype = ctypes.c_int
+        L.da_lambda_reparam_bwd.argtypes = [_fp, _fp, _fp, _fp, ctypes.c_int64, _fp, _fp, _fp, _fp, _fp, _fp]
+        L.da_lambda_reparam_bwd.restype = ctypes.c_int
         L.da_status_str.argtypes = [ctypes.c_int]
         L.da_status_str.restype = ctypes.c_char_p
         L.da_last_error.argtypes = []
@@ -166,6 +175,16 @@ def _map(m, hs):
     return ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), arr
 
 
+def _set_lambda(a, lam):
+    """A float goes by value; a device tensor (one fp32 element) by pointer, read when the kernels run."""
+    if torch.is_tensor(lam):
+        if lam.dtype != torch.float32 or lam.numel() != 1 or not lam.is_cuda:
+            raise ValueError("a lambda tensor must be one fp32 element on the device")
+        a.lambda_, a.lambda_dev = 0.0, lam.data_ptr()
+    else:
+        a.lambda_, a.lambda_dev = float(lam), None
+
+
 def _lead(t: torch.Tensor, k: int):
     if t.stride(-1) != 1:
         raise ValueError("the last dimension must be contiguous")
@@ -184,7 +203,8 @@ def fwd_args(q1, q2, k1, k2, v, out, lam, lam_init, *, eps=1e-5, norm_weight=Non
     nz, nz_keep = _map(noise_of_signal, hs)
     kv, kv_keep = _map(kv_of_signal, hs)
     a.noise_of_signal, a.kv_of_signal = nz, kv
-    a.lambda_, a.lambda_init, a.eps = float(lam), float(lam_init), float(eps)
+    _set_lambda(a, lam)
+    a.lambda_init, a.eps = float(lam_init), float(eps)
     a.norm_w = None if norm_weight is None else norm_weight.data_ptr()
     a.lse = None if lse is None else lse.data_ptr()
     a.o_maps = None if o_maps is None else o_maps.data_ptr()
@@ -252,7 +272,8 @@ def bwd_args(q1, q2, k1, k2, v, o_maps, lse, dout, grads, dlambda, lam, lam_init
     nz, nz_keep = _map(noise_of_signal, hs)
     kv, kv_keep = _map(kv_of_signal, hs)
     a.noise_of_signal, a.kv_of_signal = nz, kv
-    a.lambda_, a.lambda_init, a.eps = float(lam), float(lam_init), float(eps)
+    _set_lambda(a, lam)
+    a.lambda_init, a.eps = float(lam_init), float(eps)
     a.norm_w = None if norm_weight is None else norm_weight.data_ptr()
     a.dtype = _dtype_code(q1)
     a.flags = (DA_CAUSAL if causal else 0) | (0 if normalize else DA_NO_NORM)
@@ -288,7 +309,8 @@ def gda_bwd(q1, q2, k1, k2, v, o_maps, lse, dout, lam, lam_init, *, grads=None, 
 class _DiffAttnFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q1, q2, k1, k2, v, lam, norm_weight, lam_init, eps, causal, normalize, nz, kvm):
-        lam_f = float(lam.detach().reshape(-1)[0].item()) if torch.is_tensor(lam) else float(lam)
+        # a tensor lambda stays on the device (read by the kernels): no host round trip
+        lam_f = lam.detach().reshape(1).float().contiguous() if torch.is_tensor(lam) else float(lam)
         B, N, hs, _ = q1.shape
         lse = torch.empty(2, B, hs, N, dtype=torch.float32, device=q1.device)
         o_maps = torch.empty(2, B, N, hs, v.shape[3], dtype=torch.float32, device=q1.device)
@@ -320,6 +342,45 @@ def diff_attention(q1, q2, k1, k2, v, lam, lam_init, *, norm_weight=None, eps=1e
                              noise_of_signal, kv_of_signal)
 
 
+def lambda_reparam(lq1, lk1, lq2, lk2, lambda_init, *, out=None, stream=None):
+    """lambda = exp(lq1 . lk1) - exp(lq2 . lk2) + lambda_init on the device (fp32 [1])."""
+    vs = [x.contiguous() for x in (lq1, lk1, lq2, lk2)]
+    if any(x.dtype != torch.float32 or not x.is_cuda for x in vs):
+        raise ValueError("the lambda vectors must be fp32 device tensors")
+    out = torch.empty(1, dtype=torch.float32, device=lq1.device) if out is None else out
+    _check(lib().da_lambda_reparam(*(ctypes.c_void_p(x.data_ptr()) for x in vs), vs[0].numel(), float(lambda_init),
+                                   ctypes.c_void_p(out.data_ptr()), _stream(stream)))
+    return out
+
+
+def lambda_reparam_bwd(lq1, lk1, lq2, lk2, dlambda, *, stream=None):
+    """Gradients (dlq1, dlk1, dlq2, dlk2) of lambda_reparam for the device scalar dlambda."""
+    vs = [x.contiguous() for x in (lq1, lk1, lq2, lk2)]
+    outs = [torch.empty_like(x) for x in vs]
+    dl = dlambda.reshape(1).float().contiguous()
+    _check(lib().da_lambda_reparam_bwd(*(ctypes.c_void_p(x.data_ptr()) for x in vs), vs[0].numel(),
+                                       ctypes.c_void_p(dl.data_ptr()), *(ctypes.c_void_p(x.data_ptr()) for x in outs),
+                                       _stream(stream)))
+    return tuple(outs)
+
+
+class _LambdaFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, lq1, lk1, lq2, lk2, lambda_init):
+        ctx.save_for_backward(lq1, lk1, lq2, lk2)
+        return lambda_reparam(lq1, lk1, lq2, lk2, lambda_init).reshape(())
+
+    @staticmethod
+    def backward(ctx, dlam):
+        return lambda_reparam_bwd(*ctx.saved_tensors, dlam) + (None,)
+
+
+def lambda_from_params(lq1, lk1, lq2, lk2, lambda_init):
+    """Differentiable lambda from the four learnable vectors, computed on the device
+    ([DA-blog] "Learnable Lambda Re-parameterization"); pass it to diff_attention."""
+    return _LambdaFn.apply(lq1, lk1, lq2, lk2, lambda_init)
+
+
 def decode_args(q1, q2, k1c, k2c, vc, seq_lens, out, lam, lam_init, *, eps=1e-5, norm_weight=None, normalize=True,
                 chunk=0, noise_of_signal=None, kv_of_signal=None):
     B, hs, d = q1.shape
@@ -335,7 +396,8 @@ def decode_args(q1, q2, k1c, k2c, vc, seq_lens, out, lam, lam_init, *, eps=1e-5,
     nz, nz_keep = _map(noise_of_signal, hs)
     kv, kv_keep = _map(kv_of_signal, hs)
     a.noise_of_signal, a.kv_of_signal = nz, kv
-    a.lambda_, a.lambda_init, a.eps = float(lam), float(lam_init), float(eps)
+    _set_lambda(a, lam)
+    a.lambda_init, a.eps = float(lam_init), float(eps)
     a.norm_w = None if norm_weight is None else norm_weight.data_ptr()
     a.dtype = _dtype_code(q1)
     a.flags = 0 if normalize else DA_NO_NORM

@@ -85,6 +85,9 @@ enum {
  *   lse: device fp32 [2][B][H_s][N] or NULL.  When given, receives the natural
  *     log-sum-exp of each map's scaled logits per (b, h, i): lse[0] for A1,
  *     lse[1] for A2 (what a backward pass re-uses).
+ *   lambda_dev: device fp32 [1] or NULL.  When given, lambda is read from it
+ *     when the kernels run (the host `lambda` is then ignored), e.g. the output
+ *     of da_lambda_reparam: no host round trip per call.
  *   o_maps: device fp32 [2][B][N][H_s][dv] (dense, any dtype) or NULL.  When
  *     given, receives each map's own output A1 V and A2 V per (b, i, h), the
  *     two terms of the DiffAttn difference (what gda_bwd needs besides lse;
@@ -106,6 +109,7 @@ typedef struct da_fwd_args {
   int32_t dtype;    /* da_dtype */
   uint32_t flags;   /* DA_CAUSAL | DA_NO_NORM */
   void* o_maps;
+  const float* lambda_dev;
 } da_fwd_args;
 
 /* Plain differential attention ([DA-blog] DiffAttn + head_bar_i): requires
@@ -155,8 +159,8 @@ da_status gda_fwd_varlen(const da_fwd_args* args, const int32_t* cu_seqlens, int
  *     or NULL; receives dL/dw when the head norm is on and norm_w is given.
  *     lambda_init is a per-layer constant ([DA-blog] lambda_init schedule):
  *     no gradient.
- *   Everything else as in da_fwd_args; DA_CAUSAL and DA_NO_NORM must match the
- *     forward.  With dtype DA_BF16 the key/value map must keep the heads that
+ *   Everything else as in da_fwd_args (lambda_dev included); DA_CAUSAL and
+ *     DA_NO_NORM must match the forward.  With dtype DA_BF16 the key/value map must keep the heads that
  *     share a key/value head together: every key/value head's signal heads
  *     lie in one noise group (true for consecutive maps with H_kv >= H_n);
  *     otherwise DA_EUNSUPPORTED. */
@@ -185,6 +189,7 @@ typedef struct da_bwd_args {
   const float* norm_w;
   int32_t dtype;
   uint32_t flags;
+  const float* lambda_dev;
 } da_bwd_args;
 
 /* Bytes of device workspace gda_bwd needs (shapes and dtype only; pointers
@@ -212,7 +217,8 @@ da_status gda_bwd(const da_bwd_args* args, void* workspace, size_t workspace_byt
  *   chunk: cached positions per split-K partial (a multiple of 128, at most
  *     2048), 0 = automatic (512).  The result does not depend on it beyond
  *     rounding order.
- *   Everything else as in da_fwd_args (the causal flag is implied). */
+ *   Everything else as in da_fwd_args (the causal flag is implied; lambda_dev
+ *     included). */
 typedef struct da_decode_args {
   const void* q1;
   const void* q2;
@@ -230,6 +236,7 @@ typedef struct da_decode_args {
   const float* norm_w;
   int32_t dtype;
   uint32_t flags;   /* DA_NO_NORM only */
+  const float* lambda_dev;
 } da_decode_args;
 
 /* Bytes of device workspace gda_decode needs for these arguments.  Depends on
@@ -243,6 +250,25 @@ size_t gda_decode_workspace_bytes(const da_decode_args* args);
  * a combine kernel merges the chunks, applies the lambda difference and the
  * head norm.  Returns DA_EWORKSPACE if the workspace is NULL or too small. */
 da_status gda_decode(const da_decode_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* lambda on the device ([DA-blog] "Learnable Lambda Re-parameterization",
+ * lambda equation): lambda_out[0] = exp(lq1 . lk1) - exp(lq2 . lk2) +
+ * lambda_init, with lq1, lk1, lq2, lk2 device fp32 vectors of `dim` entries
+ * (the per-layer learnable vectors, dim = the head dimension).  lambda_out is a
+ * device fp32 [1] that the prefill, backward and decode calls can read through
+ * lambda_dev.  DA_EINVAL for NULL or misaligned pointers, dim outside [1, 65536],
+ * a non-finite lambda_init or lambda_out overlapping an input. */
+da_status da_lambda_reparam(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int64_t dim,
+                            float lambda_init, float* lambda_out, void* stream);
+
+/* Gradients of da_lambda_reparam given dlambda (device fp32 [1], e.g. what
+ * gda_bwd wrote): dlq1 = dlambda e1 lk1, dlk1 = dlambda e1 lq1,
+ * dlq2 = -dlambda e2 lk2, dlk2 = -dlambda e2 lq2 with e1 = exp(lq1 . lk1),
+ * e2 = exp(lq2 . lk2); outputs device fp32 [dim] each, written in full.
+ * Errors as for da_lambda_reparam; outputs must not overlap inputs or each other. */
+da_status da_lambda_reparam_bwd(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int64_t dim,
+                                const float* dlambda, float* dlq1, float* dlk1, float* dlq2, float* dlk2,
+                                void* stream);
 
 /* Static description of a status code. */
 const char* da_status_str(int status);

@@ -55,6 +55,7 @@ import numpy as np
 __all__ = [
     "lambda_init_schedule",
     "lambda_reparam",
+    "lambda_reparam_grad",
     "consecutive_map",
     "softmax_rows",
     "head_rms_norm",
@@ -87,9 +88,20 @@ def lambda_reparam(lq1, lk1, lq2, lk2, lambda_init: float) -> float:
     """lambda from the four learnable vectors: exp(lq1 . lk1) - exp(lq2 . lk2)
     + lambda_init ([DA-blog], lambda equation).  The kernels take the folded
     scalar; this exists so the tests can state where that scalar comes from."""
-    a = float(np.dot(np.asarray(lq1, np.float64), np.asarray(lk1, np.float64)))
-    b = float(np.dot(np.asarray(lq2, np.float64), np.asarray(lk2, np.float64)))
+    a = float(np.dot(_as64(lq1).reshape(-1), _as64(lk1).reshape(-1)))
+    b = float(np.dot(_as64(lq2).reshape(-1), _as64(lk2).reshape(-1)))
     return math.exp(a) - math.exp(b) + lambda_init
+
+
+def lambda_reparam_grad(lq1, lk1, lq2, lk2, dlambda: float):
+    """Gradients of ``lambda_reparam`` times dlambda (the chain rule of the
+    lambda equation): d/dlq1 = exp(lq1 . lk1) lk1, d/dlk1 = exp(lq1 . lk1) lq1,
+    d/dlq2 = -exp(lq2 . lk2) lk2, d/dlk2 = -exp(lq2 . lk2) lq2.  Returns float64
+    arrays (dlq1, dlk1, dlq2, dlk2)."""
+    lq1, lk1, lq2, lk2 = (np.asarray(_as64(x), np.float64).reshape(-1) for x in (lq1, lk1, lq2, lk2))
+    e1 = math.exp(float(np.dot(lq1, lk1)))
+    e2 = math.exp(float(np.dot(lq2, lk2)))
+    return dlambda * e1 * lk1, dlambda * e1 * lq1, -dlambda * e2 * lk2, -dlambda * e2 * lq2
 
 
 # ---------------------------------------------------------------------------

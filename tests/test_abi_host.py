@@ -26,8 +26,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = ops.header_functions()
     assert set(names) >= {"diffattn_fwd", "gda_fwd", "gda_fwd_varlen", "gda_bwd", "gda_bwd_workspace_bytes",
-                          "gda_decode", "gda_decode_workspace_bytes", "da_status_str", "da_last_error",
-                          "da_abi_version"}
+                          "gda_decode", "gda_decode_workspace_bytes", "da_lambda_reparam", "da_lambda_reparam_bwd",
+                          "da_status_str", "da_last_error", "da_abi_version"}
     for n in names:
         assert hasattr(L, n), f"libdiffattn.so does not export {n}"
 
@@ -220,6 +220,23 @@ def test_bwd_workspace_required(L):
     a.s_k1[:], a.s_gk1[:] = [64 * 4 * 64, 4 * 64, 64], [64 * 4 * 64, 4 * 64, 64]
     a.s_v[:], a.s_gv[:] = [64 * 4 * 128, 4 * 128, 128], [64 * 4 * 128, 4 * 128, 128]
     assert L.gda_bwd(ctypes.byref(a), None, 0, None) == ops.DA_EWORKSPACE, ops.last_error()
+
+
+def test_lambda_entry_validation(L):
+    f = lambda i: ctypes.c_void_p(FAKE + i * GIB)
+    st = L.da_lambda_reparam(f(0), f(1), f(2), f(3), 0, ctypes.c_float(0.5), f(4), None)
+    assert st == ops.DA_EINVAL and "dim" in ops.last_error()
+    st = L.da_lambda_reparam(f(0), None, f(2), f(3), 64, ctypes.c_float(0.5), f(4), None)
+    assert st == ops.DA_EINVAL and "lk1 is NULL" in ops.last_error()
+    st = L.da_lambda_reparam(f(0), f(1), f(2), f(3), 64, ctypes.c_float(float("inf")), f(4), None)
+    assert st == ops.DA_EINVAL and "finite" in ops.last_error()
+    st = L.da_lambda_reparam(f(0), f(1), f(2), f(3), 64, ctypes.c_float(0.5), ctypes.c_void_p(FAKE + 8), None)
+    assert st == ops.DA_EINVAL and "overlaps lq1" in ops.last_error()
+    st = L.da_lambda_reparam_bwd(f(0), f(1), f(2), f(3), 64, f(4), f(5), f(6), f(7), ctypes.c_void_p(FAKE + 7 * GIB + 2),
+                                 None)
+    assert st == ops.DA_EINVAL and "aligned" in ops.last_error()
+    st = L.da_lambda_reparam_bwd(f(0), f(1), f(2), f(3), 64, f(4), f(5), f(6), f(7), f(5), None)
+    assert st == ops.DA_EINVAL and "dlk2 overlaps dlq1" in ops.last_error()
 
 
 def base_dec(B=64, L_=8192, hs=18, hn=6, hkv=6, d=64, chunk=0):

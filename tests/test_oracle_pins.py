@@ -219,6 +219,20 @@ def test_lambda_reparam():
     assert O.lambda_reparam([1.0], [0.5], [0.0], [0.0], 0.2) == pytest.approx(math.exp(0.5) - 1 + 0.2)
 
 
+def test_lambda_reparam_grad_finite_differences():
+    vs = [rnd((5,), 80 + i, 0.3) for i in range(4)]
+    g = O.lambda_reparam_grad(*vs, 1.7)
+    h = 1e-6
+    for k in range(4):
+        for j in range(5):
+            up = [v.copy() for v in vs]
+            dn = [v.copy() for v in vs]
+            up[k][j] += h
+            dn[k][j] -= h
+            fd = (O.lambda_reparam(*up, 0.3) - O.lambda_reparam(*dn, 0.3)) / (2 * h)
+            assert g[k][j] == pytest.approx(1.7 * fd, rel=1e-7, abs=1e-9)
+
+
 # --- decode is the last row of the prefill --------------------------------------------------
 
 def test_decode_is_last_prefill_row():
