@@ -15,8 +15,8 @@ of the DiffAttn equation counted once, causal pairs only).  The same line
 carries the roofline of the kernel (against the 2.5 PFLOP/s dense bf16 MFMA
 peak), the F_exec view (F_alg plus the second P.V an exact one-pass kernel
 must issue), the grouped (3:1) prefill, the packed variable-length prefill
-(8 sequences of 256..4096 tokens in one call), the split-K decode (HBM GB/s
-against 8 TB/s) and the backward of the two 4096-token layers (gda_bwd) measured
+(8 sequences of 256..4096 tokens in one call), the split-K decode with bf16
+and with e4m3 caches (HBM GB/s against 8 TB/s) and the backward of the two 4096-token layers (gda_bwd) measured
 the same way, and the fp64 CPU oracle timed on a
 bounded sample of the same workload on the host's cores.
 """
@@ -112,7 +112,8 @@ def decode_bytes(w, seq_lens):
     """Each cached K1/V byte of every kv head and K2 byte of every noise head for positions < L_b,
     plus the queries and the output."""
     L = int(np.sum(seq_lens))
-    per_pos = 2 * (w.H_kv * w.d + w.H_n * w.d + w.H_kv * w.dv)
+    ce = 1 if w.cache == "fp8" else 2  # cache bytes per element
+    per_pos = ce * (w.H_kv * w.d + w.H_n * w.d + w.H_kv * w.dv)
     return L * per_pos + 2 * w.B * ((w.H_s + w.H_n) * w.d + w.H_s * w.dv)
 
 
@@ -269,13 +270,14 @@ def bench_decode(w, steps, warmup):
     import torch
     from differential_attention_diff_amd import ops
     inp = W.make_decode_inputs(w)
+    scales = inp.pop("cache_scales", None)
     d = {k: v.cuda() for k, v in inp.items()}
     out = torch.empty(w.B, w.H_s, w.dv, dtype=w.torch_dtype, device="cuda")
     nbytes = ops.gda_decode_workspace_bytes(d["q1"], d["q2"], d["k1_cache"], d["k2_cache"], d["v_cache"],
-                                            d["seq_lens"])
+                                            d["seq_lens"], cache_scales=scales)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     fn = lambda: ops.gda_decode(d["q1"], d["q2"], d["k1_cache"], d["k2_cache"], d["v_cache"], d["seq_lens"],
-                                w.lam, w.lam_init, out=out, workspace=ws, eps=w.eps)
+                                w.lam, w.lam_init, out=out, workspace=ws, eps=w.eps, cache_scales=scales)
     ms = time_steps(fn, steps, warmup)
     nb = decode_bytes(w, inp["seq_lens"].numpy())
     gbs = nb / (ms * 1e-3) / 1e9
@@ -283,7 +285,8 @@ def bench_decode(w, steps, warmup):
         "workload": w.name, "metric": "decode HBM GB/s", "value": gbs, "unit": "GB/s", "ms_per_step": ms,
         "config": {"workload": w.name, "B": w.B, "Lmax": w.N, "len_range": list(w.len_range),
                    "sum_seq_lens": int(inp["seq_lens"].sum()), "H_s": w.H_s, "H_n": w.H_n, "H_kv": w.H_kv,
-                   "d": w.d, "dv": w.dv, "entry": "gda_decode"},
+                   "d": w.d, "dv": w.dv, "cache": "e4m3 + per-cache scale" if w.cache == "fp8" else "bf16",
+                   "entry": "gda_decode"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("decode_bf16.hip", w.name),
                      "bytes_per_launch": nb,
@@ -310,7 +313,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="diff3b_bf16_n4096",
-                    choices=[k for k in W.ORDER if k != "tiny_diff_f32"] + ["gda3to1_varlen_bf16_8x4096"])
+                    choices=[k for k in W.ORDER if k != "tiny_diff_f32"] + ["gda3to1_varlen_bf16_8x4096",
+                                                                             "gda_decode_fp8_b64_l8192"])
     ap.add_argument("--no-extra", action="store_true", help="skip the grouped, packed and decode lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -344,7 +348,8 @@ def main():
         head = (bench_varlen if w.kind == "varlen" else bench_decode)(w, args.steps, args.warmup)
     extra = []
     if not args.no_extra:
-        for name in ("gda3to1_bf16_n4096", "gda_decode_bf16_b64_l8192", "gda3to1_varlen_bf16_8x4096"):
+        for name in ("gda3to1_bf16_n4096", "gda_decode_bf16_b64_l8192", "gda_decode_fp8_b64_l8192",
+                     "gda3to1_varlen_bf16_8x4096"):
             if name == w.name:
                 continue
             ew = W.WORKLOADS[name]

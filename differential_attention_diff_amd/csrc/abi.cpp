@@ -253,6 +253,12 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool chec
                                      a->lambda_init, a->eps);
   if (st != DA_OK) return st;
   if (a->dtype != DA_BF16) return fail(DA_EUNSUPPORTED, "gda_decode has a bf16 kernel only");
+  const bool fp8 = a->cache_dtype == DA_FP8_E4M3;
+  if (fp8) {
+    const float sc[3] = {a->k1_scale, a->k2_scale, a->v_scale};
+    for (float x : sc)
+      if (!(x > 0.0f) || !isfinite(x)) return fail(DA_EINVAL, "fp8 cache scales must be finite and > 0");
+  }
   if (a->d != 64) return fail(DA_EUNSUPPORTED, "gda_decode has a d = 64 kernel only");
   if (a->flags & ~(uint32_t)DA_NO_NORM) return fail(DA_EINVAL, "gda_decode accepts only DA_NO_NORM");
   if (a->chunk < 0 || a->chunk % kChunkQuantum != 0)
@@ -264,17 +270,18 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool chec
   // the partial kernel addresses a chunk's rows with 32-bit byte offsets
   if (a->s_k1[2] > kMaxPosStride || a->s_k2[2] > kMaxPosStride || a->s_v[2] > kMaxPosStride)
     return fail(DA_EUNSUPPORTED, "cache position stride exceeds %d elements", kMaxPosStride);
-  const int es = 2;
+  const int es = 2, ces = fp8 ? 1 : 2;  // element bytes of queries / output, of the caches
   struct T {
     const char* name;
     const void* p;
     const int64_t* s;
-    int nlead;
-  } ts[6] = {{"q1", a->q1, a->s_q1, 2},       {"q2", a->q2, a->s_q2, 2},       {"k1_cache", a->k1_cache, a->s_k1, 3},
-             {"k2_cache", a->k2_cache, a->s_k2, 3}, {"v_cache", a->v_cache, a->s_v, 3}, {"out", a->out, a->s_out, 2}};
+    int nlead, es;
+  } ts[6] = {{"q1", a->q1, a->s_q1, 2, es},         {"q2", a->q2, a->s_q2, 2, es},
+             {"k1_cache", a->k1_cache, a->s_k1, 3, ces}, {"k2_cache", a->k2_cache, a->s_k2, 3, ces},
+             {"v_cache", a->v_cache, a->s_v, 3, ces},    {"out", a->out, a->s_out, 2, es}};
   if (check_pointers) {
     for (auto& t : ts)
-      if ((st = check_strides(t.name, t.p, t.s, t.nlead, es)) != DA_OK) return st;
+      if ((st = check_strides(t.name, t.p, t.s, t.nlead, t.es)) != DA_OK) return st;
     if (!a->seq_lens) return fail(DA_EINVAL, "seq_lens is NULL");
     if ((uintptr_t)a->seq_lens & 3u) return fail(DA_EINVAL, "seq_lens is not 4-byte aligned");
     if (a->norm_w && ((uintptr_t)a->norm_w & 3u)) return fail(DA_EINVAL, "norm_w is not 4-byte aligned");
@@ -302,9 +309,13 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool chec
     p->nu[n] = (int16_t)u;
     umax = std::max(umax, u);
   }
-  int64_t chunk = a->chunk ? a->chunk : kDefaultChunk;
-  int64_t lmax_r = (a->Lmax + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
-  if (chunk > lmax_r) chunk = std::max<int64_t>(kChunkQuantum, lmax_r);
+  // fp8 caches are walked in sub-chunks of 2 x 128 positions
+  const int64_t quantum = fp8 ? 2 * kChunkQuantum : kChunkQuantum;
+  if (a->chunk % quantum != 0)
+    return fail(DA_EINVAL, "chunk must be 0 or a positive multiple of %lld for these caches", (long long)quantum);
+  int64_t chunk = a->chunk ? a->chunk : (fp8 ? 2 * kDefaultChunk : kDefaultChunk);  // same bytes per partial
+  int64_t lmax_r = (a->Lmax + quantum - 1) / quantum * quantum;
+  if (chunk > lmax_r) chunk = std::max<int64_t>(quantum, lmax_r);
   p->chunk = (int)chunk;
   p->nchunks = (int)((a->Lmax + chunk - 1) / chunk);
   p->slots = g + umax;
@@ -335,6 +346,10 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool chec
   p->d = (int)a->d;
   p->dv = (int)a->dv;
   p->g = g;
+  p->fp8 = fp8 ? 1 : 0;
+  p->k1_scale = fp8 ? a->k1_scale : 1.0f;
+  p->k2_scale = fp8 ? a->k2_scale : 1.0f;
+  p->v_scale = fp8 ? a->v_scale : 1.0f;
   p->normalize = (a->flags & DA_NO_NORM) ? 0 : 1;
   p->lam = a->lambda;
   p->lam_init = a->lambda_init;

@@ -12,7 +12,7 @@
 // kernels are organised around keeping enough bytes in flight:
 //
 // Kernel 1 (partial): one workgroup per (chunk of cached positions, noise
-// group, sequence).  The chunk is walked in sub-chunks of kC = 128 positions
+// group, sequence).  The chunk is walked in sub-chunks of kC = 128 positions (256 for e4m3 caches)
 // whose loads -- K2 of the noise head, K1 and V of the group's key/value head
 // (64 KiB for d = 64), each wave instruction reading 1 KiB contiguous -- are
 // all in flight at once, into registers; the next sub-chunk's keys are loaded
@@ -41,6 +41,32 @@ namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 8 cache elements as one register chunk: 16 bytes of bf16 or 8 bytes of fp8
+template <bool FP8>
+struct Chunk {
+  typedef u32x4 T;
+};
+template <>
+struct Chunk<true> {
+  typedef u32x2 T;
+};
+
+// 8 OCP e4m3 bytes (little-endian: element e is byte e) as 8 bf16 in 4 dwords.
+// Every e4m3 value is exact in bf16 (3 mantissa bits, exponents inside bf16's
+// range), so the products below are the same as on bf16 caches of those values.
+__device__ __forceinline__ u32x4 fp8_to_bf16(u32x2 c) {
+  const uint32_t lo = c[0], hi = c[1];
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 f = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, e),
+               __builtin_bit_cast(uint32_t, f)};
+}
+__device__ __forceinline__ u32x4 as_bf16(u32x4 c) { return c; }
+__device__ __forceinline__ u32x4 as_bf16(u32x2 c) { return fp8_to_bf16(c); }
 
 constexpr int kT = 256;       // threads per workgroup
 constexpr int kC = 128;       // cached positions per partial workgroup (the chunk)
@@ -48,9 +74,8 @@ constexpr int kD = 64;        // the kernels are specialised to d = 64, dv = 128
 constexpr int kDV = 128;
 constexpr int kMaxQ = 8;      // g + 1 scored queries per group (largest instantiation)
 constexpr int kMaxOut = 8;    // g + u outputs per group (largest instantiation)
-constexpr int kKC = kC * (kD / 8) / kT;   // 16-B K chunks per thread (4)
-constexpr int kVC = kC * (kDV / 8) / kT;  // 16-B V chunks per thread (8)
-static_assert(kKC == 4 && kVC == 8, "layout below assumes 128 positions, d = 64, 256 threads");
+static_assert(kC * (kD / 8) / kT == 4 && kC * (kDV / 8) / kT == 8,
+              "layout below assumes 128 positions, d = 64, 256 threads");
 
 // Cross-lane steps on DPP (VALU, no LDS round trip): quad_perm xor 1 / xor 2,
 // row_half_mirror (lane i <-> 7 - i of each 8) and row_mirror (i <-> 15 - i of
@@ -103,10 +128,21 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
 // with one key/value head per group, 8 the general case.
 // MULTI: some noise group spans several key/value heads (u > 1); the kernel then
 // re-loads K1 / V per head inside the sub-chunk.  Without it the loops collapse.
-template <int MAXO, bool MULTI>
-__global__ __launch_bounds__(kT, 4) void decode_partial_kernel(DecodeParams p) {
+// FP8: the caches hold OCP e4m3 bytes (8-byte chunks of 8 elements, same thread
+// layout, twice the positions per sub-chunk), converted to bf16 in registers;
+// keys are read as value * k_scale by scaling the scores, values as
+// value * v_scale by scaling the partial outputs.
+template <int MAXO, bool MULTI, bool FP8>
+__global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeParams p) {
   constexpr int kMaxQ = MAXO, kMaxOut = MAXO;
-  __shared__ float S[kMaxQ][kC];                // scores, then weights, of the current sub-chunk
+  constexpr uint32_t ES = FP8 ? 1 : 2;  // cache bytes per element
+  // positions per sub-chunk: fp8 caches take twice as many, so a sub-chunk keeps the
+  // same bytes (and registers) in flight
+  constexpr int CP = FP8 ? 2 * kC : kC;
+  constexpr int kKC = CP * (kD / 8) / kT;   // K chunks of 8 elements per thread
+  constexpr int kVC = CP * (kDV / 8) / kT;  // V chunks of 8 elements per thread
+  typedef typename Chunk<FP8>::T CK;
+  __shared__ float S[kMaxQ][CP];                // scores, then weights, of the current sub-chunk
   __shared__ float ML[3][kMaxQ];                // running max, running sum, last rescale per query
   __shared__ u32x4 QS[kMaxQ][kD / 8];           // the group's queries
   __shared__ float red[kT / 16][kMaxOut][kDV];  // partial outputs per 16-lane row group
@@ -135,28 +171,28 @@ __global__ __launch_bounds__(kT, 4) void decode_partial_kernel(DecodeParams p) {
   // V layout: thread t holds rows t/16 + 16 i (i < 8), channels 8 (t%16) .. +7
   const int vrow = tid >> 4, vcol = tid & 15;
 
-  u32x4 k1r[kKC], k2r[kKC], vr[kVC];
+  CK k1r[kKC], k2r[kKC], vr[kVC];
   // Rows [r0, r0 + ns) of the chunk (relative to key_lo).  Loads are branch-free so the
   // compiler can count them and wait for exactly the ones a step needs: a row past ns
   // re-reads row ns - 1 (in bounds); its score is masked and its weight is zero.
   // Addresses: a uniform 64-bit base (scalar registers) plus a 32-bit per-lane byte
   // offset (the host bounds the position stride so chunk offsets fit in 32 bits).
-  auto load_k = [&](u32x4(&dst)[kKC], const void* base, const int64_t* st, int head, int r0, int ns) {
-    const char* K = (const char*)((const __bf16*)base + b * st[0] + head * st[1] + (int64_t)(key_lo + r0) * st[2]);
-    const uint32_t rs = (uint32_t)st[2] * 2u;
+  auto load_k = [&](CK(&dst)[kKC], const void* base, const int64_t* st, int head, int r0, int ns) {
+    const char* K = (const char*)base + (b * st[0] + head * st[1] + (int64_t)(key_lo + r0) * st[2]) * ES;
+    const uint32_t rs = (uint32_t)st[2] * ES;
 #pragma unroll
     for (int i = 0; i < kKC; ++i) {
       const uint32_t r = (uint32_t)min(krow + 32 * i, ns - 1);
-      dst[i] = *(const u32x4*)(K + (r * rs + 16u * (uint32_t)kcol));
+      dst[i] = *(const CK*)(K + (r * rs + 8u * ES * (uint32_t)kcol));
     }
   };
   auto load_v = [&](int head, int r0, int ns) {
-    const char* V = (const char*)((const __bf16*)p.v + b * p.sv[0] + head * p.sv[1] + (int64_t)(key_lo + r0) * p.sv[2]);
-    const uint32_t rs = (uint32_t)p.sv[2] * 2u;
+    const char* V = (const char*)p.v + (b * p.sv[0] + head * p.sv[1] + (int64_t)(key_lo + r0) * p.sv[2]) * ES;
+    const uint32_t rs = (uint32_t)p.sv[2] * ES;
 #pragma unroll
     for (int i = 0; i < kVC; ++i) {
       const uint32_t r = (uint32_t)min(vrow + 16 * i, ns - 1);
-      vr[i] = *(const u32x4*)(V + (r * rs + 16u * (uint32_t)vcol));
+      vr[i] = *(const CK*)(V + (r * rs + 8u * ES * (uint32_t)vcol));
     }
   };
   // the group's queries in LDS (each thread reads its 8 dims when scoring):
@@ -167,11 +203,13 @@ __global__ __launch_bounds__(kT, 4) void decode_partial_kernel(DecodeParams p) {
                              : (const __bf16*)p.q2 + b * p.sq2[0] + n * p.sq2[1];
     QS[qi][col] = *(const u32x4*)(q + 8 * col);
   }
-  auto score_rows = [&](int qi, const u32x4(&kr)[kKC]) {
+  // scores in log2 units; e4m3 keys carry their cache's scale
+  const float sc1 = p.sm_scale_log2 * (FP8 ? p.k1_scale : 1.0f), sc2 = p.sm_scale_log2 * (FP8 ? p.k2_scale : 1.0f);
+  auto score_rows = [&](int qi, const CK(&kr)[kKC]) {
 #pragma unroll
     for (int i = 0; i < kKC; ++i) {
-      const float sc = sum8(dot8(kr[i], QS[qi][kcol]));
-      if (kcol == 0) S[qi][krow + 32 * i] = sc * p.sm_scale_log2;
+      const float sc = sum8(dot8(as_bf16(kr[i]), QS[qi][kcol]));
+      if (kcol == 0) S[qi][krow + 32 * i] = sc * (qi < g ? sc1 : sc2);
     }
   };
 
@@ -187,7 +225,7 @@ __global__ __launch_bounds__(kT, 4) void decode_partial_kernel(DecodeParams p) {
 
   // ---- every load of the first sub-chunk (the group's first key/value head) up front
   const int kv0 = ukv[0];
-  int ns = min(kC, nk);
+  int ns = min(CP, nk);
   // issue order K2, K1, then V (the scheduler must not interleave them): the scores then
   // wait only for the keys while the values are still in flight
   load_k(k2r, p.k2, p.sk2, n, 0, ns);
@@ -196,8 +234,8 @@ __global__ __launch_bounds__(kT, 4) void decode_partial_kernel(DecodeParams p) {
   load_v(kv0, 0, ns);
   __builtin_amdgcn_sched_barrier(0);
 
-  for (int r0 = 0; r0 < nk; r0 += kC) {
-    const int nxt = r0 + kC, ns_next = min(kC, nk - nxt);
+  for (int r0 = 0; r0 < nk; r0 += CP) {
+    const int nxt = r0 + CP, ns_next = min(CP, nk - nxt);
     __syncthreads();  // the previous sub-chunk's weights are no longer read
     // ---- scores (log2 units): the noise query on K2, each signal query on its K1
 #pragma unroll
@@ -222,17 +260,26 @@ __global__ __launch_bounds__(kT, 4) void decode_partial_kernel(DecodeParams p) {
     __syncthreads();
     // ---- merge this sub-chunk into the running softmax of each query (one wavefront per query)
     for (int qi = wave; qi < nq; qi += kT / 64) {
-      const float s0 = lane < ns ? S[qi][lane] : -INFINITY;
-      const float s1 = lane + 64 < ns ? S[qi][lane + 64] : -INFINITY;
+      constexpr int PL = CP / 64;  // positions per lane
+      float sv[PL];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < PL; ++k) {
+        sv[k] = lane + 64 * k < ns ? S[qi][lane + 64 * k] : -INFINITY;
+        mx = fmaxf(mx, sv[k]);
+      }
       const float mold = ML[0][qi];
-      const float mnew = fmaxf(mold, wave_max(fmaxf(s0, s1)));
+      const float mnew = fmaxf(mold, wave_max(mx));
       // weights are rounded to bf16 here: P.V consumes them as bf16 and the running sum
       // accumulates the same rounded values
-      const float e0 = lane < ns ? round_bf16(__builtin_amdgcn_exp2f(s0 - mnew)) : 0.f;
-      const float e1 = lane + 64 < ns ? round_bf16(__builtin_amdgcn_exp2f(s1 - mnew)) : 0.f;
-      S[qi][lane] = e0;
-      S[qi][lane + 64] = e1;
-      const float sum = wave_sum(e0 + e1);
+      float tot = 0.f;
+#pragma unroll
+      for (int k = 0; k < PL; ++k) {
+        const float e = lane + 64 * k < ns ? round_bf16(__builtin_amdgcn_exp2f(sv[k] - mnew)) : 0.f;
+        S[qi][lane + 64 * k] = e;
+        tot += e;
+      }
+      const float sum = wave_sum(tot);
       if (lane == 0) {
         const float alpha = __builtin_amdgcn_exp2f(mold - mnew);  // 0 on the first sub-chunk
         ML[0][qi] = mnew;
@@ -258,6 +305,7 @@ __global__ __launch_bounds__(kT, 4) void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < kVC; ++i) {
         const int r = vrow + 16 * i;
+        const u32x4 vb = as_bf16(vr[i]);
 #pragma unroll
         for (int o = 0; o < kMaxOut; ++o) {
           int src = -1;
@@ -273,7 +321,7 @@ __global__ __launch_bounds__(kT, 4) void decode_partial_kernel(DecodeParams p) {
             const uint32_t wlo = wb, whi = wb << 16;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const uint32_t vw = vr[i][e];
+              const uint32_t vw = vb[e];
               acc[o][2 * e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, vw),
                                                               __builtin_bit_cast(bf16x2, wlo), acc[o][2 * e], false);
               acc[o][2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, vw),
@@ -307,7 +355,7 @@ __global__ __launch_bounds__(kT, 4) void decode_partial_kernel(DecodeParams p) {
     float x = 0.f;
 #pragma unroll
     for (int k = 0; k < kT / 16; ++k) x += red[k][o][ch];
-    ws[o * (kDV + 2) + 2 + ch] = x;
+    ws[o * (kDV + 2) + 2 + ch] = FP8 ? x * p.v_scale : x;
   }
   if (tid < nout) {
     const int q = tid < g ? tid : g;
@@ -401,17 +449,27 @@ __global__ __launch_bounds__(kT) void decode_combine_kernel(DecodeParams p) {
 
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t s) {
   (void)dtype;
-  if (p.d != kD || p.dv != kDV || p.g + 1 > kMaxQ || p.slots > kMaxOut || p.chunk % kC != 0)
+  if (p.d != kD || p.dv != kDV || p.g + 1 > kMaxQ || p.slots > kMaxOut || p.chunk % (p.fp8 ? 2 * kC : kC) != 0)
     return hipErrorInvalidValue;
   if (p.nchunks > 0) {
     const dim3 grid(p.nchunks, p.Hn, p.B);
     const bool multi = p.slots > p.g + 1;  // some group uses more than one key/value head
-    if (p.g + 1 <= 4 && p.slots <= 4 && !multi)
-      hipLaunchKernelGGL((decode_partial_kernel<4, false>), grid, dim3(kT), 0, s, p);
-    else if (!multi)
-      hipLaunchKernelGGL((decode_partial_kernel<8, false>), grid, dim3(kT), 0, s, p);
-    else
-      hipLaunchKernelGGL((decode_partial_kernel<8, true>), grid, dim3(kT), 0, s, p);
+    const bool small = p.g + 1 <= 4 && p.slots <= 4 && !multi;
+    if (p.fp8) {
+      if (small)
+        hipLaunchKernelGGL((decode_partial_kernel<4, false, true>), grid, dim3(kT), 0, s, p);
+      else if (!multi)
+        hipLaunchKernelGGL((decode_partial_kernel<8, false, true>), grid, dim3(kT), 0, s, p);
+      else
+        hipLaunchKernelGGL((decode_partial_kernel<8, true, true>), grid, dim3(kT), 0, s, p);
+    } else {
+      if (small)
+        hipLaunchKernelGGL((decode_partial_kernel<4, false, false>), grid, dim3(kT), 0, s, p);
+      else if (!multi)
+        hipLaunchKernelGGL((decode_partial_kernel<8, false, false>), grid, dim3(kT), 0, s, p);
+      else
+        hipLaunchKernelGGL((decode_partial_kernel<8, true, false>), grid, dim3(kT), 0, s, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -55,6 +55,8 @@ struct DecodeParams {
   int chunk, nchunks;   // keys per partial, partials per (b, group)
   int slots;            // g (map-1 outputs) + u (distinct V heads of a group for map 2)
   int normalize;
+  int fp8;              // caches are OCP e4m3 bytes, read as value * scale
+  float k1_scale, k2_scale, v_scale;
   float lam, lam_init, eps, sm_scale_log2;
   int16_t members[DA_MAX_HEADS];   // group n's signal heads at [n*g, n*g+g)
   int16_t kv[DA_MAX_HEADS];        // signal head -> kv head

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(HERE, "libdiffattn.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "diffattn.h")
 
 DA_OK, DA_EINVAL, DA_EUNSUPPORTED, DA_EHIP, DA_EWORKSPACE = range(5)
-DA_F32, DA_BF16 = 0, 1
+DA_F32, DA_BF16, DA_FP8_E4M3 = 0, 1, 2
 DA_CAUSAL, DA_NO_NORM = 1, 2
 
 _i64x3 = ctypes.c_int64 * 3
@@ -81,6 +81,8 @@ class DecodeArgs(ctypes.Structure):
         ("norm_w", ctypes.c_void_p),
         ("dtype", ctypes.c_int32), ("flags", ctypes.c_uint32),
         ("lambda_dev", ctypes.c_void_p),
+        ("cache_dtype", ctypes.c_int32), ("k1_scale", ctypes.c_float), ("k2_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -382,7 +384,7 @@ def lambda_from_params(lq1, lk1, lq2, lk2, lambda_init):
 
 
 def decode_args(q1, q2, k1c, k2c, vc, seq_lens, out, lam, lam_init, *, eps=1e-5, norm_weight=None, normalize=True,
-                chunk=0, noise_of_signal=None, kv_of_signal=None):
+                chunk=0, noise_of_signal=None, kv_of_signal=None, cache_scales=None):
     B, hs, d = q1.shape
     a = DecodeArgs()
     a.q1, a.q2, a.k1_cache, a.k2_cache, a.v_cache = (t.data_ptr() for t in (q1, q2, k1c, k2c, vc))
@@ -401,6 +403,11 @@ def decode_args(q1, q2, k1c, k2c, vc, seq_lens, out, lam, lam_init, *, eps=1e-5,
     a.norm_w = None if norm_weight is None else norm_weight.data_ptr()
     a.dtype = _dtype_code(q1)
     a.flags = 0 if normalize else DA_NO_NORM
+    if k1c.dtype in (torch.uint8, torch.float8_e4m3fn):  # e4m3 codes, read as value * scale
+        if cache_scales is None:
+            raise ValueError("fp8 caches need cache_scales = (k1_scale, k2_scale, v_scale)")
+        a.cache_dtype = DA_FP8_E4M3
+        a.k1_scale, a.k2_scale, a.v_scale = (float(x) for x in cache_scales)
     return a, (nz_keep, kv_keep)
 
 

@@ -50,6 +50,7 @@ class Workload:
     causal: bool = True
     len_range: tuple = field(default=(0, 0))   # decode / varlen: inclusive [lo, hi] of the lengths
     seed: int = 0
+    cache: str = "same"  # decode: "same" (caches in dtype) or "fp8" (OCP e4m3 codes with per-cache scales)
 
     @property
     def torch_dtype(self):
@@ -75,6 +76,10 @@ WORKLOADS = {
     "gda_decode_bf16_b64_l8192": Workload("gda_decode_bf16_b64_l8192", "decode", "bf16", B=64, N=8192, H_s=18,
                                           H_n=6, H_kv=6, d=64, dv=128, lam=0.75, lam_init=0.75,
                                           len_range=(4096, 8192), seed=1004),
+    # the same serving step with fp8 (e4m3) caches, one scale per cache tensor
+    "gda_decode_fp8_b64_l8192": Workload("gda_decode_fp8_b64_l8192", "decode", "bf16", B=64, N=8192, H_s=18,
+                                         H_n=6, H_kv=6, d=64, dv=128, lam=0.75, lam_init=0.75,
+                                         len_range=(4096, 8192), seed=1004, cache="fp8"),
     # serving-side prefill: 8 GDA 3:1 sequences of 256..4096 tokens packed in one call
     "gda3to1_varlen_bf16_8x4096": Workload("gda3to1_varlen_bf16_8x4096", "varlen", "bf16", B=8, N=4096, H_s=18,
                                            H_n=6, H_kv=18, d=64, dv=128, lam=0.7, lam_init=0.7,
@@ -132,21 +137,37 @@ def make_varlen_inputs(w: Workload, *, seed: int | None = None, lengths=None):
     return out
 
 
+def _fp8_codes(x: torch.Tensor):
+    """OCP e4m3 codes of x / scale (round to nearest even) with scale = max|x| / 448,
+    the largest finite e4m3 value; returns (uint8 codes, scale)."""
+    scale = float(x.abs().max()) / 448.0 or 1.0
+    return (x / scale).to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), scale
+
+
 def make_decode_inputs(w: Workload, *, seed: int | None = None, B: int | None = None, Lmax: int | None = None,
                        len_range: tuple | None = None):
     """Seeded decode inputs on the CPU: q1 [B,H_s,d], q2 [B,H_n,d], caches
-    [B,H,Lmax,D] and int32 seq_lens [B] drawn uniformly from len_range."""
+    [B,H,Lmax,D] and int32 seq_lens [B] drawn uniformly from len_range.  With
+    fp8 caches the same fp32 draws are stored as e4m3 codes (uint8) and the
+    per-cache scales are returned as "cache_scales" (k1, k2, v)."""
     g = torch.Generator("cpu").manual_seed(w.seed if seed is None else seed)
     B = w.B if B is None else B
     L = w.N if Lmax is None else Lmax
     lo, hi = w.len_range if len_range is None else len_range
     dt = w.torch_dtype
+    cdt = torch.float32 if w.cache == "fp8" else dt
     out = {
         "q1": _draw(g, (B, w.H_s, w.d), w.q_std, dt),
         "q2": _draw(g, (B, w.H_n, w.d), w.q_std, dt),
-        "k1_cache": _draw(g, (B, w.H_kv, L, w.d), w.k_std, dt),
-        "k2_cache": _draw(g, (B, w.H_n, L, w.d), w.k_std, dt),
-        "v_cache": _draw(g, (B, w.H_kv, L, w.dv), w.v_std, dt),
+        "k1_cache": _draw(g, (B, w.H_kv, L, w.d), w.k_std, cdt),
+        "k2_cache": _draw(g, (B, w.H_n, L, w.d), w.k_std, cdt),
+        "v_cache": _draw(g, (B, w.H_kv, L, w.dv), w.v_std, cdt),
     }
     out["seq_lens"] = torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+    if w.cache == "fp8":
+        scales = []
+        for k in ("k1_cache", "k2_cache", "v_cache"):
+            out[k], sc = _fp8_codes(out[k])
+            scales.append(sc)
+        out["cache_scales"] = tuple(scales)
     return out

@@ -63,7 +63,7 @@ typedef enum {
   DA_EWORKSPACE = 4     /* decode workspace missing or too small */
 } da_status;
 
-typedef enum { DA_F32 = 0, DA_BF16 = 1 } da_dtype;
+typedef enum { DA_F32 = 0, DA_BF16 = 1, DA_FP8_E4M3 = 2 } da_dtype;  /* FP8: OCP e4m3 (fn), caches only */
 
 enum {
   DA_CAUSAL = 1u,   /* query i sees keys 0..i (decoder self-attention); without
@@ -214,9 +214,15 @@ da_status gda_bwd(const da_bwd_args* args, void* workspace, size_t workspace_byt
  *   seq_lens: device int32[B]; sequence b's query sees positions 0..L_b-1.
  *     0 <= L_b <= Lmax is the caller's contract (the kernels clamp to
  *     [0, Lmax]); L_b == 0 yields a zero output row.
- *   chunk: cached positions per split-K partial (a multiple of 128, at most
- *     2048), 0 = automatic (512).  The result does not depend on it beyond
- *     rounding order.
+ *   chunk: cached positions per split-K partial (a multiple of 128, of 256
+ *     for e4m3 caches; at most 2048), 0 = automatic (512; 1024 for e4m3
+ *     caches).  The result does not depend on it beyond rounding order.
+ *   cache_dtype: DA_FP8_E4M3 for caches of OCP e4m3 bytes (1 byte per element,
+ *     strides in elements = bytes), each cache read as value * its scale
+ *     (k1_scale, k2_scale, v_scale: finite, > 0; the low-bit KV cache of
+ *     [DA-blog] "Hardware Implementations and Serving Considerations"); any
+ *     other value (0 included) means the caches are in `dtype` and the scales
+ *     are ignored.
  *   Everything else as in da_fwd_args (the causal flag is implied; lambda_dev
  *     included). */
 typedef struct da_decode_args {
@@ -237,6 +243,8 @@ typedef struct da_decode_args {
   int32_t dtype;
   uint32_t flags;   /* DA_NO_NORM only */
   const float* lambda_dev;
+  int32_t cache_dtype;
+  float k1_scale, k2_scale, v_scale;
 } da_decode_args;
 
 /* Bytes of device workspace gda_decode needs for these arguments.  Depends on

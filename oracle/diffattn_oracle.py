@@ -67,6 +67,8 @@ __all__ = [
     "diff_attention_maps",
     "diff_attention_backward",
     "gda_decode",
+    "fp8_e4m3_decode",
+    "gda_decode_fp8",
     "brute_diff_attention",
     "causal_pairs",
     "flops_alg",
@@ -415,6 +417,36 @@ def diff_attention_backward(q1, q2, k1, k2, v, dout, lam: float, lambda_init: fl
     if norm_weight is not None and normalize:
         g["dnorm_weight"] = dw
     return g
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Values of OCP 8-bit e4m3 ("fn") codes, the low-bit KV cache format the
+    serving section of [DA-blog] ("Hardware Implementations and Serving
+    Considerations") points at: bit 7 the sign, bits 6-3 the exponent with
+    bias 7, bits 2-0 the mantissa; exponent 0 is subnormal (m/8 * 2^-6); the
+    all-ones exponent and mantissa is NaN; there are no infinities."""
+    c = np.asarray(codes).astype(np.uint8).astype(np.int64)
+    sign = (c >> 7) & 1
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return np.where(sign == 1, -val, val)
+
+
+def gda_decode_fp8(q1, q2, k1_codes, k2_codes, v_codes, scales, seq_lens, lam: float, lambda_init: float,
+                   **kw) -> np.ndarray:
+    """``gda_decode`` on caches stored as e4m3 codes: each cache is read as its
+    decoded value times its scale (scales = (k1, k2, v))."""
+    k1, k2, v = (fp8_e4m3_decode(_as_codes(c)) * float(sc) for c, sc in zip((k1_codes, k2_codes, v_codes), scales))
+    return gda_decode(q1, q2, k1, k2, v, seq_lens, lam, lambda_init, **kw)
+
+
+def _as_codes(x) -> np.ndarray:
+    """uint8 codes from a NumPy array or a (CPU or device) uint8 torch tensor."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").numpy()
+    return np.asarray(x)
 
 
 # ---------------------------------------------------------------------------

@@ -267,6 +267,23 @@ def test_decode_workspace_bytes(L):
     assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 0 and "exceeds" in ops.last_error()
 
 
+def test_decode_fp8_validation(L):
+    a = base_dec()
+    a.cache_dtype = ops.DA_FP8_E4M3
+    a.k1_scale, a.k2_scale, a.v_scale = 0.01, 0.0, 0.01
+    assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EINVAL and "scales" in ops.last_error()
+    a.k2_scale = float("nan")
+    assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 0 and "scales" in ops.last_error()
+    a.k2_scale = 0.02
+    L_, hkv = 8192, 6
+    a.s_k1[:] = [hkv * L_ * 64, L_ * 64, 64]   # 64-byte e4m3 rows: strides in bytes pass the 16-byte rule
+    a.s_v[:] = [hkv * L_ * 128, L_ * 128, 128]
+    a.s_k2[:] = [6 * L_ * 64, L_ * 64, 64]
+    assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EWORKSPACE, ops.last_error()
+    a.s_k1[2] = 56  # 56 bytes: not a multiple of 16
+    assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EINVAL and "16 bytes" in ops.last_error()
+
+
 def test_decode_validation(L):
     a = base_dec()
     st = L.gda_decode(ctypes.byref(a), None, 0, None)

@@ -100,3 +100,63 @@ def test_full_serving_workload_every_output():
     want = oracle(inp, w.lam, w.lam_init)
     ma, rel = assert_parity(as64(out), want, "bf16", "serving decode")
     print(f"[decode] {w.B}x{w.H_s} outputs: max-abs {ma:.3e} rel-L2 {rel:.3e}", flush=True)
+
+
+# --- fp8 (OCP e4m3) caches -------------------------------------------------------------------
+
+def fp8_inputs(B, L, hs, hn, hkv, lens, seed, d=64):
+    """bf16 queries; caches drawn in fp32, stored as e4m3 codes of x / scale (scale = max|x| / 448)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    out = {"q1": torch.randn(B, hs, d, generator=g).bfloat16(), "q2": torch.randn(B, hn, d, generator=g).bfloat16(),
+           "seq_lens": torch.tensor(lens, dtype=torch.int32)}
+    scales = []
+    for k, h, w in (("k1_cache", hkv, d), ("k2_cache", hn, d), ("v_cache", hkv, 2 * d)):
+        x = torch.randn(B, h, L, w, generator=g)
+        sc = float(x.abs().max()) / 448.0
+        out[k] = (x / sc).to(torch.float8_e4m3fn).view(torch.uint8)
+        scales.append(sc)
+    return out, tuple(scales)
+
+
+def fp8_oracle(inp, scales, lam, li, **kw):
+    return O.gda_decode_fp8(inp["q1"], inp["q2"], inp["k1_cache"], inp["k2_cache"], inp["v_cache"], scales,
+                            inp["seq_lens"], lam, li, **kw)
+
+
+@pytest.mark.parametrize("hs,hn,hkv", [(6, 2, 2), (8, 2, 4), (4, 4, 4)])
+def test_fp8_cache_ragged_lengths(hs, hn, hkv):
+    lens = [0, 1, 2, 127, 128, 129, 511, 700]
+    inp, scales = fp8_inputs(len(lens), 700, hs, hn, hkv, lens, seed=24)
+    out = run(inp, 0.75, 0.4, cache_scales=scales)
+    want = fp8_oracle(inp, scales, 0.75, 0.4)
+    ma, rel = assert_parity(as64(out), want, "bf16", f"fp8 decode {hs}/{hn}/{hkv}")
+    print(f"fp8 decode {hs}/{hn}/{hkv} max-abs {ma:.3e} rel {rel:.3e}")
+    assert torch.all(out[0] == 0)
+
+
+def test_fp8_cache_raw_output_and_split_independence():
+    lens = [2048, 1500, 3]
+    inp, scales = fp8_inputs(3, 2048, 6, 2, 2, lens, seed=25)
+    raw = run(inp, 0.6, 0.3, cache_scales=scales, normalize=False, chunk=256)
+    want = fp8_oracle(inp, scales, 0.6, 0.3, normalize=False)
+    sc = norm_scale(want, 0.3)
+    assert_parity(as64(raw) * sc, want * sc, "bf16", "fp8 raw decode")
+    # another split: the weights are rounded to bf16 against other running maxima
+    # (each within 2^-9 relative); both splits stay within the bar of the oracle
+    a = run(inp, 0.6, 0.5, cache_scales=scales, chunk=256)
+    b = run(inp, 0.6, 0.5, cache_scales=scales, chunk=1024)
+    want = fp8_oracle(inp, scales, 0.6, 0.5)
+    assert_parity(as64(b), want, "bf16", "fp8 decode, chunk 1024")
+    ma, _ = err_stats(as64(b), as64(a))
+    assert ma <= 4 * 2.0 ** -8
+
+
+def test_fp8_full_serving_workload_every_output():
+    w = W.WORKLOADS["gda_decode_fp8_b64_l8192"]
+    inp = W.make_decode_inputs(w)
+    scales = inp.pop("cache_scales")
+    print(f"[{w.name}] inputs ready, scales {scales}", flush=True)
+    out = run(inp, w.lam, w.lam_init, cache_scales=scales, eps=w.eps)
+    want = fp8_oracle(inp, scales, w.lam, w.lam_init, eps=w.eps)
+    ma, rel = assert_parity(as64(out), want, "bf16", w.name)
+    print(f"[{w.name}] max-abs {ma:.3e} rel-L2 {rel:.3e}", flush=True)

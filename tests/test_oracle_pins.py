@@ -476,3 +476,34 @@ def test_maps_are_sdpa_of_each_stream():
     m = O.diff_attention_maps(q1, q2, k1, k2, v)
     np.testing.assert_allclose(m[0], sdpa(q1, k1, v, True), rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(m[1], sdpa(q2, k2, v, True), rtol=1e-10, atol=1e-12)
+
+
+# --- fp8 (OCP e4m3) caches -------------------------------------------------------------------
+
+def test_fp8_e4m3_decode_matches_the_format():
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.fp8_e4m3_decode(codes)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().double().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(lib))
+    ok = ~np.isnan(got)
+    np.testing.assert_array_equal(got[ok], lib[ok])
+    assert O.fp8_e4m3_decode(0x7E) == 448.0 and O.fp8_e4m3_decode(0xFE) == -448.0
+    assert O.fp8_e4m3_decode(0x08) == 2.0 ** -6 and O.fp8_e4m3_decode(0x01) == 2.0 ** -9
+    assert O.fp8_e4m3_decode(0x38) == 1.0 and O.fp8_e4m3_decode(0x3C) == 1.5
+    assert np.isnan(O.fp8_e4m3_decode(0x7F)) and np.isnan(O.fp8_e4m3_decode(0xFF))
+    assert np.signbit(O.fp8_e4m3_decode(0x80)) and O.fp8_e4m3_decode(0x80) == 0.0
+
+
+def test_fp8_decode_is_decode_of_dequantised_caches():
+    rng = np.random.default_rng(62)
+    B, L, hs, hn, hkv, d, dv = 2, 9, 4, 2, 2, 4, 8
+    q1, q2 = rng.standard_normal((B, hs, d)), rng.standard_normal((B, hn, d))
+    codes = [rng.integers(0, 256, (B, h, L, w)).astype(np.uint8) for h, w in ((hkv, d), (hn, d), (hkv, dv))]
+    codes = [np.where((c & 0x7F) == 0x7F, c & 0xF0, c) for c in codes]  # no NaN codes
+    scales = (0.01, 0.02, 0.005)
+    lens = np.array([9, 4])
+    got = O.gda_decode_fp8(q1, q2, *codes, scales, lens, 0.6, 0.3)
+    deq = [O.fp8_e4m3_decode(c) * s for c, s in zip(codes, scales)]
+    np.testing.assert_array_equal(got, O.gda_decode(q1, q2, *deq, lens, 0.6, 0.3))
+    # and a hand check of the dequantisation: code 0x40 is 2.0, times the scale
+    assert O.fp8_e4m3_decode(np.uint8(0x40)) * 0.25 == 0.5
