@@ -50,15 +50,16 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "differential_attention_diff_amd", "csrc")
 MEASURED_TRAFFIC = {
     "fwd_bf16.hip": {
-        "sha256": "7f317fc5d633aba1b272810fd0a882e23d95568bf25620cd475f320cb1bc47d5",
-        "diff3b_bf16_n4096": 147766 * 1024 * 2.0 + 98304 * 1024 * 1.0,
-        "gda3to1_bf16_n4096": 97709 * 1024 * 2.0 + 73728 * 1024 * 1.0,
-        "gda3to1_varlen_bf16_8x4096": 152155 * 1024 * 2.0 + 101300 * 1024 * 1.0,
+        "sha256": "919cfc42c7ca12c375cdcc83117e92d80dc5660711190f48846f9602072f7a3d",
+        "diff3b_bf16_n4096": 147768 * 1024 * 2.0 + 98304 * 1024 * 1.0,
+        "gda3to1_bf16_n4096": 97697 * 1024 * 2.0 + 73728 * 1024 * 1.0,
+        "gda3to1_varlen_bf16_8x4096": 152162 * 1024 * 2.0 + 101300 * 1024 * 1.0,
     },
     "decode_bf16.hip": {
-        "sha256": "26a00461a84f5f191fb6441f605d2af4b2fe720c856883e852475b2df9c102d7",
+        "sha256": "662c0853b95ac2613fe28ad7dd3544669d2a5d88fe6de61707548e122cbf5f9a",
         # one step: decode_partial_kernel + decode_combine_kernel
-        "gda_decode_bf16_b64_l8192": (586379 + 4885) * 1024 * 2.0 + (9680 + 288) * 1024 * 1.0,
+        "gda_decode_bf16_b64_l8192": (586405 + 4885) * 1024 * 2.0 + (9680 + 288) * 1024 * 1.0,
+        "gda_decode_fp8_b64_l8192": (293455 + 2557) * 1024 * 2.0 + (5021 + 288) * 1024 * 1.0,
     },
 }
 
