@@ -10,6 +10,9 @@
 // in log2 units, D1 = do . o1, D2 = do . o2), per query i, visible key j:
 //   p1 = 2^(s1 sc - lse1'), p2 = 2^(s2 sc - lse2'), dp = do_i . v_j
 //   ds1 = p1 (dp - D1),  ds2 = -lambda p2 (dp - D2)
+// The prep pass stores lse2' - log2|lambda| and sgn D2 (-lambda = sgn |lambda|), so
+// the kernels form |lambda| p2 directly and ds2 = (|lambda| p2) (sgn dp - sgn D2),
+// P1 - lambda P2 = p1 + sgn (|lambda| p2).
 //   dQ1 = dS1 K1 / sqrt(d), dK1 = dS1^T Q1 / sqrt(d), dV = (P1 - lambda P2)^T do,
 //   dQ2 = dS2 K2 / sqrt(d), dK2 = dS2^T Q2 / sqrt(d)
 // One dp = do V^T product serves both maps (both use the head's V).
@@ -33,6 +36,8 @@
 // the group (checked on the host): dK1/dV accumulate over that run and are
 // stored when the key/value head changes.
 #include <math.h>
+
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const int t0 = logical / nq;
   const int n = t0 % p.Hn, b = t0 / p.Hn;
   const int q0 = qb * kRB, qw = q0 + wave * kRW, q = qw + l32, qc = min(q, p.N - 1);
-  const float lam = lambda_of(p.lam_dev, p.lam);
+  const float sgn = lambda_of(p.lam_dev, p.lam) > 0.f ? -1.f : 1.f;  // -lambda = sgn |lambda|
   const int kend = p.causal ? min(q0 + kRB, p.N) : p.N;
   const int ntile = (kend + kTR - 1) / kTR;
   const int klast = p.causal ? min(qw + kRW - 1, p.N - 1) : p.N - 1;  // last key this wavefront sees
@@ -212,10 +217,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
       const unsigned char* tk1 = lds + (tile & 1) * STAGE;
       const unsigned char* tk2 = tk1 + C::KT;
       const unsigned char* tv = tk1 + 2 * C::KT;
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
+      // one 32-key block; MASK only where some key of the block is hidden from some
+      // query of the wavefront (the causal diagonal, keys past N)
+      auto block = [&](auto mask, int jb) {
+        constexpr bool MASK = decltype(mask)::value;
         const int key0 = tile * kTR + jb * 32;
-        if (key0 > klast) continue;  // wavefront-uniform: every key of the block is hidden
         f32x16 s1 = {}, s2 = {}, dp = {};
 #pragma unroll
         for (int s = 0; s < C::NKS; ++s) {
@@ -227,12 +233,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
         float d1[16], d2[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 4 * hh + 8 * (r / 4) + (r & 3);
-          const bool vis = key <= kvis;
-          const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.sm_scale_log2, -rs.x)) : 0.f;
-          const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[r], p.sm_scale_log2, -rs.y)) : 0.f;
+          float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.sm_scale_log2, -rs.x));
+          float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[r], p.sm_scale_log2, -rs.y));  // |lambda| P2
+          if (MASK) {
+            const int key = key0 + 4 * hh + 8 * (r / 4) + (r & 3);
+            p1 = key <= kvis ? p1 : 0.f;
+            p2 = key <= kvis ? p2 : 0.f;
+          }
           d1[r] = p1 * (dp[r] - rs.z);
-          d2[r] = -lam * p2 * (dp[r] - rs.w);
+          d2[r] = p2 * __builtin_fmaf(sgn, dp[r], -rs.w);
         }
         bf16x8 b1[2], b2[2];
         to_b(d1, b1[0], b1[1]);
@@ -244,6 +253,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
             dq1[ct] = mfma(rd_tr(tk1, jb * 32, ks, ct, C::KCH, lane), b1[ks], dq1[ct]);
             dq2[ct] = mfma(rd_tr(tk2, jb * 32, ks, ct, C::KCH, lane), b2[ks], dq2[ct]);
           }
+      };
+      const int kfree = p.causal ? min(qw, p.N - 1) : p.N - 1;  // keys every query of the wavefront sees
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) {
+        const int key0 = tile * kTR + jb * 32;
+        if (key0 > klast) continue;  // wavefront-uniform: every key of the block is hidden
+        if (key0 + 31 <= kfree)
+          block(std::false_type{}, jb);
+        else
+          block(std::true_type{}, jb);
       }
       if (tile + 1 < ntile) {
         unsigned char* nt = lds + ((tile + 1) & 1) * STAGE;
@@ -278,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const int t0 = logical / nk;
   const int n = t0 % p.Hn, b = t0 / p.Hn;
   const int k0 = kb * kRB, kw = k0 + wave * kRW, key = kw + l32, kc = min(key, p.N - 1);
-  const float lam = lambda_of(p.lam_dev, p.lam);
+  const float sgn = lambda_of(p.lam_dev, p.lam) > 0.f ? -1.f : 1.f;  // -lambda = sgn |lambda|
   const int qt0 = p.causal ? k0 / kTR : 0;
   const int ntile = (p.N + kTR - 1) / kTR;
 
@@ -340,16 +359,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     load_all(qt0);
     store_all(lds);
     __syncthreads();
-    for (int qt = qt0; qt < ntile; ++qt) {
+    // one query tile (masked throughout: an unmasked copy of the sub-block code does not
+    // fit this wavefront's registers next to the masked one)
+    auto tile_step = [&](int qt, auto tmask) {
       if (qt + 1 < ntile) load_all(qt + 1);
       const unsigned char* tq1 = lds + ((qt - qt0) & 1) * STAGE;
       const unsigned char* tq2 = tq1 + C::KT;
       const unsigned char* tdo = tq1 + 2 * C::KT;
       const float* trs = (const float*)(tq1 + 2 * C::KT + C::VT);
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
+      // one 32-query sub-block; MASK only where some query of it does not see some key of
+      // the wavefront (the causal diagonal, queries past N)
+      auto block = [&](auto mask, int sb) {
+        constexpr bool MASK = decltype(mask)::value;
         const int qs0 = qt * kTR + sb * 32;
-        if (qs0 >= p.N || (p.causal && qs0 + 31 < kw)) continue;  // wavefront-uniform: nothing visible
         f32x16 s1 = {}, s2 = {}, dp = {};
 #pragma unroll
         for (int s = 0; s < C::NKS; ++s) {
@@ -362,14 +384,18 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int qi = sb * 32 + 4 * hh + 8 * (r / 4) + (r & 3);  // query row in the tile
-          const int qg = qt * kTR + qi;
-          const bool vis = qg < p.N && (!p.causal || qg >= key);
           const float4 st = *(const float4*)(trs + 4 * qi);
-          const float p1 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.sm_scale_log2, -st.x)) : 0.f;
-          const float p2 = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s2[r], p.sm_scale_log2, -st.y)) : 0.f;
-          pc[r] = __builtin_fmaf(-lam, p2, p1);
+          float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.sm_scale_log2, -st.x));
+          float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[r], p.sm_scale_log2, -st.y));  // |lambda| P2
+          if (MASK) {
+            const int qg = qs0 + qi - sb * 32;
+            const bool vis = qg < p.N && (!p.causal || qg >= key);
+            p1 = vis ? p1 : 0.f;
+            p2 = vis ? p2 : 0.f;
+          }
+          pc[r] = __builtin_fmaf(sgn, p2, p1);
           d1[r] = p1 * (dp[r] - st.z);
-          d2[r] = -lam * p2 * (dp[r] - st.w);
+          d2[r] = p2 * __builtin_fmaf(sgn, dp[r], -st.w);
         }
         bf16x8 bc[2], b1[2], b2[2];
         to_b(pc, bc[0], bc[1]);
@@ -385,10 +411,17 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
             dk2[ct] = mfma(rd_tr(tq2, sb * 32, ks, ct, C::KCH, lane), b2[ks], dk2[ct]);
           }
         }
+      };
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const int qs0 = qt * kTR + sb * 32;
+        if (qs0 >= p.N || (p.causal && qs0 + 31 < kw)) continue;  // wavefront-uniform: nothing visible
+        block(tmask, sb);
       }
       if (qt + 1 < ntile) store_all(lds + ((qt + 1 - qt0) & 1) * STAGE);
       __syncthreads();
-    }
+    };
+    for (int qt = qt0; qt < ntile; ++qt) tile_step(qt, std::true_type{});
   }
   if (key < p.N) {
     store_rows<C::NDT>((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)key * p.sgk1[1] + cur * p.sgk1[2], dk1, p.sm_scale,

@@ -8,6 +8,8 @@
 // D1, D2) and do, per query i and visible key j of signal head h:
 //   p1 = 2^(s1 sc - lse1'), p2 = 2^(s2 sc - lse2'), dp = do_i . v_j
 //   ds1 = p1 (dp - D1),  ds2 = -lambda p2 (dp - D2)
+// (the statistics hold lse2' - log2|lambda| and sgn D2 with -lambda = sgn |lambda|:
+// the code forms |lambda| p2 and ds2 = (|lambda| p2) (sgn dp - sgn D2))
 //   dq1_i += ds1 k1_j / sqrt(d)   dk1_j += ds1 q1_i / sqrt(d)   dv_j += (p1 - lambda p2) do_i
 //   dq2_i += ds2 k2_j / sqrt(d)   dk2_j += ds2 q2_i / sqrt(d)
 // Shared heads are summed inside one wavefront (a noise group's signal heads
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(BwdParams p) {
   const int i = p.N - 1 - (int)blockIdx.x;  // longest rows first
   const int n = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x, d = p.d, dv = p.dv;
-  const float lam = lambda_of(p.lam_dev, p.lam);
+  const float sgn = lambda_of(p.lam_dev, p.lam) > 0.f ? -1.f : 1.f;
   __shared__ float q1s[64], q2s[64], dos[128], ds1s[64], ds2s[64];
   const float* q2 = (const float*)p.q2 + b * p.sq2[0] + (int64_t)i * p.sq2[1] + n * p.sq2[2];
   if (lane < d) q2s[lane] = q2[lane];
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(BwdParams p) {
         const float p1 = exp2f(fmaf(s1, p.sm_scale_log2, -rs.l1));
         const float p2 = exp2f(fmaf(s2, p.sm_scale_log2, -rs.l2));
         ds1 = p1 * (dp - rs.d1);
-        ds2 = -lam * p2 * (dp - rs.d2);
+        ds2 = p2 * fmaf(sgn, dp, -rs.d2);
       }
       ds1s[lane] = ds1;
       ds2s[lane] = ds2;
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(BwdParams p) {
 __global__ __launch_bounds__(64) void bwd_f32_dk2_kernel(BwdParams p) {
   const int j = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x, d = p.d, dv = p.dv;
-  const float lam = lambda_of(p.lam_dev, p.lam);
+  const float sgn = lambda_of(p.lam_dev, p.lam) > 0.f ? -1.f : 1.f;
   __shared__ float k2s[64], vs[128], ds2s[64];
   const float* k2 = (const float*)p.k2 + b * p.sk2[0] + (int64_t)j * p.sk2[1] + n * p.sk2[2];
   if (lane < d) k2s[lane] = k2[lane];
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(64) void bwd_f32_dk2_kernel(BwdParams p) {
         const RowStat rs = row_stat(p, b, h, i);
         const float s2 = dot_lds(k2s, q2 + (int64_t)i * p.sq2[1], d);
         const float dp = dot_lds(vs, (const float*)p.dop + (((int64_t)b * p.N + i) * p.Hs + h) * dv, dv);
-        ds2 = -lam * exp2f(fmaf(s2, p.sm_scale_log2, -rs.l2)) * (dp - rs.d2);
+        ds2 = exp2f(fmaf(s2, p.sm_scale_log2, -rs.l2)) * fmaf(sgn, dp, -rs.d2);
       }
       ds2s[lane] = ds2;
       __syncthreads();
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(64) void bwd_f32_dk2_kernel(BwdParams p) {
 __global__ __launch_bounds__(64) void bwd_f32_dk1dv_kernel(BwdParams p) {
   const int j = blockIdx.x, k = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x, d = p.d, dv = p.dv;
-  const float lam = lambda_of(p.lam_dev, p.lam);
+  const float sgn = lambda_of(p.lam_dev, p.lam) > 0.f ? -1.f : 1.f;
   __shared__ float k1s[64], k2s[64], vs[128], ds1s[64], pcs[64];
   const float* k1 = (const float*)p.k1 + b * p.sk1[0] + (int64_t)j * p.sk1[1] + k * p.sk1[2];
   const float* v = (const float*)p.v + b * p.sv[0] + (int64_t)j * p.sv[1] + k * p.sv[2];
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(64) void bwd_f32_dk1dv_kernel(BwdParams p) {
         const float p1 = exp2f(fmaf(s1, p.sm_scale_log2, -rs.l1));
         const float p2 = exp2f(fmaf(s2, p.sm_scale_log2, -rs.l2));
         ds1 = p1 * (dp - rs.d1);
-        pc = fmaf(-lam, p2, p1);
+        pc = fmaf(sgn, p2, p1);
       }
       ds1s[lane] = ds1;
       pcs[lane] = pc;

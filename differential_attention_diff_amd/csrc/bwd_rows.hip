@@ -82,6 +82,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   const int64_t plane = rows * DV;  // one map of o_maps
   const float cst = 1.0f - p.lam_init;
   const float lam = lambda_of(p.lam_dev, p.lam);
+  const float sgn = lam > 0.f ? -1.f : 1.f, llam = log2f(fabsf(lam));  // log2 0 = -inf
   double lam_part = 0.0, dw[8] = {};  // sums over many rows: fp64
   float w[8];
 #pragma unroll
@@ -139,7 +140,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
     if (valid && sub == 0) {
       const int64_t li = ((int64_t)b * p.Hs + h) * p.N + i;
       const float l1 = p.lse[li], l2 = p.lse[(int64_t)p.B * p.Hs * p.N + li];
-      *(float4*)(p.rowstat + 4 * li) = make_float4(l1 * kLog2e, l2 * kLog2e, D1, D2);
+      // map 2 folded with lambda: 2^(s - (lse2' - log2|lambda|)) = |lambda| P2 (0 for
+      // lambda = 0), and sgn D2 with -lambda = sgn |lambda|
+      *(float4*)(p.rowstat + 4 * li) = make_float4(l1 * kLog2e, l2 * kLog2e - llam, D1, sgn * D2);
     }
   }
   // sums over the wavefront's row slots, then over the 4 wavefronts, into this

@@ -68,8 +68,9 @@ struct DecodeParams {
 // Backward.  Workspace sections (offsets in bytes, each 256-aligned):
 //   dop     [B][N][H_s][dv] dense, the gradient at o (head norm undone), in
 //           the storage dtype (the MFMA operand of the bf16 passes)
-//   rowstat [B][H_s][N] x float4 {lse1 log2(e), lse2 log2(e), D1, D2} with
-//           D1 = dop . o1 and D2 = dop . o2 per row
+//   rowstat [B][H_s][N] x float4 {lse1 log2(e), lse2 log2(e) - log2|lambda|,
+//           D1, sgn D2} with D1 = dop . o1, D2 = dop . o2 per row and
+//           -lambda = sgn |lambda| (so 2^(s2 sc - .y) is |lambda| P2)
 //   partial [prep workgroups][1 + dv] fp64: per-workgroup sums of -D2 (for
 //           dlambda) and of dy c o / r per channel (for dw)
 struct BwdParams {
