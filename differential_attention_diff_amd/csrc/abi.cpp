@@ -311,6 +311,17 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool chec
   }
   // fp8 caches are walked in sub-chunks of 2 x 128 positions
   const int64_t quantum = fp8 ? 2 * kChunkQuantum : kChunkQuantum;
+  if (a->block_table) {  // paged caches: every sub-chunk inside one block
+    if (a->block_size < quantum || a->block_size % quantum != 0 || a->block_size > INT32_MAX)
+      return fail(DA_EUNSUPPORTED, "block_size %lld: paged caches need a multiple of %lld positions",
+                  (long long)a->block_size, (long long)quantum);
+    if (a->max_blocks < 1 || a->num_blocks < 1 || a->max_blocks > INT32_MAX || a->num_blocks > INT32_MAX)
+      return fail(DA_EINVAL, "max_blocks and num_blocks must be in [1, 2^31)");
+    if (a->Lmax > a->max_blocks * a->block_size)
+      return fail(DA_EINVAL, "Lmax %lld exceeds max_blocks x block_size", (long long)a->Lmax);
+    if (check_pointers && ((uintptr_t)a->block_table & 3u))
+      return fail(DA_EINVAL, "block_table is not 4-byte aligned");
+  }
   if (a->chunk % quantum != 0)
     return fail(DA_EINVAL, "chunk must be 0 or a positive multiple of %lld for these caches", (long long)quantum);
   int64_t chunk = a->chunk ? a->chunk : (fp8 ? 2 * kDefaultChunk : kDefaultChunk);  // same bytes per partial
@@ -347,6 +358,10 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool chec
   p->dv = (int)a->dv;
   p->g = g;
   p->fp8 = fp8 ? 1 : 0;
+  p->block_table = a->block_table;
+  p->block_size = a->block_table ? (int)a->block_size : 0;
+  p->max_blocks = a->block_table ? (int)a->max_blocks : 0;
+  p->num_blocks = a->block_table ? (int)a->num_blocks : 0;
   p->k1_scale = fp8 ? a->k1_scale : 1.0f;
   p->k2_scale = fp8 ? a->k2_scale : 1.0f;
   p->v_scale = fp8 ? a->v_scale : 1.0f;

@@ -177,8 +177,16 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
   // re-reads row ns - 1 (in bounds); its score is masked and its weight is zero.
   // Addresses: a uniform 64-bit base (scalar registers) plus a 32-bit per-lane byte
   // offset (the host bounds the position stride so chunk offsets fit in 32 bits).
+  // rows [pos, pos + CP) of a cache: one block of a paged cache holds the whole sub-chunk
+  auto cache_row0 = [&](const int64_t* st, int head, int pos) -> int64_t {
+    if (p.block_table) {
+      const int blk = min(max(p.block_table[(int64_t)b * p.max_blocks + pos / p.block_size], 0), p.num_blocks - 1);
+      return blk * st[0] + head * st[1] + (int64_t)(pos % p.block_size) * st[2];
+    }
+    return b * st[0] + head * st[1] + (int64_t)pos * st[2];
+  };
   auto load_k = [&](CK(&dst)[kKC], const void* base, const int64_t* st, int head, int r0, int ns) {
-    const char* K = (const char*)base + (b * st[0] + head * st[1] + (int64_t)(key_lo + r0) * st[2]) * ES;
+    const char* K = (const char*)base + cache_row0(st, head, key_lo + r0) * ES;
     const uint32_t rs = (uint32_t)st[2] * ES;
 #pragma unroll
     for (int i = 0; i < kKC; ++i) {
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
     }
   };
   auto load_v = [&](int head, int r0, int ns) {
-    const char* V = (const char*)p.v + (b * p.sv[0] + head * p.sv[1] + (int64_t)(key_lo + r0) * p.sv[2]) * ES;
+    const char* V = (const char*)p.v + cache_row0(p.sv, head, key_lo + r0) * ES;
     const uint32_t rs = (uint32_t)p.sv[2] * ES;
 #pragma unroll
     for (int i = 0; i < kVC; ++i) {

@@ -56,6 +56,8 @@ struct DecodeParams {
   int slots;            // g (map-1 outputs) + u (distinct V heads of a group for map 2)
   int normalize;
   int fp8;              // caches are OCP e4m3 bytes, read as value * scale
+  const int32_t* block_table;  // paged caches: [B][max_blocks] or nullptr
+  int block_size, max_blocks, num_blocks;
   float k1_scale, k2_scale, v_scale;
   float lam, lam_init, eps, sm_scale_log2;
   int16_t members[DA_MAX_HEADS];   // group n's signal heads at [n*g, n*g+g)

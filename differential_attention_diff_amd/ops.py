@@ -83,6 +83,8 @@ class DecodeArgs(ctypes.Structure):
         ("lambda_dev", ctypes.c_void_p),
         ("cache_dtype", ctypes.c_int32), ("k1_scale", ctypes.c_float), ("k2_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
+        ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int64), ("max_blocks", ctypes.c_int64),
+        ("num_blocks", ctypes.c_int64),
     ]
 
 
@@ -384,7 +386,7 @@ def lambda_from_params(lq1, lk1, lq2, lk2, lambda_init):
 
 
 def decode_args(q1, q2, k1c, k2c, vc, seq_lens, out, lam, lam_init, *, eps=1e-5, norm_weight=None, normalize=True,
-                chunk=0, noise_of_signal=None, kv_of_signal=None, cache_scales=None):
+                chunk=0, noise_of_signal=None, kv_of_signal=None, cache_scales=None, block_table=None):
     B, hs, d = q1.shape
     a = DecodeArgs()
     a.q1, a.q2, a.k1_cache, a.k2_cache, a.v_cache = (t.data_ptr() for t in (q1, q2, k1c, k2c, vc))
@@ -408,6 +410,14 @@ def decode_args(q1, q2, k1c, k2c, vc, seq_lens, out, lam, lam_init, *, eps=1e-5,
             raise ValueError("fp8 caches need cache_scales = (k1_scale, k2_scale, v_scale)")
         a.cache_dtype = DA_FP8_E4M3
         a.k1_scale, a.k2_scale, a.v_scale = (float(x) for x in cache_scales)
+    if block_table is not None:  # paged: caches are pools [num_blocks, H, block_size, D]
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be an int32 [B, max_blocks] tensor")
+        if not block_table.is_contiguous() or block_table.device != q1.device:
+            raise ValueError("block_table must be contiguous and on the device of q1")
+        a.block_table = block_table.data_ptr()
+        a.block_size, a.max_blocks, a.num_blocks = k1c.shape[2], block_table.shape[1], k1c.shape[0]
+        a.Lmax = a.max_blocks * a.block_size
     return a, (nz_keep, kv_keep)
 
 

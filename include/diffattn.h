@@ -217,6 +217,15 @@ da_status gda_bwd(const da_bwd_args* args, void* workspace, size_t workspace_byt
  *   chunk: cached positions per split-K partial (a multiple of 128, of 256
  *     for e4m3 caches; at most 2048), 0 = automatic (512; 1024 for e4m3
  *     caches).  The result does not depend on it beyond rounding order.
+ *   block_table: device int32 [B][max_blocks] or NULL.  When given the caches
+ *     are paged: each cache is a pool [num_blocks][heads][block_size][width]
+ *     (strides of (block, head, position) in s_k1 / s_k2 / s_v) and position p
+ *     of sequence b is row p % block_size of block block_table[b][p /
+ *     block_size] (the paged KV cache of serving engines).  block_size is a
+ *     multiple of 128 (of 256 for e4m3 caches) so that every sub-chunk of 128
+ *     (256) positions lies in one block; Lmax <= max_blocks * block_size; block
+ *     indices are clamped to [0, num_blocks - 1] (a broken table never reads
+ *     outside the pool); DA_EUNSUPPORTED for other block sizes.
  *   cache_dtype: DA_FP8_E4M3 for caches of OCP e4m3 bytes (1 byte per element,
  *     strides in elements = bytes), each cache read as value * its scale
  *     (k1_scale, k2_scale, v_scale: finite, > 0; the low-bit KV cache of
@@ -245,6 +254,8 @@ typedef struct da_decode_args {
   const float* lambda_dev;
   int32_t cache_dtype;
   float k1_scale, k2_scale, v_scale;
+  const int32_t* block_table;
+  int64_t block_size, max_blocks, num_blocks;
 } da_decode_args;
 
 /* Bytes of device workspace gda_decode needs for these arguments.  Depends on

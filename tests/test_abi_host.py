@@ -284,6 +284,23 @@ def test_decode_fp8_validation(L):
     assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EINVAL and "16 bytes" in ops.last_error()
 
 
+def test_decode_paged_validation(L):
+    a = base_dec()
+    a.block_table = FAKE + 50 * GIB
+    a.block_size, a.max_blocks, a.num_blocks = 64, 128, 8192
+    assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EUNSUPPORTED and "block_size" in ops.last_error()
+    a.block_size, a.max_blocks = 256, 16  # 4096 positions < Lmax 8192
+    assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EINVAL and "Lmax" in ops.last_error()
+    a.max_blocks, a.num_blocks = 32, 0
+    assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EINVAL and "num_blocks" in ops.last_error()
+    a.num_blocks = 2048
+    assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EWORKSPACE, ops.last_error()
+    a.cache_dtype = ops.DA_FP8_E4M3
+    a.k1_scale = a.k2_scale = a.v_scale = 0.01
+    a.block_size, a.max_blocks = 128, 64  # e4m3 caches need blocks of 256 positions
+    assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EUNSUPPORTED and "256" in ops.last_error()
+
+
 def test_decode_validation(L):
     a = base_dec()
     st = L.gda_decode(ctypes.byref(a), None, 0, None)

@@ -160,3 +160,40 @@ def test_fp8_full_serving_workload_every_output():
     want = fp8_oracle(inp, scales, w.lam, w.lam_init, eps=w.eps)
     ma, rel = assert_parity(as64(out), want, "bf16", w.name)
     print(f"[{w.name}] max-abs {ma:.3e} rel-L2 {rel:.3e}", flush=True)
+
+
+# --- paged caches (block tables) -------------------------------------------------------------
+
+def to_pages(cache, block_size, perm):
+    """[B, H, L, D] -> pool [B * L / block_size, H, block_size, D] with sequence b's block j at
+    pool index perm[b * nb + j]."""
+    B, H, L, D = cache.shape
+    nb = L // block_size
+    blocks = cache.reshape(B, H, nb, block_size, D).permute(0, 2, 1, 3, 4).reshape(B * nb, H, block_size, D)
+    pool = torch.empty_like(blocks)
+    pool[perm] = blocks
+    return pool.contiguous(), perm.reshape(B, nb).to(torch.int32)
+
+
+@pytest.mark.parametrize("fp8,block_size", [(False, 128), (False, 512), (True, 256)])
+def test_paged_caches_equal_contiguous(fp8, block_size):
+    lens = [1, 129, 700, 1024, 0, 513]
+    L = 1024
+    if fp8:
+        inp, scales = fp8_inputs(len(lens), L, 6, 2, 2, lens, seed=26)
+        kw = dict(cache_scales=scales)
+    else:
+        inp, kw = decode_inputs(len(lens), L, 6, 2, 2, lens, seed=26), {}
+    ref = run(inp, 0.7, 0.4, **kw)
+    g = torch.Generator("cpu").manual_seed(27)
+    perm = torch.randperm(len(lens) * (L // block_size), generator=g)
+    paged = dict(inp)
+    for k in ("k1_cache", "k2_cache", "v_cache"):
+        paged[k], table = to_pages(inp[k], block_size, perm)
+    d = to_dev(paged)
+    out = ops.gda_decode(d["q1"], d["q2"], d["k1_cache"], d["k2_cache"], d["v_cache"], d["seq_lens"], 0.7, 0.4,
+                         block_table=table.cuda(), **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)  # same products in the same order
+    want = fp8_oracle(inp, scales, 0.7, 0.4) if fp8 else oracle(inp, 0.7, 0.4)
+    assert_parity(as64(out), want, "bf16", f"paged decode fp8={fp8} block {block_size}")
