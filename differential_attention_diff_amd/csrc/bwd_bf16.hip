@@ -147,14 +147,71 @@ __device__ __forceinline__ int xcd_logical(int bid, int total) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ pass: workgroup = (b, noise group n, 128 queries)
+// dQ pass: workgroup = (b, noise group n, 128 queries), 8 wavefronts of 16 queries
+// on v_mfma_f32_16x16x32_bf16 (lane l: A row l%16, B column l%16, k 8 (l/16) .. +7;
+// accumulator rows 4 (l/16) + r of column l%16), so a wavefront needs about half
+// the registers of a 32-query one and two fit per SIMD.
 // ---------------------------------------------------------------------------
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+constexpr int kQW16 = 16;                 // queries per dQ wavefront
+constexpr int kDqWaves = kRB / kQW16;     // 8
+constexpr int kDqThreads = 64 * kDqWaves;
+
+__device__ __forceinline__ f32x4v mfma16(bf16x8 a, bf16x8 b, f32x4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Rows [r0, r0 + 64) of a tensor into an LDS tile by NT threads (see tile_load); a
+// tile of fewer 16-byte chunks than threads leaves the last threads idle.
+template <int NT, int CH>
+struct TileLoads {
+  static constexpr int n = (kTR * CH + NT - 1) / NT;
+};
+template <int NT, int CH, int L>
+__device__ __forceinline__ void tile_load_n(u32x4 (&reg)[L], const __bf16* base, int64_t rs, int r0, int last) {
+  static_assert(L == TileLoads<NT, CH>::n, "register count");
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    const int idx = (int)threadIdx.x + NT * k, r = idx / CH, c = idx % CH;
+    if (kTR * CH % NT == 0 || idx < kTR * CH) reg[k] = *(const u32x4*)(base + (int64_t)min(r0 + r, last) * rs + c * 8);
+  }
+}
+template <int NT, int CH, int L>
+__device__ __forceinline__ void tile_store_n(unsigned char* t, const u32x4 (&reg)[L]) {
+  static_assert(L == TileLoads<NT, CH>::n, "register count");
+#pragma unroll
+  for (int k = 0; k < L; ++k) {
+    const int idx = (int)threadIdx.x + NT * k, r = idx / CH, c = idx % CH;
+    if (kTR * CH % NT == 0 || idx < kTR * CH) *(u32x4*)(t + swz(r, c, CH)) = reg[k];
+  }
+}
+
+// A operand of a 16 x 32 step read row-wise: lane l holds row rb + l%16, elements
+// 32 s + 8 (l/16) .. + 7.
+__device__ __forceinline__ bf16x8 rd_rows16(const unsigned char* t, int rb, int s, int ch, int lane) {
+  return *(const bf16x8*)(t + swz(rb + (lane & 15), 4 * s + (lane >> 4), ch));
+}
+// Transposed A operand of a 16 x 32 step: rows rb + {4 (l/16) + 0..3} and rb + 16 + {..}
+// (the order of two 16-row accumulator tiles), columns 16 ct + l%16.  Lane i of a 16-lane
+// group reads row 4 (l/16) + i/4 at columns 16 ct + 4 (i%4); the transposing read hands
+// lane i the 4 rows of column 16 ct + i.
+__device__ __forceinline__ bf16x8 rd_tr16(const unsigned char* t, int rb, int ct, int ch, int lane) {
+  const int row = rb + 4 * (lane >> 4) + (lane & 15) / 4;
+  const int col = ct * 16 + 4 * (lane & 3);
+  const int cc = col >> 3, within = (col & 7) * 2;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + swz(row, cc, ch) + within));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + swz(row + 16, cc, ch) + within));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
   using C = BC<D>;
   constexpr int STAGE = 2 * C::KT + C::VT;
+  constexpr int NS = D / 32, NVS = C::DV / 32, NDT = D / 16;   // k steps over d, dv; 16-row d tiles
+  constexpr int KL = TileLoads<kDqThreads, C::KCH>::n, VL = TileLoads<kDqThreads, C::VCH>::n;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
-  const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, jg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const int nq = (p.N + kRB - 1) / kRB;
@@ -162,99 +219,101 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const int qb = nq - 1 - logical % nq;  // longest causal range first
   const int t0 = logical / nq;
   const int n = t0 % p.Hn, b = t0 / p.Hn;
-  const int q0 = qb * kRB, qw = q0 + wave * kRW, q = qw + l32, qc = min(q, p.N - 1);
+  const int q0 = qb * kRB, qw = q0 + wave * kQW16, q = qw + l16, qc = min(q, p.N - 1);
   const float sgn = lambda_of(p.lam_dev, p.lam) > 0.f ? -1.f : 1.f;  // -lambda = sgn |lambda|
   const int kend = p.causal ? min(q0 + kRB, p.N) : p.N;
   const int ntile = (kend + kTR - 1) / kTR;
-  const int klast = p.causal ? min(qw + kRW - 1, p.N - 1) : p.N - 1;  // last key this wavefront sees
-  const int kvis = p.causal ? min(q, p.N - 1) : p.N - 1;              // last key this lane sees
+  const int klast = p.causal ? min(qw + kQW16 - 1, p.N - 1) : p.N - 1;  // last key this wavefront sees
+  const int kvis = p.causal ? min(q, p.N - 1) : p.N - 1;                  // last key this lane sees
+  const int kfree = p.causal ? min(qw, p.N - 1) : p.N - 1;                // keys every query sees
 
   const __bf16* K2 = (const __bf16*)p.k2 + b * p.sk2[0] + n * p.sk2[2];
-  bf16x8 q2f[C::NKS];
+  bf16x8 q2f[NS];
   {
     const __bf16* Q2 = (const __bf16*)p.q2 + b * p.sq2[0] + (int64_t)qc * p.sq2[1] + n * p.sq2[2];
 #pragma unroll
-    for (int s = 0; s < C::NKS; ++s) q2f[s] = *(const bf16x8*)(Q2 + 16 * s + 8 * hh);
+    for (int s = 0; s < NS; ++s) q2f[s] = *(const bf16x8*)(Q2 + 32 * s + 8 * jg);
   }
-  f32x16 dq2[C::NDT];
+  f32x4v dq2[NDT];
 #pragma unroll
-  for (int ct = 0; ct < C::NDT; ++ct) dq2[ct] = f32x16{};
+  for (int ct = 0; ct < NDT; ++ct) dq2[ct] = f32x4v{};
 
   for (int mem = 0; mem < p.g; ++mem) {
     const int h = __builtin_amdgcn_readfirstlane(p.members[n * p.g + mem]);
     const int kh = __builtin_amdgcn_readfirstlane(p.kv[h]);
     const __bf16* K1 = (const __bf16*)p.k1 + b * p.sk1[0] + kh * p.sk1[2];
     const __bf16* V = (const __bf16*)p.v + b * p.sv[0] + kh * p.sv[2];
-    bf16x8 q1f[C::NKS], dof[C::NVS];
+    bf16x8 q1f[NS], dof[NVS];
     {
       const __bf16* Q1 = (const __bf16*)p.q1 + b * p.sq1[0] + (int64_t)qc * p.sq1[1] + h * p.sq1[2];
       const __bf16* DO = (const __bf16*)p.dop + (((int64_t)b * p.N + qc) * p.Hs + h) * C::DV;
 #pragma unroll
-      for (int s = 0; s < C::NKS; ++s) q1f[s] = *(const bf16x8*)(Q1 + 16 * s + 8 * hh);
+      for (int s = 0; s < NS; ++s) q1f[s] = *(const bf16x8*)(Q1 + 32 * s + 8 * jg);
 #pragma unroll
-      for (int s = 0; s < C::NVS; ++s) dof[s] = *(const bf16x8*)(DO + 16 * s + 8 * hh);
+      for (int s = 0; s < NVS; ++s) dof[s] = *(const bf16x8*)(DO + 32 * s + 8 * jg);
     }
     const float4 rs = *(const float4*)(p.rowstat + 4 * (((int64_t)b * p.Hs + h) * p.N + qc));
-    f32x16 dq1[C::NDT];
+    f32x4v dq1[NDT];
 #pragma unroll
-    for (int ct = 0; ct < C::NDT; ++ct) dq1[ct] = f32x16{};
+    for (int ct = 0; ct < NDT; ++ct) dq1[ct] = f32x4v{};
 
-    u32x4 r1[C::KL], r2[C::KL], rv[C::VL];
-    tile_load<C::KL, C::KCH>(r1, K1, p.sk1[1], 0, p.N - 1);
-    tile_load<C::KL, C::KCH>(r2, K2, p.sk2[1], 0, p.N - 1);
-    tile_load<C::VL, C::VCH>(rv, V, p.sv[1], 0, p.N - 1);
-    tile_store<C::KL, C::KCH>(lds, r1);
-    tile_store<C::KL, C::KCH>(lds + C::KT, r2);
-    tile_store<C::VL, C::VCH>(lds + 2 * C::KT, rv);
+    u32x4 r1[KL], r2[KL], rv[VL];
+    tile_load_n<kDqThreads, C::KCH>(r1, K1, p.sk1[1], 0, p.N - 1);
+    tile_load_n<kDqThreads, C::KCH>(r2, K2, p.sk2[1], 0, p.N - 1);
+    tile_load_n<kDqThreads, C::VCH>(rv, V, p.sv[1], 0, p.N - 1);
+    tile_store_n<kDqThreads, C::KCH>(lds, r1);
+    tile_store_n<kDqThreads, C::KCH>(lds + C::KT, r2);
+    tile_store_n<kDqThreads, C::VCH>(lds + 2 * C::KT, rv);
     __syncthreads();
     for (int tile = 0; tile < ntile; ++tile) {
       if (tile + 1 < ntile) {
         const int r0 = (tile + 1) * kTR;
-        tile_load<C::KL, C::KCH>(r1, K1, p.sk1[1], r0, p.N - 1);
-        tile_load<C::KL, C::KCH>(r2, K2, p.sk2[1], r0, p.N - 1);
-        tile_load<C::VL, C::VCH>(rv, V, p.sv[1], r0, p.N - 1);
+        tile_load_n<kDqThreads, C::KCH>(r1, K1, p.sk1[1], r0, p.N - 1);
+        tile_load_n<kDqThreads, C::KCH>(r2, K2, p.sk2[1], r0, p.N - 1);
+        tile_load_n<kDqThreads, C::VCH>(rv, V, p.sv[1], r0, p.N - 1);
       }
       const unsigned char* tk1 = lds + (tile & 1) * STAGE;
       const unsigned char* tk2 = tk1 + C::KT;
       const unsigned char* tv = tk1 + 2 * C::KT;
-      // one 32-key block; MASK only where some key of the block is hidden from some
-      // query of the wavefront (the causal diagonal, keys past N)
+      // one 32-key block (two 16-key accumulator tiles); MASK only where some key of
+      // the block is hidden from some query of the wavefront
       auto block = [&](auto mask, int jb) {
         constexpr bool MASK = decltype(mask)::value;
         const int key0 = tile * kTR + jb * 32;
-        f32x16 s1 = {}, s2 = {}, dp = {};
+        f32x4v s1[2], s2[2], dp[2];
 #pragma unroll
-        for (int s = 0; s < C::NKS; ++s) {
-          s1 = mfma(rd_rows(tk1, jb * 32, s, C::KCH, l32, hh), q1f[s], s1);
-          s2 = mfma(rd_rows(tk2, jb * 32, s, C::KCH, l32, hh), q2f[s], s2);
-        }
+        for (int t = 0; t < 2; ++t) {
+          s1[t] = s2[t] = dp[t] = f32x4v{};
 #pragma unroll
-        for (int s = 0; s < C::NVS; ++s) dp = mfma(rd_rows(tv, jb * 32, s, C::VCH, l32, hh), dof[s], dp);
-        float d1[16], d2[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.sm_scale_log2, -rs.x));
-          float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[r], p.sm_scale_log2, -rs.y));  // |lambda| P2
-          if (MASK) {
-            const int key = key0 + 4 * hh + 8 * (r / 4) + (r & 3);
-            p1 = key <= kvis ? p1 : 0.f;
-            p2 = key <= kvis ? p2 : 0.f;
+          for (int s = 0; s < NS; ++s) {
+            s1[t] = mfma16(rd_rows16(tk1, jb * 32 + 16 * t, s, C::KCH, lane), q1f[s], s1[t]);
+            s2[t] = mfma16(rd_rows16(tk2, jb * 32 + 16 * t, s, C::KCH, lane), q2f[s], s2[t]);
           }
-          d1[r] = p1 * (dp[r] - rs.z);
-          d2[r] = p2 * __builtin_fmaf(sgn, dp[r], -rs.w);
+#pragma unroll
+          for (int s = 0; s < NVS; ++s) dp[t] = mfma16(rd_rows16(tv, jb * 32 + 16 * t, s, C::VCH, lane), dof[s], dp[t]);
         }
-        bf16x8 b1[2], b2[2];
-        to_b(d1, b1[0], b1[1]);
-        to_b(d2, b2[0], b2[1]);
+        // k order of the dS^T operand: slots 0-3 = tile 0 rows 4 (l/16) + r, slots 4-7 = tile 1
+        bf16x8 b1, b2;
 #pragma unroll
-        for (int ct = 0; ct < C::NDT; ++ct)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            dq1[ct] = mfma(rd_tr(tk1, jb * 32, ks, ct, C::KCH, lane), b1[ks], dq1[ct]);
-            dq2[ct] = mfma(rd_tr(tk2, jb * 32, ks, ct, C::KCH, lane), b2[ks], dq2[ct]);
+          for (int r = 0; r < 4; ++r) {
+            float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[t][r], p.sm_scale_log2, -rs.x));
+            float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[t][r], p.sm_scale_log2, -rs.y));  // |lambda| P2
+            if (MASK) {
+              const int key = key0 + 16 * t + 4 * jg + r;
+              p1 = key <= kvis ? p1 : 0.f;
+              p2 = key <= kvis ? p2 : 0.f;
+            }
+            b1[4 * t + r] = (__bf16)(p1 * (dp[t][r] - rs.z));
+            b2[4 * t + r] = (__bf16)(p2 * __builtin_fmaf(sgn, dp[t][r], -rs.w));
           }
+#pragma unroll
+        for (int ct = 0; ct < NDT; ++ct) {
+          dq1[ct] = mfma16(rd_tr16(tk1, jb * 32, ct, C::KCH, lane), b1, dq1[ct]);
+          dq2[ct] = mfma16(rd_tr16(tk2, jb * 32, ct, C::KCH, lane), b2, dq2[ct]);
+        }
       };
-      const int kfree = p.causal ? min(qw, p.N - 1) : p.N - 1;  // keys every query of the wavefront sees
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb) {
         const int key0 = tile * kTR + jb * 32;
@@ -266,17 +325,29 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
       }
       if (tile + 1 < ntile) {
         unsigned char* nt = lds + ((tile + 1) & 1) * STAGE;
-        tile_store<C::KL, C::KCH>(nt, r1);
-        tile_store<C::KL, C::KCH>(nt + C::KT, r2);
-        tile_store<C::VL, C::VCH>(nt + 2 * C::KT, rv);
+        tile_store_n<kDqThreads, C::KCH>(nt, r1);
+        tile_store_n<kDqThreads, C::KCH>(nt + C::KT, r2);
+        tile_store_n<kDqThreads, C::VCH>(nt + 2 * C::KT, rv);
       }
       __syncthreads();
     }
-    if (q < p.N)
-      store_rows<C::NDT>((__bf16*)p.gq1 + b * p.sgq1[0] + (int64_t)q * p.sgq1[1] + h * p.sgq1[2], dq1, p.sm_scale, hh);
+    if (q < p.N) {
+      __bf16* row = (__bf16*)p.gq1 + b * p.sgq1[0] + (int64_t)q * p.sgq1[1] + h * p.sgq1[2];
+#pragma unroll
+      for (int ct = 0; ct < NDT; ++ct) {
+        const f32x4 y = dq1[ct] * p.sm_scale;
+        *(bf16x4*)(row + 16 * ct + 4 * jg) = __builtin_convertvector(y, bf16x4);
+      }
+    }
   }
-  if (q < p.N)
-    store_rows<C::NDT>((__bf16*)p.gq2 + b * p.sgq2[0] + (int64_t)q * p.sgq2[1] + n * p.sgq2[2], dq2, p.sm_scale, hh);
+  if (q < p.N) {
+    __bf16* row = (__bf16*)p.gq2 + b * p.sgq2[0] + (int64_t)q * p.sgq2[1] + n * p.sgq2[2];
+#pragma unroll
+    for (int ct = 0; ct < NDT; ++ct) {
+      const f32x4 y = dq2[ct] * p.sm_scale;
+      *(bf16x4*)(row + 16 * ct + 4 * jg) = __builtin_convertvector(y, bf16x4);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -439,10 +510,10 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
   const int64_t grid = (int64_t)p.B * p.Hn * nblk;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   if (p.d == 64) {
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)grid), dim3(kDqThreads), 0, s, p);
     hipLaunchKernelGGL(bwd_dkv_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   } else {
-    hipLaunchKernelGGL(bwd_dq_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(bwd_dq_kernel<32>, dim3((unsigned)grid), dim3(kDqThreads), 0, s, p);
     hipLaunchKernelGGL(bwd_dkv_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   }
   return hipGetLastError();
