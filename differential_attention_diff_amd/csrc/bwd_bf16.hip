@@ -351,15 +351,18 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dKV pass: workgroup = (b, noise group n, 128 keys)
+// dKV pass: workgroup = (b, noise group n, 128 keys), 8 wavefronts of 16 keys on
+// v_mfma_f32_16x16x32_bf16 (two wavefronts per SIMD)
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kDqThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   using C = BC<D>;
   constexpr int RS = kTR * 16;  // row statistics of a tile (float4 per query)
   constexpr int STAGE = 2 * C::KT + C::VT + RS;
+  constexpr int NS = D / 32, NVS = C::DV / 32, NDT = D / 16, NVT = C::DV / 16;
+  constexpr int KL = TileLoads<kDqThreads, C::KCH>::n, VL = TileLoads<kDqThreads, C::VCH>::n;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, jg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int nk = (p.N + kRB - 1) / kRB;
@@ -367,139 +370,142 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const int kb = p.causal ? logical % nk : nk - 1 - logical % nk;  // causal: most queries first
   const int t0 = logical / nk;
   const int n = t0 % p.Hn, b = t0 / p.Hn;
-  const int k0 = kb * kRB, kw = k0 + wave * kRW, key = kw + l32, kc = min(key, p.N - 1);
+  const int k0 = kb * kRB, kw = k0 + wave * kQW16, key = kw + l16, kc = min(key, p.N - 1);
   const float sgn = lambda_of(p.lam_dev, p.lam) > 0.f ? -1.f : 1.f;  // -lambda = sgn |lambda|
   const int qt0 = p.causal ? k0 / kTR : 0;
   const int ntile = (p.N + kTR - 1) / kTR;
 
   const __bf16* Q2 = (const __bf16*)p.q2 + b * p.sq2[0] + n * p.sq2[2];
-  bf16x8 kf2[C::NKS];
+  bf16x8 kf2[NS];
   {
     const __bf16* K2 = (const __bf16*)p.k2 + b * p.sk2[0] + (int64_t)kc * p.sk2[1] + n * p.sk2[2];
 #pragma unroll
-    for (int s = 0; s < C::NKS; ++s) kf2[s] = *(const bf16x8*)(K2 + 16 * s + 8 * hh);
+    for (int s = 0; s < NS; ++s) kf2[s] = *(const bf16x8*)(K2 + 32 * s + 8 * jg);
   }
-  f32x16 dk2[C::NDT], dk1[C::NDT], dv[C::NVT];
+  f32x4v dk2[NDT], dk1[NDT], dv[NVT];
 #pragma unroll
-  for (int ct = 0; ct < C::NDT; ++ct) dk2[ct] = dk1[ct] = f32x16{};
+  for (int ct = 0; ct < NDT; ++ct) dk2[ct] = dk1[ct] = f32x4v{};
 #pragma unroll
-  for (int vt = 0; vt < C::NVT; ++vt) dv[vt] = f32x16{};
-  bf16x8 kf1[C::NKS], vf[C::NVS];
+  for (int vt = 0; vt < NVT; ++vt) dv[vt] = f32x4v{};
+  bf16x8 kf1[NS], vf[NVS];
   int cur = -1;  // key/value head of the accumulating run
+
+  // accumulator tiles as gradient rows: lane l of tile ct holds column 16 ct + 4 (l/16) + r
+  // of key row `key`
+  auto store16 = [&](__bf16* row, const f32x4v* acc, int nt, float scale) {
+    for (int ct = 0; ct < nt; ++ct) {
+      const f32x4 y = acc[ct] * scale;
+      *(bf16x4*)(row + 16 * ct + 4 * jg) = __builtin_convertvector(y, bf16x4);
+    }
+  };
 
   for (int mem = 0; mem < p.g; ++mem) {
     const int h = __builtin_amdgcn_readfirstlane(p.members[n * p.g + mem]);
     const int kh = __builtin_amdgcn_readfirstlane(p.kv[h]);
     if (kh != cur) {
       if (cur >= 0 && key < p.N) {
-        store_rows<C::NDT>((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)key * p.sgk1[1] + cur * p.sgk1[2], dk1,
-                           p.sm_scale, hh);
-        store_rows<C::NVT>((__bf16*)p.gv + b * p.sgv[0] + (int64_t)key * p.sgv[1] + cur * p.sgv[2], dv, 1.0f, hh);
+        store16((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)key * p.sgk1[1] + cur * p.sgk1[2], dk1, NDT, p.sm_scale);
+        store16((__bf16*)p.gv + b * p.sgv[0] + (int64_t)key * p.sgv[1] + cur * p.sgv[2], dv, NVT, 1.0f);
       }
 #pragma unroll
-      for (int ct = 0; ct < C::NDT; ++ct) dk1[ct] = f32x16{};
+      for (int ct = 0; ct < NDT; ++ct) dk1[ct] = f32x4v{};
 #pragma unroll
-      for (int vt = 0; vt < C::NVT; ++vt) dv[vt] = f32x16{};
+      for (int vt = 0; vt < NVT; ++vt) dv[vt] = f32x4v{};
       cur = kh;
       const __bf16* K1 = (const __bf16*)p.k1 + b * p.sk1[0] + (int64_t)kc * p.sk1[1] + kh * p.sk1[2];
       const __bf16* V = (const __bf16*)p.v + b * p.sv[0] + (int64_t)kc * p.sv[1] + kh * p.sv[2];
 #pragma unroll
-      for (int s = 0; s < C::NKS; ++s) kf1[s] = *(const bf16x8*)(K1 + 16 * s + 8 * hh);
+      for (int s = 0; s < NS; ++s) kf1[s] = *(const bf16x8*)(K1 + 32 * s + 8 * jg);
 #pragma unroll
-      for (int s = 0; s < C::NVS; ++s) vf[s] = *(const bf16x8*)(V + 16 * s + 8 * hh);
+      for (int s = 0; s < NVS; ++s) vf[s] = *(const bf16x8*)(V + 32 * s + 8 * jg);
     }
     const __bf16* Q1 = (const __bf16*)p.q1 + b * p.sq1[0] + h * p.sq1[2];
     const __bf16* DO = (const __bf16*)p.dop + ((int64_t)b * p.N * p.Hs + h) * C::DV;  // row i at + i Hs dv
     const float* RSB = p.rowstat + 4 * ((int64_t)b * p.Hs + h) * p.N;
     const int64_t dors = (int64_t)p.Hs * C::DV;
 
-    u32x4 r1[C::KL], r2[C::KL], rv[C::VL], rr;
+    u32x4 r1[KL], r2[KL], rv[VL], rr;
     auto load_all = [&](int qt) {
       const int r0 = qt * kTR;
-      tile_load<C::KL, C::KCH>(r1, Q1, p.sq1[1], r0, p.N - 1);
-      tile_load<C::KL, C::KCH>(r2, Q2, p.sq2[1], r0, p.N - 1);
-      tile_load<C::VL, C::VCH>(rv, DO, dors, r0, p.N - 1);
+      tile_load_n<kDqThreads, C::KCH>(r1, Q1, p.sq1[1], r0, p.N - 1);
+      tile_load_n<kDqThreads, C::KCH>(r2, Q2, p.sq2[1], r0, p.N - 1);
+      tile_load_n<kDqThreads, C::VCH>(rv, DO, dors, r0, p.N - 1);
       if (tid < kTR) rr = *(const u32x4*)(RSB + 4 * (int64_t)min(r0 + tid, p.N - 1));
     };
     auto store_all = [&](unsigned char* t) {
-      tile_store<C::KL, C::KCH>(t, r1);
-      tile_store<C::KL, C::KCH>(t + C::KT, r2);
-      tile_store<C::VL, C::VCH>(t + 2 * C::KT, rv);
+      tile_store_n<kDqThreads, C::KCH>(t, r1);
+      tile_store_n<kDqThreads, C::KCH>(t + C::KT, r2);
+      tile_store_n<kDqThreads, C::VCH>(t + 2 * C::KT, rv);
       if (tid < kTR) *(u32x4*)(t + 2 * C::KT + C::VT + 16 * tid) = rr;
     };
     load_all(qt0);
     store_all(lds);
     __syncthreads();
-    // one query tile (masked throughout: an unmasked copy of the sub-block code does not
-    // fit this wavefront's registers next to the masked one)
-    auto tile_step = [&](int qt, auto tmask) {
+    for (int qt = qt0; qt < ntile; ++qt) {
       if (qt + 1 < ntile) load_all(qt + 1);
       const unsigned char* tq1 = lds + ((qt - qt0) & 1) * STAGE;
       const unsigned char* tq2 = tq1 + C::KT;
       const unsigned char* tdo = tq1 + 2 * C::KT;
       const float* trs = (const float*)(tq1 + 2 * C::KT + C::VT);
-      // one 32-query sub-block; MASK only where some query of it does not see some key of
-      // the wavefront (the causal diagonal, queries past N)
+      // one 32-query sub-block (two 16-query accumulator tiles); MASK only where some
+      // query of it does not see some key of the wavefront
       auto block = [&](auto mask, int sb) {
         constexpr bool MASK = decltype(mask)::value;
         const int qs0 = qt * kTR + sb * 32;
-        f32x16 s1 = {}, s2 = {}, dp = {};
+        f32x4v s1[2], s2[2], dp[2];
 #pragma unroll
-        for (int s = 0; s < C::NKS; ++s) {
-          s1 = mfma(rd_rows(tq1, sb * 32, s, C::KCH, l32, hh), kf1[s], s1);
-          s2 = mfma(rd_rows(tq2, sb * 32, s, C::KCH, l32, hh), kf2[s], s2);
-        }
+        for (int t = 0; t < 2; ++t) {
+          s1[t] = s2[t] = dp[t] = f32x4v{};
 #pragma unroll
-        for (int s = 0; s < C::NVS; ++s) dp = mfma(rd_rows(tdo, sb * 32, s, C::VCH, l32, hh), vf[s], dp);
-        float pc[16], d1[16], d2[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = sb * 32 + 4 * hh + 8 * (r / 4) + (r & 3);  // query row in the tile
-          const float4 st = *(const float4*)(trs + 4 * qi);
-          float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], p.sm_scale_log2, -st.x));
-          float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[r], p.sm_scale_log2, -st.y));  // |lambda| P2
-          if (MASK) {
-            const int qg = qs0 + qi - sb * 32;
-            const bool vis = qg < p.N && (!p.causal || qg >= key);
-            p1 = vis ? p1 : 0.f;
-            p2 = vis ? p2 : 0.f;
+          for (int s = 0; s < NS; ++s) {
+            s1[t] = mfma16(rd_rows16(tq1, sb * 32 + 16 * t, s, C::KCH, lane), kf1[s], s1[t]);
+            s2[t] = mfma16(rd_rows16(tq2, sb * 32 + 16 * t, s, C::KCH, lane), kf2[s], s2[t]);
           }
-          pc[r] = __builtin_fmaf(sgn, p2, p1);
-          d1[r] = p1 * (dp[r] - st.z);
-          d2[r] = p2 * __builtin_fmaf(sgn, dp[r], -st.w);
+#pragma unroll
+          for (int s = 0; s < NVS; ++s) dp[t] = mfma16(rd_rows16(tdo, sb * 32 + 16 * t, s, C::VCH, lane), vf[s], dp[t]);
         }
-        bf16x8 bc[2], b1[2], b2[2];
-        to_b(pc, bc[0], bc[1]);
-        to_b(d1, b1[0], b1[1]);
-        to_b(d2, b2[0], b2[1]);
+        // k order of the B operands: slots 0-3 = tile 0 rows 4 (l/16) + r, slots 4-7 = tile 1
+        bf16x8 bc, b1, b2;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int vt = 0; vt < C::NVT; ++vt) dv[vt] = mfma(rd_tr(tdo, sb * 32, ks, vt, C::VCH, lane), bc[ks], dv[vt]);
-#pragma unroll
-          for (int ct = 0; ct < C::NDT; ++ct) {
-            dk1[ct] = mfma(rd_tr(tq1, sb * 32, ks, ct, C::KCH, lane), b1[ks], dk1[ct]);
-            dk2[ct] = mfma(rd_tr(tq2, sb * 32, ks, ct, C::KCH, lane), b2[ks], dk2[ct]);
+          for (int r = 0; r < 4; ++r) {
+            const int qi = sb * 32 + 16 * t + 4 * jg + r;  // query row in the tile
+            const float4 st = *(const float4*)(trs + 4 * qi);
+            float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[t][r], p.sm_scale_log2, -st.x));
+            float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[t][r], p.sm_scale_log2, -st.y));  // |lambda| P2
+            if (MASK) {
+              const int qg = qs0 + 16 * t + 4 * jg + r;
+              const bool vis = qg < p.N && (!p.causal || qg >= key);
+              p1 = vis ? p1 : 0.f;
+              p2 = vis ? p2 : 0.f;
+            }
+            bc[4 * t + r] = (__bf16)__builtin_fmaf(sgn, p2, p1);
+            b1[4 * t + r] = (__bf16)(p1 * (dp[t][r] - st.z));
+            b2[4 * t + r] = (__bf16)(p2 * __builtin_fmaf(sgn, dp[t][r], -st.w));
           }
+#pragma unroll
+        for (int vt = 0; vt < NVT; ++vt) dv[vt] = mfma16(rd_tr16(tdo, sb * 32, vt, C::VCH, lane), bc, dv[vt]);
+#pragma unroll
+        for (int ct = 0; ct < NDT; ++ct) {
+          dk1[ct] = mfma16(rd_tr16(tq1, sb * 32, ct, C::KCH, lane), b1, dk1[ct]);
+          dk2[ct] = mfma16(rd_tr16(tq2, sb * 32, ct, C::KCH, lane), b2, dk2[ct]);
         }
       };
-#pragma unroll
+#pragma unroll 1
       for (int sb = 0; sb < 2; ++sb) {
         const int qs0 = qt * kTR + sb * 32;
         if (qs0 >= p.N || (p.causal && qs0 + 31 < kw)) continue;  // wavefront-uniform: nothing visible
-        block(tmask, sb);
+        block(std::true_type{}, sb);
       }
       if (qt + 1 < ntile) store_all(lds + ((qt + 1 - qt0) & 1) * STAGE);
       __syncthreads();
-    };
-    for (int qt = qt0; qt < ntile; ++qt) tile_step(qt, std::true_type{});
+    }
   }
   if (key < p.N) {
-    store_rows<C::NDT>((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)key * p.sgk1[1] + cur * p.sgk1[2], dk1, p.sm_scale,
-                       hh);
-    store_rows<C::NVT>((__bf16*)p.gv + b * p.sgv[0] + (int64_t)key * p.sgv[1] + cur * p.sgv[2], dv, 1.0f, hh);
-    store_rows<C::NDT>((__bf16*)p.gk2 + b * p.sgk2[0] + (int64_t)key * p.sgk2[1] + n * p.sgk2[2], dk2, p.sm_scale,
-                       hh);
+    store16((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)key * p.sgk1[1] + cur * p.sgk1[2], dk1, NDT, p.sm_scale);
+    store16((__bf16*)p.gv + b * p.sgv[0] + (int64_t)key * p.sgv[1] + cur * p.sgv[2], dv, NVT, 1.0f);
+    store16((__bf16*)p.gk2 + b * p.sgk2[0] + (int64_t)key * p.sgk2[1] + n * p.sgk2[2], dk2, NDT, p.sm_scale);
   }
 }
 
@@ -511,10 +517,10 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   if (p.d == 64) {
     hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)grid), dim3(kDqThreads), 0, s, p);
-    hipLaunchKernelGGL(bwd_dkv_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(bwd_dkv_kernel<64>, dim3((unsigned)grid), dim3(kDqThreads), 0, s, p);
   } else {
     hipLaunchKernelGGL(bwd_dq_kernel<32>, dim3((unsigned)grid), dim3(kDqThreads), 0, s, p);
-    hipLaunchKernelGGL(bwd_dkv_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(bwd_dkv_kernel<32>, dim3((unsigned)grid), dim3(kDqThreads), 0, s, p);
   }
   return hipGetLastError();
 }
