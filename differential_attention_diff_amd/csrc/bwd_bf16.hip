@@ -17,16 +17,18 @@
 //   dQ2 = dS2 K2 / sqrt(d), dK2 = dS2^T Q2 / sqrt(d)
 // One dp = do V^T product serves both maps (both use the head's V).
 //
-// Both passes: a workgroup of 4 wavefronts owns 128 rows (32 per wavefront)
-// of one (batch, noise group) and walks the group's signal heads in turn, so
-// the noise head's sums (dQ2, dK2) stay in registers and every gradient row is
+// Both passes: a workgroup of 8 wavefronts owns 128 rows (16 per wavefront) of
+// one (batch, noise group) and walks the group's signal heads in turn, so the
+// noise head's sums (dQ2, dK2) stay in registers and every gradient row is
 // written once; the other operand side is staged through LDS in 64-row tiles,
 // double-buffered (the next tile's global loads are in flight during the
-// current tile's products; one barrier per tile).  v_mfma_f32_32x32x16_bf16
-// throughout; operands that must be transposed are read with
-// ds_read_b64_tr_b16.  A product's B operand taken from another product's
-// accumulator uses that accumulator's row order as its k order, and the A
-// operand read from LDS follows the same order.
+// current tile's products; one barrier per tile).  v_mfma_f32_16x16x32_bf16
+// throughout (lane l: A row l%16, B column l%16, k 8 (l/16) .. +7; accumulator
+// rows 4 (l/16) + r of column l%16): a 16-row wavefront needs about half the
+// registers of a 32-row one, so two fit per SIMD.  Operands that must be
+// transposed are read with ds_read_b64_tr_b16.  A product's B operand taken
+// from other products' accumulators uses their row order as its k order, and
+// the A operand read from LDS follows the same order.
 //   dQ pass: S^T = K Q^T (lane = query), so the weights of a lane's query are
 //     in its own registers and dS^T is the B operand of dQ^T = K^T dS^T.
 //   dKV pass: S = Q K^T (lane = key), so dS and P1 - lambda P2 are the B
@@ -46,27 +48,25 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-constexpr int kWaves = 4;
+constexpr int kRB = 128;              // rows per workgroup
+constexpr int kRW = 16;               // rows per wavefront
+constexpr int kWaves = kRB / kRW;     // 8
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRW = 32;               // rows per wavefront
-constexpr int kRB = kWaves * kRW;     // rows per workgroup
 constexpr int kTR = 64;               // rows per LDS tile
 
 template <int D>
 struct BC {
   static constexpr int DV = 2 * D;
-  static constexpr int NKS = D / 16, NVS = DV / 16;   // 16-wide k steps over d, dv
-  static constexpr int NDT = D / 32, NVT = DV / 32;   // 32-row output tiles over d, dv
+  static constexpr int NS = D / 32, NVS = DV / 32;     // 32-wide k steps over d, dv
+  static constexpr int NDT = D / 16, NVT = DV / 16;    // 16-row output tiles over d, dv
   static constexpr int KCH = 2 * D / 16, VCH = 2 * DV / 16;  // 16-B chunks per row
   static constexpr int KT = kTR * 2 * D, VT = kTR * 2 * DV;  // tile bytes
-  static constexpr int KL = kTR * KCH / kThreads, VL = kTR * VCH / kThreads;  // 16-B loads per thread
-  static_assert(KL >= 1 && VL >= 1, "tile split over threads");
+  // 16-B tile loads per thread (a tile of fewer chunks than threads leaves the last threads idle)
+  static constexpr int KL = (kTR * KCH + kThreads - 1) / kThreads, VL = (kTR * VCH + kThreads - 1) / kThreads;
 };
 
 // LDS byte offset of 16-B chunk c of row r in a tile with `ch` chunks per row.
@@ -78,112 +78,29 @@ __device__ __forceinline__ int swz(int r, int c, int ch) {
   return r * ch * 16 + ((c ^ f) << 4);
 }
 
-// Rows [r0, r0 + 64) of a tensor (element row stride rs), rows past `last`
-// re-read row `last`; thread t handles chunks t, t + 256, ...
-template <int L, int CH>
+// Rows [r0, r0 + 64) of a tensor (element row stride rs) into registers, then into
+// an LDS tile; rows past `last` re-read row `last`; thread t handles chunks t,
+// t + kThreads, ...
+template <int CH, int L>
 __device__ __forceinline__ void tile_load(u32x4 (&reg)[L], const __bf16* base, int64_t rs, int r0, int last) {
 #pragma unroll
   for (int k = 0; k < L; ++k) {
     const int idx = (int)threadIdx.x + kThreads * k, r = idx / CH, c = idx % CH;
-    reg[k] = *(const u32x4*)(base + (int64_t)min(r0 + r, last) * rs + c * 8);
+    if (kTR * CH % kThreads == 0 || idx < kTR * CH)
+      reg[k] = *(const u32x4*)(base + (int64_t)min(r0 + r, last) * rs + c * 8);
   }
 }
-template <int L, int CH>
+template <int CH, int L>
 __device__ __forceinline__ void tile_store(unsigned char* t, const u32x4 (&reg)[L]) {
 #pragma unroll
   for (int k = 0; k < L; ++k) {
     const int idx = (int)threadIdx.x + kThreads * k, r = idx / CH, c = idx % CH;
-    *(u32x4*)(t + swz(r, c, CH)) = reg[k];
+    if (kTR * CH % kThreads == 0 || idx < kTR * CH) *(u32x4*)(t + swz(r, c, CH)) = reg[k];
   }
 }
 
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Row-wise A operand: lane (r, half) holds row rb + r, elements 16 s + 8 half .. + 7.
-__device__ __forceinline__ bf16x8 rd_rows(const unsigned char* t, int rb, int s, int ch, int l32, int hh) {
-  return *(const bf16x8*)(t + swz(rb + l32, 2 * s + hh, ch));
-}
-
-// Transposed A operand of a 32 x 16 step: rows rb + 16 ks + {4 half + 0..3,
-// 8 + 4 half + 0..3} (the accumulator row order), column block ct (32 columns).
-// Lane j of a 16-lane group reads row 4 half + j / 4 at columns 16 g + 4 (j % 4);
-// the transposing read hands lane i the 4 rows of column 16 g + i.
-__device__ __forceinline__ bf16x8 rd_tr(const unsigned char* t, int rb, int ks, int ct, int ch, int lane) {
-  const int hh = lane >> 5, row = rb + 16 * ks + 4 * hh + (lane & 15) / 4;
-  const int col = ct * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int cc = col >> 3, within = (col & 7) * 2;
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + swz(row, cc, ch) + within));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + swz(row + 8, cc, ch) + within));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// accumulator registers 0-7 / 8-15 as bf16 B operands (k = accumulator rows)
-__device__ __forceinline__ void to_b(const float (&x)[16], bf16x8& b0, bf16x8& b1) {
-  const f32x8 lo = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
-  const f32x8 hi = {x[8], x[9], x[10], x[11], x[12], x[13], x[14], x[15]};
-  b0 = __builtin_convertvector(lo, bf16x8);
-  b1 = __builtin_convertvector(hi, bf16x8);
-}
-
-// store a 32-column accumulator tile (rows = columns of the gradient row `lane`)
-// as bf16: register 4 g4 + e is column 32 ct + 8 g4 + 4 half + e
-template <int NT>
-__device__ __forceinline__ void store_rows(__bf16* row, const f32x16 (&acc)[NT], float scale, int hh) {
-#pragma unroll
-  for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x4 y = {acc[ct][4 * g4] * scale, acc[ct][4 * g4 + 1] * scale, acc[ct][4 * g4 + 2] * scale,
-                       acc[ct][4 * g4 + 3] * scale};
-      *(bf16x4*)(row + ct * 32 + 8 * g4 + 4 * hh) = __builtin_convertvector(y, bf16x4);
-    }
-}
-
-__device__ __forceinline__ int xcd_logical(int bid, int total) {
-  const int xcd = bid & 7, q8 = total >> 3, r8 = total & 7;
-  return xcd * q8 + min(xcd, r8) + (bid >> 3);
-}
-
-// ---------------------------------------------------------------------------
-// dQ pass: workgroup = (b, noise group n, 128 queries), 8 wavefronts of 16 queries
-// on v_mfma_f32_16x16x32_bf16 (lane l: A row l%16, B column l%16, k 8 (l/16) .. +7;
-// accumulator rows 4 (l/16) + r of column l%16), so a wavefront needs about half
-// the registers of a 32-query one and two fit per SIMD.
-// ---------------------------------------------------------------------------
-typedef float f32x4v __attribute__((ext_vector_type(4)));
-constexpr int kQW16 = 16;                 // queries per dQ wavefront
-constexpr int kDqWaves = kRB / kQW16;     // 8
-constexpr int kDqThreads = 64 * kDqWaves;
-
-__device__ __forceinline__ f32x4v mfma16(bf16x8 a, bf16x8 b, f32x4v c) {
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Rows [r0, r0 + 64) of a tensor into an LDS tile by NT threads (see tile_load); a
-// tile of fewer 16-byte chunks than threads leaves the last threads idle.
-template <int NT, int CH>
-struct TileLoads {
-  static constexpr int n = (kTR * CH + NT - 1) / NT;
-};
-template <int NT, int CH, int L>
-__device__ __forceinline__ void tile_load_n(u32x4 (&reg)[L], const __bf16* base, int64_t rs, int r0, int last) {
-  static_assert(L == TileLoads<NT, CH>::n, "register count");
-#pragma unroll
-  for (int k = 0; k < L; ++k) {
-    const int idx = (int)threadIdx.x + NT * k, r = idx / CH, c = idx % CH;
-    if (kTR * CH % NT == 0 || idx < kTR * CH) reg[k] = *(const u32x4*)(base + (int64_t)min(r0 + r, last) * rs + c * 8);
-  }
-}
-template <int NT, int CH, int L>
-__device__ __forceinline__ void tile_store_n(unsigned char* t, const u32x4 (&reg)[L]) {
-  static_assert(L == TileLoads<NT, CH>::n, "register count");
-#pragma unroll
-  for (int k = 0; k < L; ++k) {
-    const int idx = (int)threadIdx.x + NT * k, r = idx / CH, c = idx % CH;
-    if (kTR * CH % NT == 0 || idx < kTR * CH) *(u32x4*)(t + swz(r, c, CH)) = reg[k];
-  }
 }
 
 // A operand of a 16 x 32 step read row-wise: lane l holds row rb + l%16, elements
@@ -204,12 +121,31 @@ __device__ __forceinline__ bf16x8 rd_tr16(const unsigned char* t, int rb, int ct
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Accumulator tiles as a gradient row: lane l of tile ct holds columns
+// 16 ct + 4 (l/16) + 0..3 of the row; stored as bf16 after `scale`.
+template <int NT>
+__device__ __forceinline__ void store_row16(__bf16* row, const f32x4 (&acc)[NT], float scale, int jg) {
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    const f32x4 y = acc[ct] * scale;
+    *(bf16x4*)(row + 16 * ct + 4 * jg) = __builtin_convertvector(y, bf16x4);
+  }
+}
+
+__device__ __forceinline__ int xcd_logical(int bid, int total) {
+  const int xcd = bid & 7, q8 = total >> 3, r8 = total & 7;
+  return xcd * q8 + min(xcd, r8) + (bid >> 3);
+}
+
+// ---------------------------------------------------------------------------
+// dQ pass: workgroup = (b, noise group n, 128 queries)
+// ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   using C = BC<D>;
   constexpr int STAGE = 2 * C::KT + C::VT;
-  constexpr int NS = D / 32, NVS = C::DV / 32, NDT = D / 16;   // k steps over d, dv; 16-row d tiles
-  constexpr int KL = TileLoads<kDqThreads, C::KCH>::n, VL = TileLoads<kDqThreads, C::VCH>::n;
+  constexpr int NS = C::NS, NVS = C::NVS, NDT = C::NDT;
+  constexpr int KL = C::KL, VL = C::VL;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
   const int lane = threadIdx.x & 63, l16 = lane & 15, jg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -219,11 +155,11 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const int qb = nq - 1 - logical % nq;  // longest causal range first
   const int t0 = logical / nq;
   const int n = t0 % p.Hn, b = t0 / p.Hn;
-  const int q0 = qb * kRB, qw = q0 + wave * kQW16, q = qw + l16, qc = min(q, p.N - 1);
+  const int q0 = qb * kRB, qw = q0 + wave * kRW, q = qw + l16, qc = min(q, p.N - 1);
   const float sgn = lambda_of(p.lam_dev, p.lam) > 0.f ? -1.f : 1.f;  // -lambda = sgn |lambda|
   const int kend = p.causal ? min(q0 + kRB, p.N) : p.N;
   const int ntile = (kend + kTR - 1) / kTR;
-  const int klast = p.causal ? min(qw + kQW16 - 1, p.N - 1) : p.N - 1;  // last key this wavefront sees
+  const int klast = p.causal ? min(qw + kRW - 1, p.N - 1) : p.N - 1;  // last key this wavefront sees
   const int kvis = p.causal ? min(q, p.N - 1) : p.N - 1;                  // last key this lane sees
   const int kfree = p.causal ? min(qw, p.N - 1) : p.N - 1;                // keys every query sees
 
@@ -234,9 +170,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) q2f[s] = *(const bf16x8*)(Q2 + 32 * s + 8 * jg);
   }
-  f32x4v dq2[NDT];
+  f32x4 dq2[NDT];
 #pragma unroll
-  for (int ct = 0; ct < NDT; ++ct) dq2[ct] = f32x4v{};
+  for (int ct = 0; ct < NDT; ++ct) dq2[ct] = f32x4{};
 
   for (int mem = 0; mem < p.g; ++mem) {
     const int h = __builtin_amdgcn_readfirstlane(p.members[n * p.g + mem]);
@@ -253,24 +189,24 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
       for (int s = 0; s < NVS; ++s) dof[s] = *(const bf16x8*)(DO + 32 * s + 8 * jg);
     }
     const float4 rs = *(const float4*)(p.rowstat + 4 * (((int64_t)b * p.Hs + h) * p.N + qc));
-    f32x4v dq1[NDT];
+    f32x4 dq1[NDT];
 #pragma unroll
-    for (int ct = 0; ct < NDT; ++ct) dq1[ct] = f32x4v{};
+    for (int ct = 0; ct < NDT; ++ct) dq1[ct] = f32x4{};
 
     u32x4 r1[KL], r2[KL], rv[VL];
-    tile_load_n<kDqThreads, C::KCH>(r1, K1, p.sk1[1], 0, p.N - 1);
-    tile_load_n<kDqThreads, C::KCH>(r2, K2, p.sk2[1], 0, p.N - 1);
-    tile_load_n<kDqThreads, C::VCH>(rv, V, p.sv[1], 0, p.N - 1);
-    tile_store_n<kDqThreads, C::KCH>(lds, r1);
-    tile_store_n<kDqThreads, C::KCH>(lds + C::KT, r2);
-    tile_store_n<kDqThreads, C::VCH>(lds + 2 * C::KT, rv);
+    tile_load<C::KCH>(r1, K1, p.sk1[1], 0, p.N - 1);
+    tile_load<C::KCH>(r2, K2, p.sk2[1], 0, p.N - 1);
+    tile_load<C::VCH>(rv, V, p.sv[1], 0, p.N - 1);
+    tile_store<C::KCH>(lds, r1);
+    tile_store<C::KCH>(lds + C::KT, r2);
+    tile_store<C::VCH>(lds + 2 * C::KT, rv);
     __syncthreads();
     for (int tile = 0; tile < ntile; ++tile) {
       if (tile + 1 < ntile) {
         const int r0 = (tile + 1) * kTR;
-        tile_load_n<kDqThreads, C::KCH>(r1, K1, p.sk1[1], r0, p.N - 1);
-        tile_load_n<kDqThreads, C::KCH>(r2, K2, p.sk2[1], r0, p.N - 1);
-        tile_load_n<kDqThreads, C::VCH>(rv, V, p.sv[1], r0, p.N - 1);
+        tile_load<C::KCH>(r1, K1, p.sk1[1], r0, p.N - 1);
+        tile_load<C::KCH>(r2, K2, p.sk2[1], r0, p.N - 1);
+        tile_load<C::VCH>(rv, V, p.sv[1], r0, p.N - 1);
       }
       const unsigned char* tk1 = lds + (tile & 1) * STAGE;
       const unsigned char* tk2 = tk1 + C::KT;
@@ -280,10 +216,10 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
       auto block = [&](auto mask, int jb) {
         constexpr bool MASK = decltype(mask)::value;
         const int key0 = tile * kTR + jb * 32;
-        f32x4v s1[2], s2[2], dp[2];
+        f32x4 s1[2], s2[2], dp[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          s1[t] = s2[t] = dp[t] = f32x4v{};
+          s1[t] = s2[t] = dp[t] = f32x4{};
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
             s1[t] = mfma16(rd_rows16(tk1, jb * 32 + 16 * t, s, C::KCH, lane), q1f[s], s1[t]);
@@ -325,42 +261,29 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(BwdParams p) {
       }
       if (tile + 1 < ntile) {
         unsigned char* nt = lds + ((tile + 1) & 1) * STAGE;
-        tile_store_n<kDqThreads, C::KCH>(nt, r1);
-        tile_store_n<kDqThreads, C::KCH>(nt + C::KT, r2);
-        tile_store_n<kDqThreads, C::VCH>(nt + 2 * C::KT, rv);
+        tile_store<C::KCH>(nt, r1);
+        tile_store<C::KCH>(nt + C::KT, r2);
+        tile_store<C::VCH>(nt + 2 * C::KT, rv);
       }
       __syncthreads();
     }
-    if (q < p.N) {
-      __bf16* row = (__bf16*)p.gq1 + b * p.sgq1[0] + (int64_t)q * p.sgq1[1] + h * p.sgq1[2];
-#pragma unroll
-      for (int ct = 0; ct < NDT; ++ct) {
-        const f32x4 y = dq1[ct] * p.sm_scale;
-        *(bf16x4*)(row + 16 * ct + 4 * jg) = __builtin_convertvector(y, bf16x4);
-      }
-    }
+    if (q < p.N)
+      store_row16((__bf16*)p.gq1 + b * p.sgq1[0] + (int64_t)q * p.sgq1[1] + h * p.sgq1[2], dq1, p.sm_scale, jg);
   }
-  if (q < p.N) {
-    __bf16* row = (__bf16*)p.gq2 + b * p.sgq2[0] + (int64_t)q * p.sgq2[1] + n * p.sgq2[2];
-#pragma unroll
-    for (int ct = 0; ct < NDT; ++ct) {
-      const f32x4 y = dq2[ct] * p.sm_scale;
-      *(bf16x4*)(row + 16 * ct + 4 * jg) = __builtin_convertvector(y, bf16x4);
-    }
-  }
+  if (q < p.N)
+    store_row16((__bf16*)p.gq2 + b * p.sgq2[0] + (int64_t)q * p.sgq2[1] + n * p.sgq2[2], dq2, p.sm_scale, jg);
 }
 
 // ---------------------------------------------------------------------------
-// dKV pass: workgroup = (b, noise group n, 128 keys), 8 wavefronts of 16 keys on
-// v_mfma_f32_16x16x32_bf16 (two wavefronts per SIMD)
+// dKV pass: workgroup = (b, noise group n, 128 keys)
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kDqThreads, 1) void bwd_dkv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   using C = BC<D>;
   constexpr int RS = kTR * 16;  // row statistics of a tile (float4 per query)
   constexpr int STAGE = 2 * C::KT + C::VT + RS;
-  constexpr int NS = D / 32, NVS = C::DV / 32, NDT = D / 16, NVT = C::DV / 16;
-  constexpr int KL = TileLoads<kDqThreads, C::KCH>::n, VL = TileLoads<kDqThreads, C::VCH>::n;
+  constexpr int NS = C::NS, NVS = C::NVS, NDT = C::NDT, NVT = C::NVT;
+  constexpr int KL = C::KL, VL = C::VL;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, jg = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -370,7 +293,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const int kb = p.causal ? logical % nk : nk - 1 - logical % nk;  // causal: most queries first
   const int t0 = logical / nk;
   const int n = t0 % p.Hn, b = t0 / p.Hn;
-  const int k0 = kb * kRB, kw = k0 + wave * kQW16, key = kw + l16, kc = min(key, p.N - 1);
+  const int k0 = kb * kRB, kw = k0 + wave * kRW, key = kw + l16, kc = min(key, p.N - 1);
   const float sgn = lambda_of(p.lam_dev, p.lam) > 0.f ? -1.f : 1.f;  // -lambda = sgn |lambda|
   const int qt0 = p.causal ? k0 / kTR : 0;
   const int ntile = (p.N + kTR - 1) / kTR;
@@ -382,35 +305,26 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) kf2[s] = *(const bf16x8*)(K2 + 32 * s + 8 * jg);
   }
-  f32x4v dk2[NDT], dk1[NDT], dv[NVT];
+  f32x4 dk2[NDT], dk1[NDT], dv[NVT];
 #pragma unroll
-  for (int ct = 0; ct < NDT; ++ct) dk2[ct] = dk1[ct] = f32x4v{};
+  for (int ct = 0; ct < NDT; ++ct) dk2[ct] = dk1[ct] = f32x4{};
 #pragma unroll
-  for (int vt = 0; vt < NVT; ++vt) dv[vt] = f32x4v{};
+  for (int vt = 0; vt < NVT; ++vt) dv[vt] = f32x4{};
   bf16x8 kf1[NS], vf[NVS];
   int cur = -1;  // key/value head of the accumulating run
-
-  // accumulator tiles as gradient rows: lane l of tile ct holds column 16 ct + 4 (l/16) + r
-  // of key row `key`
-  auto store16 = [&](__bf16* row, const f32x4v* acc, int nt, float scale) {
-    for (int ct = 0; ct < nt; ++ct) {
-      const f32x4 y = acc[ct] * scale;
-      *(bf16x4*)(row + 16 * ct + 4 * jg) = __builtin_convertvector(y, bf16x4);
-    }
-  };
 
   for (int mem = 0; mem < p.g; ++mem) {
     const int h = __builtin_amdgcn_readfirstlane(p.members[n * p.g + mem]);
     const int kh = __builtin_amdgcn_readfirstlane(p.kv[h]);
     if (kh != cur) {
       if (cur >= 0 && key < p.N) {
-        store16((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)key * p.sgk1[1] + cur * p.sgk1[2], dk1, NDT, p.sm_scale);
-        store16((__bf16*)p.gv + b * p.sgv[0] + (int64_t)key * p.sgv[1] + cur * p.sgv[2], dv, NVT, 1.0f);
+        store_row16((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)key * p.sgk1[1] + cur * p.sgk1[2], dk1, p.sm_scale, jg);
+        store_row16((__bf16*)p.gv + b * p.sgv[0] + (int64_t)key * p.sgv[1] + cur * p.sgv[2], dv, 1.0f, jg);
       }
 #pragma unroll
-      for (int ct = 0; ct < NDT; ++ct) dk1[ct] = f32x4v{};
+      for (int ct = 0; ct < NDT; ++ct) dk1[ct] = f32x4{};
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt) dv[vt] = f32x4v{};
+      for (int vt = 0; vt < NVT; ++vt) dv[vt] = f32x4{};
       cur = kh;
       const __bf16* K1 = (const __bf16*)p.k1 + b * p.sk1[0] + (int64_t)kc * p.sk1[1] + kh * p.sk1[2];
       const __bf16* V = (const __bf16*)p.v + b * p.sv[0] + (int64_t)kc * p.sv[1] + kh * p.sv[2];
@@ -427,15 +341,15 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     u32x4 r1[KL], r2[KL], rv[VL], rr;
     auto load_all = [&](int qt) {
       const int r0 = qt * kTR;
-      tile_load_n<kDqThreads, C::KCH>(r1, Q1, p.sq1[1], r0, p.N - 1);
-      tile_load_n<kDqThreads, C::KCH>(r2, Q2, p.sq2[1], r0, p.N - 1);
-      tile_load_n<kDqThreads, C::VCH>(rv, DO, dors, r0, p.N - 1);
+      tile_load<C::KCH>(r1, Q1, p.sq1[1], r0, p.N - 1);
+      tile_load<C::KCH>(r2, Q2, p.sq2[1], r0, p.N - 1);
+      tile_load<C::VCH>(rv, DO, dors, r0, p.N - 1);
       if (tid < kTR) rr = *(const u32x4*)(RSB + 4 * (int64_t)min(r0 + tid, p.N - 1));
     };
     auto store_all = [&](unsigned char* t) {
-      tile_store_n<kDqThreads, C::KCH>(t, r1);
-      tile_store_n<kDqThreads, C::KCH>(t + C::KT, r2);
-      tile_store_n<kDqThreads, C::VCH>(t + 2 * C::KT, rv);
+      tile_store<C::KCH>(t, r1);
+      tile_store<C::KCH>(t + C::KT, r2);
+      tile_store<C::VCH>(t + 2 * C::KT, rv);
       if (tid < kTR) *(u32x4*)(t + 2 * C::KT + C::VT + 16 * tid) = rr;
     };
     load_all(qt0);
@@ -447,15 +361,15 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dkv_kernel(BwdParams p) {
       const unsigned char* tq2 = tq1 + C::KT;
       const unsigned char* tdo = tq1 + 2 * C::KT;
       const float* trs = (const float*)(tq1 + 2 * C::KT + C::VT);
-      // one 32-query sub-block (two 16-query accumulator tiles); MASK only where some
-      // query of it does not see some key of the wavefront
+      // one 32-query sub-block (two 16-query accumulator tiles), always masked: an
+      // unmasked copy next to it does not fit two wavefronts' registers per SIMD
       auto block = [&](auto mask, int sb) {
         constexpr bool MASK = decltype(mask)::value;
         const int qs0 = qt * kTR + sb * 32;
-        f32x4v s1[2], s2[2], dp[2];
+        f32x4 s1[2], s2[2], dp[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          s1[t] = s2[t] = dp[t] = f32x4v{};
+          s1[t] = s2[t] = dp[t] = f32x4{};
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
             s1[t] = mfma16(rd_rows16(tq1, sb * 32 + 16 * t, s, C::KCH, lane), kf1[s], s1[t]);
@@ -503,9 +417,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dkv_kernel(BwdParams p) {
     }
   }
   if (key < p.N) {
-    store16((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)key * p.sgk1[1] + cur * p.sgk1[2], dk1, NDT, p.sm_scale);
-    store16((__bf16*)p.gv + b * p.sgv[0] + (int64_t)key * p.sgv[1] + cur * p.sgv[2], dv, NVT, 1.0f);
-    store16((__bf16*)p.gk2 + b * p.sgk2[0] + (int64_t)key * p.sgk2[1] + n * p.sgk2[2], dk2, NDT, p.sm_scale);
+    store_row16((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)key * p.sgk1[1] + cur * p.sgk1[2], dk1, p.sm_scale, jg);
+    store_row16((__bf16*)p.gv + b * p.sgv[0] + (int64_t)key * p.sgv[1] + cur * p.sgv[2], dv, 1.0f, jg);
+    store_row16((__bf16*)p.gk2 + b * p.sgk2[0] + (int64_t)key * p.sgk2[1] + n * p.sgk2[2], dk2, p.sm_scale, jg);
   }
 }
 
@@ -516,11 +430,11 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
   const int64_t grid = (int64_t)p.B * p.Hn * nblk;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
   if (p.d == 64) {
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)grid), dim3(kDqThreads), 0, s, p);
-    hipLaunchKernelGGL(bwd_dkv_kernel<64>, dim3((unsigned)grid), dim3(kDqThreads), 0, s, p);
+    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(bwd_dkv_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   } else {
-    hipLaunchKernelGGL(bwd_dq_kernel<32>, dim3((unsigned)grid), dim3(kDqThreads), 0, s, p);
-    hipLaunchKernelGGL(bwd_dkv_kernel<32>, dim3((unsigned)grid), dim3(kDqThreads), 0, s, p);
+    hipLaunchKernelGGL(bwd_dq_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(bwd_dkv_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   }
   return hipGetLastError();
 }
