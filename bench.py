@@ -56,10 +56,10 @@ MEASURED_TRAFFIC = {
         "gda3to1_varlen_bf16_8x4096": 152162 * 1024 * 2.0 + 101300 * 1024 * 1.0,
     },
     "decode_bf16.hip": {
-        "sha256": "662c0853b95ac2613fe28ad7dd3544669d2a5d88fe6de61707548e122cbf5f9a",
+        "sha256": "d4fd5403c952a892359a89a55de42dd90be61951f3ca32afc3c956261ebc301b",
         # one step: decode_partial_kernel + decode_combine_kernel
-        "gda_decode_bf16_b64_l8192": (586405 + 4885) * 1024 * 2.0 + (9680 + 288) * 1024 * 1.0,
-        "gda_decode_fp8_b64_l8192": (293455 + 2557) * 1024 * 2.0 + (5021 + 288) * 1024 * 1.0,
+        "gda_decode_bf16_b64_l8192": (586384 + 4885) * 1024 * 2.0 + (9679 + 288) * 1024 * 1.0,
+        "gda_decode_fp8_b64_l8192": (293461 + 2557) * 1024 * 2.0 + (5021 + 288) * 1024 * 1.0,
     },
 }
 
