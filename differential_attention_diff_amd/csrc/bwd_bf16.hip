@@ -137,6 +137,20 @@ __device__ __forceinline__ int xcd_logical(int bid, int total) {
   return xcd * q8 + min(xcd, r8) + (bid >> 3);
 }
 
+// Work item `logical` of ngroups (batch, noise group) pairs x nblk blocks.
+// With few pairs per XCD (grouped heads) and few blocks per pair, clusters of
+// about one XCD's pairs are walked block-major, longest block first across the
+// cluster, so the XCD's workgroups finish together; otherwise each pair's
+// blocks are consecutive (its operands stay in L2) and balance the XCD by
+// themselves.  blk counts from the first block walked.
+__device__ __forceinline__ void bwd_item(int logical, int ngroups, int nblk, int& grp, int& blk) {
+  const int cl = (ngroups >= 64 || nblk >= 64) ? 1 : (ngroups + 7) / 8;
+  const int per = cl * nblk, c = logical / per, idx = logical % per;
+  const int cs = min(cl, ngroups - c * cl);  // the last cluster may be smaller
+  blk = idx / cs;
+  grp = c * cl + idx % cs;
+}
+
 // ---------------------------------------------------------------------------
 // dQ pass: workgroup = (b, noise group n, 128 queries)
 // ---------------------------------------------------------------------------
@@ -151,9 +165,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const int nq = (p.N + kRB - 1) / kRB;
-  const int logical = xcd_logical(blockIdx.x, (int)gridDim.x);
-  const int qb = nq - 1 - logical % nq;  // longest causal range first
-  const int t0 = logical / nq;
+  int t0, blk;
+  bwd_item(xcd_logical(blockIdx.x, (int)gridDim.x), p.B * p.Hn, nq, t0, blk);
+  const int qb = nq - 1 - blk;  // longest causal range first
   const int n = t0 % p.Hn, b = t0 / p.Hn;
   const int q0 = qb * kRB, qw = q0 + wave * kRW, q = qw + l16, qc = min(q, p.N - 1);
   const float sgn = lambda_of(p.lam_dev, p.lam) > 0.f ? -1.f : 1.f;  // -lambda = sgn |lambda|
@@ -289,9 +303,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int nk = (p.N + kRB - 1) / kRB;
-  const int logical = xcd_logical(blockIdx.x, (int)gridDim.x);
-  const int kb = p.causal ? logical % nk : nk - 1 - logical % nk;  // causal: most queries first
-  const int t0 = logical / nk;
+  int t0, blk;
+  bwd_item(xcd_logical(blockIdx.x, (int)gridDim.x), p.B * p.Hn, nk, t0, blk);
+  const int kb = p.causal ? blk : nk - 1 - blk;  // causal: most queries first
   const int n = t0 % p.Hn, b = t0 / p.Hn;
   const int k0 = kb * kRB, kw = k0 + wave * kRW, key = kw + l16, kc = min(key, p.N - 1);
   const float sgn = lambda_of(p.lam_dev, p.lam) > 0.f ? -1.f : 1.f;  // -lambda = sgn |lambda|

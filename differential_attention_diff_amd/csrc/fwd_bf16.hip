@@ -18,9 +18,12 @@
 //     map's O (64 registers), so a wavefront fits in 256 registers with room
 //     for the pipeline below.  Workgroup ids are remapped so that each XCD (ids
 //     congruent mod 8) walks a contiguous range of items ordered (batch, noise
-//     group, signal head of the group, query block longest causal block
-//     first): the ~32 workgroups an XCD runs at once share one head's K1/V and
-//     the group's K2, about 2 MB, which stays in that XCD's 4 MB L2.
+//     group, query block longest causal block first, signal head of the
+//     group) when a head has fewer than 64 query blocks -- the longest blocks
+//     of every head of the group start first, so the XCD's queue drains
+//     evenly -- and (batch, noise group, signal head, query block) otherwise,
+//     where a head's many blocks balance the XCD and the ~32 workgroups it
+//     runs at once share that head's K1/V and the group's K2 in its 4 MB L2.
 //   * K1, K2 and V tiles of 64 keys go straight from global memory into a
 //     four-slot LDS ring (global_load_lds_dwordx4, no staging registers); the
 //     two tiles after the two being read are in flight.  One barrier per
@@ -345,16 +348,31 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   const int bid = blockIdx.x;
   const int xcd = bid & 7, q8 = total >> 3, r8 = total & 7;
   const int logical = xcd * q8 + min(xcd, r8) + (bid >> 3);
-  const int qb = nq - 1 - logical % nq;
-  int t = logical / nq, member, n, sq;  // sq: sequence
+  int qb, member, n, sq;  // sq: sequence
   if (p.cu_seqlens) {
     // packed sequences of unequal lengths: sequence fastest, so the contiguous
     // range each XCD walks holds every sequence's share of the work
+    qb = nq - 1 - logical % nq;
+    int t = logical / nq;
     sq = t % p.nseq;
     t /= p.nseq;
     member = t % p.g;
     n = t / p.g;
+  } else if (nq < 64) {
+    // few query blocks per head: the signal heads of a noise group interleaved,
+    // longest query block first, so an XCD's workgroups finish together (a
+    // head's blocks alone are about one round of the XCD's CUs); the ones
+    // running at once share the group's K2
+    const int per = p.g * nq, idx = logical % per, grp = logical / per;
+    qb = nq - 1 - idx / p.g;
+    member = idx % p.g;
+    n = grp % p.Hn;
+    sq = grp / p.Hn;
   } else {
+    // long sequences: a head's blocks are consecutive, longest first (the
+    // workgroups running at once share that head's K/V prefix in L2)
+    qb = nq - 1 - logical % nq;
+    int t = logical / nq;
     member = t % p.g;
     t /= p.g;
     n = t % p.Hn;
