@@ -50,10 +50,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "differential_attention_diff_amd", "csrc")
 MEASURED_TRAFFIC = {
     "fwd_bf16.hip": {
-        "sha256": "919cfc42c7ca12c375cdcc83117e92d80dc5660711190f48846f9602072f7a3d",
-        "diff3b_bf16_n4096": 147768 * 1024 * 2.0 + 98304 * 1024 * 1.0,
-        "gda3to1_bf16_n4096": 97697 * 1024 * 2.0 + 73728 * 1024 * 1.0,
-        "gda3to1_varlen_bf16_8x4096": 152162 * 1024 * 2.0 + 101300 * 1024 * 1.0,
+        "sha256": "c2552a44db8f4e9dd2b74396cdcfb2a98e7bd7a737ca21eb1bc2a01c1a0e5f31",
+        "diff3b_bf16_n4096": 147919 * 1024 * 2.0 + 98304 * 1024 * 1.0,
+        "gda3to1_bf16_n4096": 143099 * 1024 * 2.0 + 73729 * 1024 * 1.0,
+        "gda3to1_varlen_bf16_8x4096": 152180 * 1024 * 2.0 + 101300 * 1024 * 1.0,
     },
     "decode_bf16.hip": {
         "sha256": "d4fd5403c952a892359a89a55de42dd90be61951f3ca32afc3c956261ebc301b",
