@@ -70,11 +70,18 @@ struct BC {
 };
 
 // LDS byte offset of 16-B chunk c of row r in a tile with `ch` chunks per row.
-// The XOR term takes 16 distinct values over 16 consecutive rows (row-wise
-// 16-B operand reads spread over the banks) and 4 values, 2 bits apart, over
-// the 4 rows a transposing read touches.
+// Both read shapes hit 64 distinct 4-byte banks: a row-wise 16-B operand read
+// (16 lanes, 16 consecutive rows, one chunk) and a transposing read (32 lanes,
+// 8 consecutive rows, two adjacent chunks).  Rows of 256 B: the XOR term runs
+// over 16 values in 16 rows, rows r and r + 4 differing in bits 1-3.  Rows of
+// 128 B (two per 256 B): the term runs over 8 values on the even rows of 16
+// and 8 on the odd ones, the 4 even rows of an 8-row window differing in bits
+// 1-2.  Rows of 64 B: one value per 4-row window, windows r and r + 4 differing
+// in bit 1.
 __device__ __forceinline__ int swz(int r, int c, int ch) {
-  const int f = ch >= 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ch == 8 ? (((r & 3) << 1) | ((r >> 2) & 1)) : (r & 3);
+  const int f = ch >= 16  ? (((r & 7) << 1) | ((r >> 3) & 1))
+                : ch == 8 ? ((((r >> 1) & 3) << 1) | ((r >> 3) & 1))
+                          : ((((r >> 2) & 1) << 1) | ((r >> 3) & 1));
   return r * ch * 16 + ((c ^ f) << 4);
 }
 

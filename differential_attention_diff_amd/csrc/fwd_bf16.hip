@@ -88,6 +88,7 @@ struct Cfg {
   static constexpr int KCH = KROW / 16;          // 16-B chunks per K row (8 for d = 64)
   static constexpr int VCH = VROW / 16;          // 16-B chunks per V row (16 for dv = 128)
   static constexpr int KSW = (KCH >= 8 ? 8 : KCH) - 1;   // K swizzle mask
+  static constexpr int KSH = KROW >= 128 ? 1 : 2;         // K swizzle term: (r >> KSH) & KSW
   static constexpr int VSH = VCH >= 16 ? 2 : 1;           // V swizzle: chunk ^ ((r mod 4) << VSH)
   static constexpr int KRPL = 1024 / KROW, VRPL = 1024 / VROW;  // rows per KiB
   // tile DMA: waves 0-1 load K1, 2-3 K2, 4-7 V, TLOADS KiB each
@@ -97,18 +98,27 @@ struct Cfg {
   static_assert(TLOADS * 2 * 1024 == KBYTES && TLOADS * 4 * 1024 == VBYTES, "tile split over waves");
   static_assert(QLOADS * 4 * 1024 == QBYTES, "Q split over waves");
   static_assert(VCH >= 8, "V swizzle needs 8 chunks per row");
-  static_assert(KRPL % (KSW + 1) == 0 && VRPL % 4 == 0, "swizzle term must depend on the lane only");
+  // the K swizzle term of row row0 + l (row0 a multiple of KRPL, l < KRPL) is the
+  // term of row l, XOR KFLIP when row0 / KRPL is odd
+  static constexpr int KFLIP = (KRPL >> KSH) & KSW;
+  static_assert(((2 * KRPL) >> KSH) % (KSW + 1) == 0 && (KFLIP == 0 || ((KRPL - 1) >> KSH) < KFLIP),
+                "K swizzle term of a 1-KiB load: the lane's term, flipped by the load's parity");
+  static_assert(VRPL % 4 == 0, "V swizzle term must depend on the lane only");
+  static_assert(KFLIP == 0 || (TLOADS % 2 == 0 && QLOADS % 2 == 0), "a wave's K and Q loads start on an even KiB");
   static_assert(2 * QBYTES <= STAGE, "Q1 and Q2 are staged in one ring slot");
   static_assert(kGroups * kQW * DV * 4 <= 2 * STAGE, "O2 hand-off fits in two ring slots");
 };
 
 // LDS byte offset of 16-B chunk c of row r (XOR swizzle).  K (and Q): chunk ^
-// (r mod 8) spreads the rows an MFMA operand read touches over all banks.  V:
-// chunk ^ ((r mod 4) << VSH) puts the 4 rows a transposing read touches in
-// distinct bank windows (64 B apart for dv = 128, 32 B for dv = 64).
+// ((r >> KSH) mod 8) -- an MFMA operand read takes one chunk of 16 consecutive
+// rows per 16 lanes, and with rows of 128 B (two per 256-B bank window) the
+// term must differ between the 8 even rows and between the 8 odd ones, so it
+// counts pairs of rows (quads for 64-B rows).  V: chunk ^ ((r mod 4) << VSH)
+// puts the 4 rows a transposing read touches in distinct bank windows (64 B
+// apart for dv = 128, 32 B for dv = 64).
 template <int D>
 __device__ __forceinline__ int k_off(int r, int c) {
-  return r * Cfg<D>::KROW + ((c ^ (r & Cfg<D>::KSW)) << 4);
+  return r * Cfg<D>::KROW + ((c ^ ((r >> Cfg<D>::KSH) & Cfg<D>::KSW)) << 4);
 }
 template <int D>
 __device__ __forceinline__ int v_off(int r, int c) {
@@ -423,22 +433,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   const uint32_t tdst = (v_wave ? 2 * C::KBYTES : (wave < 2 ? 0 : C::KBYTES)) + tblk0 * 1024;
   const int lrow = v_wave ? lane / C::VCH : lane / C::KCH;
   const uint32_t lchunk = v_wave ? (uint32_t)(((lane % C::VCH) ^ ((lrow & 3) << C::VSH)) << 4)
-                                 : (uint32_t)(((lane % C::KCH) ^ (lrow & C::KSW)) << 4);
-  const uint32_t loff = (uint32_t)lrow * trs + lchunk;
+                                 : (uint32_t)(((lane % C::KCH) ^ ((lrow >> C::KSH) & C::KSW)) << 4);
+  // K rows of the odd KiB loads (tblk0 is even) take the flipped term
+  const uint32_t lflip = v_wave ? 0u : (uint32_t)(C::KFLIP << 4);
+  const uint32_t loff = (uint32_t)lrow * trs + lchunk, loff1 = (uint32_t)lrow * trs + (lchunk ^ lflip);
   auto issue_tile = [&](int tile) {
     const uint32_t dst = ring_lds + (tile % kSlots) * C::STAGE + tdst;
     const int key0 = tile * kKT;  // < N for every tile issued
     if (key0 + kKT <= N) {
       const char* g = (const char*)(tsrc + (int64_t)(key0 + tblk0 * rpl) * trow);
 #pragma unroll
-      for (int i = 0; i < C::TLOADS; ++i) dma16(g + (uint32_t)(i * rpl) * trs, loff, dst + i * 1024);
+      for (int i = 0; i < C::TLOADS; ++i) dma16(g + (uint32_t)(i * rpl) * trs, (i & 1) ? loff1 : loff, dst + i * 1024);
     } else {
       // rows relative to the tile start, clamped to the last valid row N - 1 - key0 >= 0
       const char* g = (const char*)(tsrc + (int64_t)key0 * trow);
       const int lim = N - 1 - key0;
 #pragma unroll
       for (int i = 0; i < C::TLOADS; ++i)
-        dma16(g, (uint32_t)min((tblk0 + i) * rpl + lrow, lim) * trs + lchunk, dst + i * 1024);
+        dma16(g, (uint32_t)min((tblk0 + i) * rpl + lrow, lim) * trs + ((i & 1) ? (lchunk ^ lflip) : lchunk),
+              dst + i * 1024);
     }
   };
   // before block 2t: blocks 2t and 2t + 1 read tiles t and t + 1.  Wait for this
@@ -462,13 +475,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
     const uint32_t qrs = (uint32_t)qrow * 2u;
     const int qblk0 = (wave & 3) * C::QLOADS;
     const int kr_l = lane / C::KCH;
-    const uint32_t kc_l = (uint32_t)(((lane % C::KCH) ^ (kr_l & C::KSW)) << 4);
+    const uint32_t kc_l = (uint32_t)(((lane % C::KCH) ^ ((kr_l >> C::KSH) & C::KSW)) << 4);
+    const uint32_t kc_l1 = kc_l ^ (uint32_t)(C::KFLIP << 4);  // odd KiB loads (qblk0 is even)
     const uint32_t qdst = ring_lds + (kSlots - 1) * C::STAGE + (q2w ? C::QBYTES : 0) + qblk0 * 1024;
     const int lim = N - 1 - q0;  // query rows past N re-read row N - 1 (never stored)
     const char* g = (const char*)(qsrc + (int64_t)q0 * qrow);
 #pragma unroll
     for (int i = 0; i < C::QLOADS; ++i)
-      dma16(g, (uint32_t)min((qblk0 + i) * C::KRPL + kr_l, lim) * qrs + kc_l, qdst + i * 1024);
+      dma16(g, (uint32_t)min((qblk0 + i) * C::KRPL + kr_l, lim) * qrs + ((i & 1) ? kc_l1 : kc_l), qdst + i * 1024);
   }
   for (int tt = 0; tt < min(ntiles, kSlots - 1); ++tt) issue_tile(tt);
   wait_tiles_in_flight<C::TLOADS>(min(ntiles, kSlots - 1) - 1);  // the Q rows and tile 0 have landed
