@@ -42,39 +42,49 @@ METRIC = "diff-attn fwd TFLOP/s (% bf16 MFMA peak) at seq 4096; decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 
-# HBM bytes per launch of the dominant kernel, from rocprofv3 FETCH_SIZE and WRITE_SIZE
-# passes (KiB per dispatch) scaled by what the same counters read for a plain 1 GiB
-# device copy in the same run (FETCH x 2.0, WRITE x 1.0); see
-# profiles/fwd_bf16_decode_hbm_counters.md.  Valid only for the kernel source the
-# counters were taken on (sha256 of the .hip file); reported as null otherwise.
+# HBM bytes per launch of the dominant kernel (per step of the multi-kernel decode and
+# backward), from rocprofv3 FETCH_SIZE and WRITE_SIZE passes (KiB per dispatch, mean of
+# the workload's 3 calls) scaled by what the same counters read for a plain 1 GiB device
+# copy in the same run (FETCH x 2.0, WRITE x 1.0); see profiles/fwd_bf16_decode_hbm_counters.md.
+# Valid only for the kernel sources the counters were taken on (sha256 of each file);
+# reported as null otherwise.
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "differential_attention_diff_amd", "csrc")
 MEASURED_TRAFFIC = {
-    "fwd_bf16.hip": {
-        "sha256": "c2552a44db8f4e9dd2b74396cdcfb2a98e7bd7a737ca21eb1bc2a01c1a0e5f31",
-        "diff3b_bf16_n4096": 147919 * 1024 * 2.0 + 98304 * 1024 * 1.0,
-        "gda3to1_bf16_n4096": 143099 * 1024 * 2.0 + 73729 * 1024 * 1.0,
-        "gda3to1_varlen_bf16_8x4096": 152180 * 1024 * 2.0 + 101300 * 1024 * 1.0,
+    "prefill": {
+        "sha256": {"fwd_bf16.hip": "0a6937bd55e74110ff675d7491648cf440558541797e1691019c5811cdd4abcc"},
+        "diff3b_bf16_n4096": 147801 * 1024 * 2.0 + 98304 * 1024 * 1.0,
+        "gda3to1_bf16_n4096": 143109 * 1024 * 2.0 + 73729 * 1024 * 1.0,
+        "gda3to1_varlen_bf16_8x4096": 152179 * 1024 * 2.0 + 101300 * 1024 * 1.0,
     },
-    "decode_bf16.hip": {
-        "sha256": "d4fd5403c952a892359a89a55de42dd90be61951f3ca32afc3c956261ebc301b",
+    "decode": {
+        "sha256": {"decode_bf16.hip": "d4fd5403c952a892359a89a55de42dd90be61951f3ca32afc3c956261ebc301b"},
         # one step: decode_partial_kernel + decode_combine_kernel
         "gda_decode_bf16_b64_l8192": (586384 + 4885) * 1024 * 2.0 + (9679 + 288) * 1024 * 1.0,
         "gda_decode_fp8_b64_l8192": (293461 + 2557) * 1024 * 2.0 + (5021 + 288) * 1024 * 1.0,
     },
+    "backward": {
+        "sha256": {"bwd_bf16.hip": "9cf7285a595b8c4b7468171251e3f2bc62aaeccfdae20dc5f755b3f393801f0c",
+                   "bwd_rows.hip": "10ca45ddf9f90b87d21211eb16910bcfbd2c6eebd9dc5fe721610504e8190ca7"},
+        # one step: bwd_prep_kernel + bwd_dq_kernel + bwd_dkv_kernel + bwd_finalize_kernel
+        "diff3b_bf16_n4096": (258210 + 200407 + 201198 + 527) * 1024 * 2.0 + (119055 + 98304 + 196608) * 1024 * 1.0,
+        "gda3to1_bf16_n4096": (193674 + 292652 + 516835 + 527) * 1024 * 2.0 + (91395 + 49152 + 122882) * 1024 * 1.0,
+    },
 }
 
 
-def measured_traffic(source: str, workload: str):
-    """Counter-derived HBM bytes per launch, or None if absent or the kernel source changed."""
-    entry = MEASURED_TRAFFIC.get(source)
+def measured_traffic(path: str, workload: str):
+    """Counter-derived HBM bytes per launch (or step), or None if absent or a kernel source changed."""
+    entry = MEASURED_TRAFFIC.get(path)
     if entry is None or workload not in entry:
         return None
-    try:
-        with open(os.path.join(CSRC, source), "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()
-    except OSError:
-        return None
-    return entry[workload] if digest == entry["sha256"] else None
+    for source, sha in entry["sha256"].items():
+        try:
+            with open(os.path.join(CSRC, source), "rb") as f:
+                if hashlib.sha256(f.read()).hexdigest() != sha:
+                    return None
+        except OSError:
+            return None
+    return entry[workload]
 
 
 # ---------------------------------------------------------------------------
@@ -205,7 +215,7 @@ def bench_prefill(w, steps, warmup, inp=None):
                    "dv": w.dv, "causal": w.causal, "entry": "diffattn_fwd" if plain else "gda_fwd",
                    "flop_convention": "F_alg"},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic("fwd_bf16.hip", w.name),
+                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill", w.name),
                      "flops_per_launch": fa, "kernel": "fwd_bf16_kernel<64>"},
         "roofline_exec": {"achieved": ache, "frac": ache / PEAK_BF16_TFLOPS, "flops_per_launch": fe},
         "algorithmic_bytes": prefill_bytes(w),
@@ -233,7 +243,7 @@ def bench_varlen(w, steps, warmup):
                    "max_seqlen": d["max_seqlen"], "H_s": w.H_s, "H_n": w.H_n, "H_kv": w.H_kv, "d": w.d, "dv": w.dv,
                    "causal": True, "entry": "gda_fwd_varlen", "flop_convention": "F_alg"},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic("fwd_bf16.hip", w.name),
+                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill", w.name),
                      "flops_per_launch": fa, "kernel": "fwd_bf16_kernel<64>"},
     }
 
@@ -262,7 +272,8 @@ def bench_backward(w, steps, warmup):
         "config": {"workload": w.name, "B": w.B, "N": w.N, "H_s": w.H_s, "H_n": w.H_n, "H_kv": w.H_kv, "d": w.d,
                    "dv": w.dv, "causal": w.causal, "entry": "gda_bwd", "flop_convention": "F_alg backward"},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "flops_per_launch": fb,
+                     "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic("backward", w.name),
+                     "flops_per_launch": fb,
                      "kernel": "bwd_prep + bwd_dq_kernel<64> + bwd_dkv_kernel<64> + bwd_finalize (step time)"},
     }
 
@@ -289,7 +300,7 @@ def bench_decode(w, steps, warmup):
                    "d": w.d, "dv": w.dv, "cache": "e4m3 + per-cache scale" if w.cache == "fp8" else "bf16",
                    "entry": "gda_decode"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("decode_bf16.hip", w.name),
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("decode", w.name),
                      "bytes_per_launch": nb,
                      "kernel": "decode_partial_kernel + decode_combine_kernel (step time)"},
     }
