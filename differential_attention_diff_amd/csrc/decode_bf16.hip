@@ -112,6 +112,30 @@ __device__ __forceinline__ float round_bf16(float x) {
   return (float)h;
 }
 
+// Channels of two cached rows a, b (8 each) as bf16 pairs: cv[c] = (a[c], b[c]), so a
+// v_dot2 against the pair of the rows' weights adds both rows' products at once.
+// e4m3: the fp8 bytes are interleaved first and then converted (exact, as above).
+__device__ __forceinline__ void pair_rows(u32x4 a, u32x4 b, uint32_t (&cv)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t x = a[e], y = b[e];
+    cv[2 * e] = __builtin_amdgcn_perm(y, x, 0x05040100u);      // low halves
+    cv[2 * e + 1] = __builtin_amdgcn_perm(y, x, 0x07060302u);  // high halves
+  }
+}
+__device__ __forceinline__ void pair_rows(u32x2 a, u32x2 b, uint32_t (&cv)[8]) {
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint32_t x = a[e], y = b[e];
+    const uint32_t lo = __builtin_amdgcn_perm(y, x, 0x05010400u);  // a.c0 b.c0 a.c1 b.c1
+    const uint32_t hi = __builtin_amdgcn_perm(y, x, 0x07030602u);  // a.c2 b.c2 a.c3 b.c3
+    cv[4 * e + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+    cv[4 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+    cv[4 * e + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+    cv[4 * e + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+  }
+}
+
 // dot of 8 bf16 pairs held in two u32x4 (lanes are copied to scalars first:
 // this compiler's __builtin_bit_cast of a vector element reads element 0)
 __device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
@@ -310,10 +334,12 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
       if (u >= nu) continue;
       const int kvh = ukv[u];
       if (u > 0) load_v(kvh, r0, ns);
+      static_assert(kVC % 2 == 0, "rows are taken in pairs");
 #pragma unroll
-      for (int i = 0; i < kVC; ++i) {
-        const int r = vrow + 16 * i;
-        const u32x4 vb = as_bf16(vr[i]);
+      for (int i = 0; i < kVC; i += 2) {
+        const int r = vrow + 16 * i;  // rows r and r + 16
+        uint32_t cv[8];
+        pair_rows(vr[i], vr[i + 1], cv);
 #pragma unroll
         for (int o = 0; o < kMaxOut; ++o) {
           int src = -1;
@@ -323,22 +349,17 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
             src = g;
           }
           if (src >= 0) {
-            // the bf16 weight as the pairs (w, 0) and (0, w): v_dot2 against a V dword then
-            // yields w * v[2e] and w * v[2e + 1] without converting V to fp32
-            const uint32_t wb = __float_as_uint(S[src][r]) >> 16;
-            const uint32_t wlo = wb, whi = wb << 16;
+            // the two rows' bf16 weights (the upper halves of their fp32 values, which are
+            // bf16-rounded) as one pair: each v_dot2 adds w_r v_r[c] + w_r' v_r'[c]
+            const uint32_t wp =
+                __builtin_amdgcn_perm(__float_as_uint(S[src][r + 16]), __float_as_uint(S[src][r]), 0x07060302u);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t vw = vb[e];
-              acc[o][2 * e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, vw),
-                                                              __builtin_bit_cast(bf16x2, wlo), acc[o][2 * e], false);
-              acc[o][2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, vw),
-                                                                  __builtin_bit_cast(bf16x2, whi), acc[o][2 * e + 1],
-                                                                  false);
-            }
+            for (int ch = 0; ch < 8; ++ch)
+              acc[o][ch] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, cv[ch]),
+                                                           __builtin_bit_cast(bf16x2, wp), acc[o][ch], false);
           }
         }
-        // one row's weights live at a time (keeps the kernel at 3 wavefronts per SIMD)
+        // one row pair's weights live at a time (keeps the kernel's wavefronts per SIMD)
         __builtin_amdgcn_sched_barrier(0);
       }
     }
