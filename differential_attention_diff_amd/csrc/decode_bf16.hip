@@ -17,12 +17,14 @@
 // (64 KiB for d = 64), each wave instruction reading 1 KiB contiguous -- are
 // all in flight at once, into registers; the next sub-chunk's keys are loaded
 // as soon as the scores are taken and its values as soon as P.V is done:
-//   scores  thread (row, 16-B column) dots its 8 dims with each query (v_dot2
-//           bf16), 8 lanes reduce a row; the g signal queries use K1, the
-//           noise query K2; scores go to LDS in log2 units;
+//   scores  S = K Q^T on v_mfma_f32_16x16x32_bf16, 16 cached rows per product
+//           with the group's queries as the columns: the g signal queries
+//           against K1, the noise query against K2; scores go to LDS in log2
+//           units;
 //   softmax wave q merges the sub-chunk into query q's running max m and sum
 //           l (the accumulators are rescaled by 2^(m_old - m_new)), P in LDS;
-//   P.V     thread (8 rows, 8 channels) accumulates one output per signal head
+//   P.V     thread (8 rows, 8 channels; rows taken in pairs, one v_dot2 per
+//           channel and pair) accumulates one output per signal head
 //           (map 1) and one per distinct V head (map 2, shared by the group's
 //           signal heads) from its V registers; partial sums are reduced over
 //           the chunk's rows through lane swaps and LDS.
@@ -40,6 +42,8 @@ namespace da {
 namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -136,18 +140,6 @@ __device__ __forceinline__ void pair_rows(u32x2 a, u32x2 b, uint32_t (&cv)[8]) {
   }
 }
 
-// dot of 8 bf16 pairs held in two u32x4 (lanes are copied to scalars first:
-// this compiler's __builtin_bit_cast of a vector element reads element 0)
-__device__ __forceinline__ float dot8(u32x4 a, u32x4 b) {
-  float acc = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t x = a[e], y = b[e];
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), acc, false);
-  }
-  return acc;
-}
-
 // MAXO bounds both g + 1 (scored queries) and g + u (outputs); 4 covers 3:1 GDA
 // with one key/value head per group, 8 the general case.
 // MULTI: some noise group spans several key/value heads (u > 1); the kernel then
@@ -165,8 +157,9 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
   constexpr int CP = FP8 ? 2 * kC : kC;
   constexpr int kKC = CP * (kD / 8) / kT;   // K chunks of 8 elements per thread
   constexpr int kVC = CP * (kDV / 8) / kT;  // V chunks of 8 elements per thread
+  static_assert(kKC == 2 * (CP / 64) && kD == 64, "K: two 32-dim steps per 16-row group, CP / 64 groups per wave");
   typedef typename Chunk<FP8>::T CK;
-  __shared__ float S[kMaxQ][CP];                // scores, then weights, of the current sub-chunk
+  __shared__ __attribute__((aligned(16))) float S[kMaxQ][CP];  // scores, then weights, of the current sub-chunk
   __shared__ float ML[3][kMaxQ];                // running max, running sum, last rescale per query
   __shared__ u32x4 QS[kMaxQ][kD / 8];           // the group's queries
   __shared__ float red[kT / 16][kMaxOut][kDV];  // partial outputs per 16-lane row group
@@ -190,8 +183,10 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
 #pragma unroll
   for (int u = 0; u < kMaxOut; ++u) ukv[u] = u < nu ? uni(p.ukv[n * g + u]) : -1;
 
-  // K layout: thread t holds rows t/8 + 32 i (i < 4), dims 8 (t%8) .. +7
-  const int krow = tid >> 3, kcol = tid & 7;
+  // K layout (A operands of v_mfma_f32_16x16x32_bf16): wave w owns CP/4 rows in groups of
+  // 16; for group j and 32-dim step s, lane l holds row 16 j + l%16 of the wave's rows,
+  // dims 32 s + 8 (l/16) .. +7 (register i = 2 j + s)
+  const int krow = wave * (CP / 4) + (lane & 15), kq = lane >> 4;
   // V layout: thread t holds rows t/16 + 16 i (i < 8), channels 8 (t%16) .. +7
   const int vrow = tid >> 4, vcol = tid & 15;
 
@@ -214,8 +209,8 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
     const uint32_t rs = (uint32_t)st[2] * ES;
 #pragma unroll
     for (int i = 0; i < kKC; ++i) {
-      const uint32_t r = (uint32_t)min(krow + 32 * i, ns - 1);
-      dst[i] = *(const CK*)(K + (r * rs + 8u * ES * (uint32_t)kcol));
+      const uint32_t r = (uint32_t)min(krow + 16 * (i >> 1), ns - 1);
+      dst[i] = *(const CK*)(K + (r * rs + 8u * ES * (uint32_t)(kq + 4 * (i & 1))));
     }
   };
   auto load_v = [&](int head, int r0, int ns) {
@@ -237,11 +232,24 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
   }
   // scores in log2 units; e4m3 keys carry their cache's scale
   const float sc1 = p.sm_scale_log2 * (FP8 ? p.k1_scale : 1.0f), sc2 = p.sm_scale_log2 * (FP8 ? p.k2_scale : 1.0f);
-  auto score_rows = [&](int qi, const CK(&kr)[kKC]) {
+  // S = K Q^T per 16 rows on MFMA: the B operand holds the group's queries as columns
+  // (lane l: query l%16, zero past the noise query g), so one product of K1 gives the
+  // signal queries' scores and one of K2 the noise query's; lane l receives rows
+  // 4 (l/16) .. +3 of column l%16 and stores those of its own query and map.
+  const int qq = lane & 15;
+  int qkv = -1;  // key/value head of the signal query in column qq
 #pragma unroll
-    for (int i = 0; i < kKC; ++i) {
-      const float sc = sum8(dot8(as_bf16(kr[i]), QS[qi][kcol]));
-      if (kcol == 0) S[qi][krow + 32 * i] = sc * (qi < g ? sc1 : sc2);
+  for (int i = 0; i < kMaxQ; ++i) qkv = qq == i ? mem_kv[i] : qkv;
+  bf16x8 qf[2];
+  auto score_rows = [&](const CK(&kr)[kKC], bool mine, float scale) {
+#pragma unroll
+    for (int j = 0; j < kKC / 2; ++j) {
+      f32x4 c = {};
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, as_bf16(kr[2 * j + s])), qf[s], c, 0, 0,
+                                                    0);
+      if (mine) *(f32x4*)&S[qq][wave * (CP / 4) + 16 * j + 4 * kq] = c * scale;
     }
   };
 
@@ -271,16 +279,17 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
     __syncthreads();  // the previous sub-chunk's weights are no longer read
     // ---- scores (log2 units): the noise query on K2, each signal query on its K1
 #pragma unroll
-    for (int qi = 0; qi < kMaxQ; ++qi)
-      if (qi == g) score_rows(qi, k2r);
+    for (int s = 0; s < 2; ++s) {
+      const u32x4 x = QS[min(qq, g)][4 * s + kq];
+      qf[s] = __builtin_bit_cast(bf16x8, qq <= g ? x : u32x4{0u, 0u, 0u, 0u});
+    }
+    score_rows(k2r, qq == g, sc2);
 #pragma unroll
     for (int u = 0; u < (MULTI ? kMaxOut : 1); ++u) {
       if (u < nu) {
         const int kvh = ukv[u];
         if (u > 0) load_k(k1r, p.k1, p.sk1, kvh, r0, ns);
-#pragma unroll
-        for (int qi = 0; qi < kMaxQ; ++qi)
-          if (qi < g && mem_kv[qi] == kvh) score_rows(qi, k1r);
+        score_rows(k1r, qq < g && qkv == kvh, sc1);
       }
     }
     if (nxt < nk) {  // K registers are free: prefetch the next sub-chunk's keys
