@@ -159,7 +159,8 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
   constexpr int kVC = CP * (kDV / 8) / kT;  // V chunks of 8 elements per thread
   static_assert(kKC == 2 * (CP / 64) && kD == 64, "K: two 32-dim steps per 16-row group, CP / 64 groups per wave");
   typedef typename Chunk<FP8>::T CK;
-  __shared__ __attribute__((aligned(16))) float S[kMaxQ][CP];  // scores, then weights, of the current sub-chunk
+  // scores, then weights, of a sub-chunk; two buffers, alternating by sub-chunk
+  __shared__ __attribute__((aligned(16))) float S2[2][kMaxQ][CP];
   __shared__ float ML[3][kMaxQ];                // running max, running sum, last rescale per query
   __shared__ u32x4 QS[kMaxQ][kD / 8];           // the group's queries
   __shared__ float red[kT / 16][kMaxOut][kDV];  // partial outputs per 16-lane row group
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
 #pragma unroll
   for (int i = 0; i < kMaxQ; ++i) qkv = qq == i ? mem_kv[i] : qkv;
   bf16x8 qf[2];
-  auto score_rows = [&](const CK(&kr)[kKC], bool mine, float scale) {
+  auto score_rows = [&](float(*Sb)[CP], const CK(&kr)[kKC], bool mine, float scale) {
 #pragma unroll
     for (int j = 0; j < kKC / 2; ++j) {
       f32x4 c = {};
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
       for (int s = 0; s < 2; ++s)
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, as_bf16(kr[2 * j + s])), qf[s], c, 0, 0,
                                                     0);
-      if (mine) *(f32x4*)&S[qq][wave * (CP / 4) + 16 * j + 4 * kq] = c * scale;
+      if (mine) *(f32x4*)&Sb[qq][wave * (CP / 4) + 16 * j + 4 * kq] = c * scale;
     }
   };
 
@@ -274,22 +275,26 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
   load_v(kv0, 0, ns);
   __builtin_amdgcn_sched_barrier(0);
 
+  // the queries and the running statistics are written above; from here on the score
+  // barrier of sub-chunk t also ends every wave's P.V of sub-chunk t - 1, so sub-chunk
+  // t + 1 may write its scores into the buffer t - 1 used without a further barrier
+  __syncthreads();
   for (int r0 = 0; r0 < nk; r0 += CP) {
     const int nxt = r0 + CP, ns_next = min(CP, nk - nxt);
-    __syncthreads();  // the previous sub-chunk's weights are no longer read
+    float(*S)[CP] = S2[(r0 / CP) & 1];
     // ---- scores (log2 units): the noise query on K2, each signal query on its K1
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const u32x4 x = QS[min(qq, g)][4 * s + kq];
       qf[s] = __builtin_bit_cast(bf16x8, qq <= g ? x : u32x4{0u, 0u, 0u, 0u});
     }
-    score_rows(k2r, qq == g, sc2);
+    score_rows(S, k2r, qq == g, sc2);
 #pragma unroll
     for (int u = 0; u < (MULTI ? kMaxOut : 1); ++u) {
       if (u < nu) {
         const int kvh = ukv[u];
         if (u > 0) load_k(k1r, p.k1, p.sk1, kvh, r0, ns);
-        score_rows(k1r, qq < g && qkv == kvh, sc1);
+        score_rows(S, k1r, qq < g && qkv == kvh, sc1);
       }
     }
     if (nxt < nk) {  // K registers are free: prefetch the next sub-chunk's keys
