@@ -12,22 +12,27 @@
 // kernels are organised around keeping enough bytes in flight:
 //
 // Kernel 1 (partial): one workgroup per (chunk of cached positions, noise
-// group, sequence).  The chunk is walked in sub-chunks of kC = 128 positions (256 for e4m3 caches)
-// whose loads -- K2 of the noise head, K1 and V of the group's key/value head
-// (64 KiB for d = 64), each wave instruction reading 1 KiB contiguous -- are
-// all in flight at once, into registers; the next sub-chunk's keys are loaded
-// as soon as the scores are taken and its values as soon as P.V is done:
+// group, sequence).  The chunk is walked in sub-chunks of kC = 128 positions
+// (256 for e4m3 caches); each of the four wavefronts owns a quarter of every
+// sub-chunk and runs its own softmax over it, so the loop has no workgroup
+// barrier.  A wavefront's loads of a sub-chunk -- K2 of the noise head, K1 and
+// V of the group's key/value head (16 KiB for d = 64) -- are all in flight at
+// once, into registers; the next sub-chunk's keys are loaded as soon as the
+// scores are taken and its values as soon as P.V is done:
 //   scores  S = K Q^T on v_mfma_f32_16x16x32_bf16, 16 cached rows per product
 //           with the group's queries as the columns: the g signal queries
-//           against K1, the noise query against K2; scores go to LDS in log2
-//           units;
-//   softmax wave q merges the sub-chunk into query q's running max m and sum
-//           l (the accumulators are rescaled by 2^(m_old - m_new)), P in LDS;
+//           against K1, the noise query against K2, in log2 units; lane l
+//           keeps the scores of query l%16;
+//   softmax the 4 lanes of a query column reduce its max and sum by lane
+//           swaps; the wavefront's running max m and sum l per query move
+//           (its accumulators are rescaled by 2^(m_old - m_new)); the bf16
+//           weights go to the wavefront's own LDS rows;
 //   P.V     thread (8 rows, 8 channels; rows taken in pairs, one v_dot2 per
 //           channel and pair) accumulates one output per signal head
 //           (map 1) and one per distinct V head (map 2, shared by the group's
-//           signal heads) from its V registers; partial sums are reduced over
-//           the chunk's rows through lane swaps and LDS.
+//           signal heads) from its V registers.
+// At the end the four wavefronts' partials are put on a common max (rescale by
+// 2^(m_w - M)) and summed over the chunk's rows through LDS.
 // Each output's (m, l, o[dv]) goes to the workspace.  A group whose signal
 // heads use several key/value heads loops over them.
 // Kernel 2 (combine): one workgroup per (noise group, sequence) merges the
@@ -149,7 +154,7 @@ __device__ __forceinline__ void pair_rows(u32x2 a, u32x2 b, uint32_t (&cv)[8]) {
 // keys are read as value * k_scale by scaling the scores, values as
 // value * v_scale by scaling the partial outputs.
 template <int MAXO, bool MULTI, bool FP8>
-__global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kT, 3) void decode_partial_kernel(DecodeParams p) {
   constexpr int kMaxQ = MAXO, kMaxOut = MAXO;
   constexpr uint32_t ES = FP8 ? 1 : 2;  // cache bytes per element
   // positions per sub-chunk: fp8 caches take twice as many, so a sub-chunk keeps the
@@ -158,10 +163,11 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
   constexpr int kKC = CP * (kD / 8) / kT;   // K chunks of 8 elements per thread
   constexpr int kVC = CP * (kDV / 8) / kT;  // V chunks of 8 elements per thread
   static_assert(kKC == 2 * (CP / 64) && kD == 64, "K: two 32-dim steps per 16-row group, CP / 64 groups per wave");
+  static_assert(kT / 64 == 4 && kVC == CP / 16, "four waves, each with CP/4 rows of every sub-chunk");
   typedef typename Chunk<FP8>::T CK;
-  // scores, then weights, of a sub-chunk; two buffers, alternating by sub-chunk
-  __shared__ __attribute__((aligned(16))) float S2[2][kMaxQ][CP];
-  __shared__ float ML[3][kMaxQ];                // running max, running sum, last rescale per query
+  // weights of a wave's rows of the current sub-chunk, per query (each wave its own)
+  __shared__ __attribute__((aligned(16))) float SW[kT / 64][kMaxQ][CP / 4];
+  __shared__ float MLW[kT / 64][2][kMaxQ];      // each wave's running max and sum per query
   __shared__ u32x4 QS[kMaxQ][kD / 8];           // the group's queries
   __shared__ float red[kT / 16][kMaxOut][kDV];  // partial outputs per 16-lane row group
   const int c = blockIdx.x, n = blockIdx.y, b = blockIdx.z;
@@ -188,8 +194,9 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
   // 16; for group j and 32-dim step s, lane l holds row 16 j + l%16 of the wave's rows,
   // dims 32 s + 8 (l/16) .. +7 (register i = 2 j + s)
   const int krow = wave * (CP / 4) + (lane & 15), kq = lane >> 4;
-  // V layout: thread t holds rows t/16 + 16 i (i < 8), channels 8 (t%16) .. +7
-  const int vrow = tid >> 4, vcol = tid & 15;
+  // V layout: wave w owns the same CP/4 rows as for K; lane l holds rows l/16 + 4 i of them
+  // (i < kVC), channels 8 (l%16) .. +7
+  const int vrow = wave * (CP / 4) + (lane >> 4), vcol = lane & 15;
 
   CK k1r[kKC], k2r[kKC], vr[kVC];
   // Rows [r0, r0 + ns) of the chunk (relative to key_lo).  Loads are branch-free so the
@@ -219,7 +226,7 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
     const uint32_t rs = (uint32_t)p.sv[2] * ES;
 #pragma unroll
     for (int i = 0; i < kVC; ++i) {
-      const uint32_t r = (uint32_t)min(vrow + 16 * i, ns - 1);
+      const uint32_t r = (uint32_t)min(vrow + 4 * i, ns - 1);
       vr[i] = *(const CK*)(V + (r * rs + 8u * ES * (uint32_t)vcol));
     }
   };
@@ -236,13 +243,13 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
   // S = K Q^T per 16 rows on MFMA: the B operand holds the group's queries as columns
   // (lane l: query l%16, zero past the noise query g), so one product of K1 gives the
   // signal queries' scores and one of K2 the noise query's; lane l receives rows
-  // 4 (l/16) .. +3 of column l%16 and stores those of its own query and map.
+  // 4 (l/16) .. +3 of column l%16 and keeps those of its own query and map.
   const int qq = lane & 15;
   int qkv = -1;  // key/value head of the signal query in column qq
 #pragma unroll
   for (int i = 0; i < kMaxQ; ++i) qkv = qq == i ? mem_kv[i] : qkv;
   bf16x8 qf[2];
-  auto score_rows = [&](float(*Sb)[CP], const CK(&kr)[kKC], bool mine, float scale) {
+  auto score_rows = [&](f32x4(&sv)[kKC / 2], const CK(&kr)[kKC], bool mine, float scale) {
 #pragma unroll
     for (int j = 0; j < kKC / 2; ++j) {
       f32x4 c = {};
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
       for (int s = 0; s < 2; ++s)
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, as_bf16(kr[2 * j + s])), qf[s], c, 0, 0,
                                                     0);
-      if (mine) *(f32x4*)&Sb[qq][wave * (CP / 4) + 16 * j + 4 * kq] = c * scale;
+      sv[j] = mine ? c * scale : sv[j];
     }
   };
 
@@ -259,10 +266,9 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
   for (int o = 0; o < kMaxOut; ++o)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[o][e] = 0.f;
-  if (tid < kMaxQ) {
-    ML[0][tid] = -INFINITY;
-    ML[1][tid] = 0.f;
-  }
+  // this wave's running max and sum for the query in column qq (the same in the 4 lanes
+  // qq + 16 k); the max starts finite so that rows all masked give factor 1, weight 0
+  float m_run = -1e30f, l_run = 0.f;
 
   // ---- every load of the first sub-chunk (the group's first key/value head) up front
   const int kv0 = ukv[0];
@@ -275,26 +281,29 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
   load_v(kv0, 0, ns);
   __builtin_amdgcn_sched_barrier(0);
 
-  // the queries and the running statistics are written above; from here on the score
-  // barrier of sub-chunk t also ends every wave's P.V of sub-chunk t - 1, so sub-chunk
-  // t + 1 may write its scores into the buffer t - 1 used without a further barrier
+  // The queries are in LDS after this barrier.  From here on each wave walks its own
+  // CP/4 rows of every sub-chunk with its own running softmax: no workgroup barrier until
+  // the four waves' partials are merged at the end.
   __syncthreads();
+  float(*W)[CP / 4] = SW[wave];
   for (int r0 = 0; r0 < nk; r0 += CP) {
     const int nxt = r0 + CP, ns_next = min(CP, nk - nxt);
-    float(*S)[CP] = S2[(r0 / CP) & 1];
     // ---- scores (log2 units): the noise query on K2, each signal query on its K1
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const u32x4 x = QS[min(qq, g)][4 * s + kq];
       qf[s] = __builtin_bit_cast(bf16x8, qq <= g ? x : u32x4{0u, 0u, 0u, 0u});
     }
-    score_rows(S, k2r, qq == g, sc2);
+    f32x4 sv[kKC / 2];
+#pragma unroll
+    for (int j = 0; j < kKC / 2; ++j) sv[j] = f32x4{};
+    score_rows(sv, k2r, qq == g, sc2);
 #pragma unroll
     for (int u = 0; u < (MULTI ? kMaxOut : 1); ++u) {
       if (u < nu) {
         const int kvh = ukv[u];
         if (u > 0) load_k(k1r, p.k1, p.sk1, kvh, r0, ns);
-        score_rows(S, k1r, qq < g && qkv == kvh, sc1);
+        score_rows(sv, k1r, qq < g && qkv == kvh, sc1);
       }
     }
     if (nxt < nk) {  // K registers are free: prefetch the next sub-chunk's keys
@@ -303,44 +312,49 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
       load_k(k1r, p.k1, p.sk1, kv0, nxt, ns_next);
       __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
-    // ---- merge this sub-chunk into the running softmax of each query (one wavefront per query)
-    for (int qi = wave; qi < nq; qi += kT / 64) {
-      constexpr int PL = CP / 64;  // positions per lane
-      float sv[PL];
-      float mx = -INFINITY;
+    // ---- this wave's rows into the running softmax of the query in column qq: the lane's
+    // rows are rb + 16 j + r; the 4 lanes qq + 16 k hold the query's rows between them
+    const int rb = wave * (CP / 4) + 4 * kq;
+    float mx = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < PL; ++k) {
-        sv[k] = lane + 64 * k < ns ? S[qi][lane + 64 * k] : -INFINITY;
-        mx = fmaxf(mx, sv[k]);
-      }
-      const float mold = ML[0][qi];
-      const float mnew = fmaxf(mold, wave_max(mx));
-      // weights are rounded to bf16 here: P.V consumes them as bf16 and the running sum
-      // accumulates the same rounded values
-      float tot = 0.f;
+    for (int j = 0; j < kKC / 2; ++j)
 #pragma unroll
-      for (int k = 0; k < PL; ++k) {
-        const float e = lane + 64 * k < ns ? round_bf16(__builtin_amdgcn_exp2f(sv[k] - mnew)) : 0.f;
-        S[qi][lane + 64 * k] = e;
-        tot += e;
+      for (int r = 0; r < 4; ++r) {
+        sv[j][r] = rb + 16 * j + r < ns ? sv[j][r] : -INFINITY;
+        mx = fmaxf(mx, sv[j][r]);
       }
-      const float sum = wave_sum(tot);
-      if (lane == 0) {
-        const float alpha = __builtin_amdgcn_exp2f(mold - mnew);  // 0 on the first sub-chunk
-        ML[0][qi] = mnew;
-        ML[1][qi] = ML[1][qi] * alpha + sum;
-        ML[2][qi] = alpha;
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the wave's first valid rows
+    // weights are rounded to bf16 here: P.V consumes them as bf16 and the running sum
+    // accumulates the same rounded values (masked rows: 2^-inf = 0)
+    float tot = 0.f;
+#pragma unroll
+    for (int j = 0; j < kKC / 2; ++j) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sv[j][r] = round_bf16(__builtin_amdgcn_exp2f(sv[j][r] - m_new));
+        tot += sv[j][r];
       }
+      if (qq <= g) *(f32x4*)&W[qq][16 * j + 4 * kq] = sv[j];
     }
-    __syncthreads();
+    tot += __shfl_xor(tot, 16);
+    tot += __shfl_xor(tot, 32);
+    l_run = l_run * alpha + tot;
+    m_run = m_new;
+    // the weights were written by other lanes of this wave: LDS serves a wave's accesses in
+    // order, and nothing may be moved across this point
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // ---- P.V: outputs 0..g-1 = map 1 of each member, g + u = map 2 on the group's u-th V head
 #pragma unroll
     for (int o = 0; o < kMaxOut; ++o) {
       if (o < nout) {
-        const float alpha = ML[2][o < g ? o : g];
+        const float a = lane_f(alpha, o < g ? o : g);  // lane q holds query q's factor
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[o][e] *= alpha;
+        for (int e = 0; e < 8; ++e) acc[o][e] *= a;
       }
     }
 #pragma unroll
@@ -351,7 +365,7 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
       static_assert(kVC % 2 == 0, "rows are taken in pairs");
 #pragma unroll
       for (int i = 0; i < kVC; i += 2) {
-        const int r = vrow + 16 * i;  // rows r and r + 16
+        const int lr = (lane >> 4) + 4 * i;  // the wave's rows lr and lr + 4
         uint32_t cv[8];
         pair_rows(vr[i], vr[i + 1], cv);
 #pragma unroll
@@ -366,7 +380,7 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
             // the two rows' bf16 weights (the upper halves of their fp32 values, which are
             // bf16-rounded) as one pair: each v_dot2 adds w_r v_r[c] + w_r' v_r'[c]
             const uint32_t wp =
-                __builtin_amdgcn_perm(__float_as_uint(S[src][r + 16]), __float_as_uint(S[src][r]), 0x07060302u);
+                __builtin_amdgcn_perm(__float_as_uint(W[src][lr + 4]), __float_as_uint(W[src][lr]), 0x07060302u);
 #pragma unroll
             for (int ch = 0; ch < 8; ++ch)
               acc[o][ch] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, cv[ch]),
@@ -383,14 +397,28 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
       __builtin_amdgcn_sched_barrier(0);
     }
     ns = ns_next;
+    // the next sub-chunk's weights overwrite these only after this wave's reads above
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // ---- reduce over the 16 row groups (threads t and t + 16 k hold the same channels) via LDS
+  // ---- merge the four waves (each relative to its own running max), then reduce over the
+  // 16 row groups (threads t and t + 16 k hold the same channels) via LDS
+  if (lane <= g) {
+    MLW[wave][0][lane] = m_run;
+    MLW[wave][1][lane] = l_run;
+  }
+  __syncthreads();
 #pragma unroll
   for (int o = 0; o < kMaxOut; ++o)
-    if (o < nout)
+    if (o < nout) {
+      const int q = o < g ? o : g;
+      const float M = fmaxf(fmaxf(MLW[0][0][q], MLW[1][0][q]), fmaxf(MLW[2][0][q], MLW[3][0][q]));
+      const float f = __builtin_amdgcn_exp2f(MLW[wave][0][q] - M);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) red[vrow][o][8 * vcol + e] = acc[o][e];
+      for (int e = 0; e < 8; ++e) red[tid >> 4][o][8 * vcol + e] = acc[o][e] * f;
+    }
   __syncthreads();
   float* ws = p.ws + (((int64_t)b * p.Hn + n) * p.nchunks + c) * (int64_t)p.slots * (kDV + 2);
   for (int i = tid; i < nout * kDV; i += kT) {
@@ -402,8 +430,12 @@ __global__ __launch_bounds__(kT, FP8 ? 3 : 4) void decode_partial_kernel(DecodeP
   }
   if (tid < nout) {
     const int q = tid < g ? tid : g;
-    ws[tid * (kDV + 2) + 0] = ML[0][q];
-    ws[tid * (kDV + 2) + 1] = ML[1][q];
+    const float M = fmaxf(fmaxf(MLW[0][0][q], MLW[1][0][q]), fmaxf(MLW[2][0][q], MLW[3][0][q]));
+    float Lq = 0.f;
+#pragma unroll
+    for (int w = 0; w < kT / 64; ++w) Lq += MLW[w][1][q] * __builtin_amdgcn_exp2f(MLW[w][0][q] - M);
+    ws[tid * (kDV + 2) + 0] = M;
+    ws[tid * (kDV + 2) + 1] = Lq;
   }
 }
 
