@@ -293,6 +293,7 @@ def bench_decode(w, steps, warmup):
     ms = time_steps(fn, steps, warmup)
     nb = decode_bytes(w, inp["seq_lens"].numpy())
     gbs = nb / (ms * 1e-3) / 1e9
+    probe = stream_read_probe(nb, steps, warmup)
     return {
         "workload": w.name, "metric": "decode HBM GB/s", "value": gbs, "unit": "GB/s", "ms_per_step": ms,
         "config": {"workload": w.name, "B": w.B, "Lmax": w.N, "len_range": list(w.len_range),
@@ -302,8 +303,25 @@ def bench_decode(w, steps, warmup):
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("decode", w.name),
                      "bytes_per_launch": nb,
-                     "kernel": "decode_partial_kernel + decode_combine_kernel (step time)"},
+                     "kernel": "decode_partial_kernel + decode_combine_kernel (step time)",
+                     "stream_read_probe": probe, "frac_of_probe": gbs / probe["value"]},
     }
+
+
+def stream_read_probe(nbytes, steps, warmup):
+    """Read rate of the library's plain streaming-read kernel (da_hbm_read_probe) over a
+    buffer of `nbytes`, the size of one decode step's reads: the measured reference beside
+    the published 8 TB/s."""
+    import torch
+    from differential_attention_diff_amd import ops
+    nb = (int(nbytes) + 15) // 16 * 16
+    buf = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ms = time_steps(lambda: ops.hbm_read_probe(buf, sink), steps, warmup)
+    del buf
+    return {"value": nb / (ms * 1e-3) / 1e9, "unit": "GB/s", "bytes": nb,
+            "kernel": "hbm_read_probe_kernel (non-temporal 16-B loads, 4 in flight per thread, 16384 x 256 threads)"}
 
 
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):

@@ -637,6 +637,20 @@ da_status da_lambda_reparam_bwd(const float* lq1, const float* lk1, const float*
   return DA_OK;
 }
 
+da_status da_hbm_read_probe(const void* src, size_t nbytes, float* sink, void* stream) {
+  if (nbytes == 0) return DA_OK;
+  if (!src || !sink) return fail(DA_EINVAL, "src and sink must be non-NULL");
+  if ((uintptr_t)src % 16 != 0 || nbytes % 16 != 0)
+    return fail(DA_EINVAL, "src must be 16-byte aligned and nbytes a multiple of 16");
+  if ((uintptr_t)sink % 4 != 0) return fail(DA_EINVAL, "sink must be 4-byte aligned");
+  if (nbytes > ((size_t)1 << 40)) return fail(DA_EINVAL, "nbytes above 1 TiB");
+  const Extent es{(uintptr_t)sink, (uintptr_t)sink + sizeof(float)}, ei{(uintptr_t)src, (uintptr_t)src + nbytes};
+  if (overlaps(es, ei)) return fail(DA_EINVAL, "sink overlaps src");
+  hipError_t e = da::launch_hbm_read_probe(src, (int64_t)nbytes, sink, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "read probe launch");
+  return DA_OK;
+}
+
 const char* da_status_str(int status) {
   switch (status) {
     case DA_OK: return "DA_OK: success";

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(L):
     names = ops.header_functions()
     assert set(names) >= {"diffattn_fwd", "gda_fwd", "gda_fwd_varlen", "gda_bwd", "gda_bwd_workspace_bytes",
                           "gda_decode", "gda_decode_workspace_bytes", "da_lambda_reparam", "da_lambda_reparam_bwd",
-                          "da_status_str", "da_last_error", "da_abi_version"}
+                          "da_status_str", "da_last_error", "da_abi_version", "da_hbm_read_probe"}
     for n in names:
         assert hasattr(L, n), f"libdiffattn.so does not export {n}"
 
@@ -338,3 +338,18 @@ def test_decode_workspace_query_ignores_pointers(L):
     a = base_dec()
     a.q1 = a.q2 = a.k1_cache = a.k2_cache = a.v_cache = a.seq_lens = a.out = None
     assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 64 * 6 * 16 * 4 * 130 * 4
+
+
+def test_read_probe_validation(L):
+    f = lambda i: ctypes.c_void_p(FAKE + i * GIB)
+    assert L.da_hbm_read_probe(None, 0, None, None) == ops.DA_OK  # nothing to read: no launch
+    st = L.da_hbm_read_probe(None, 1024, f(1), None)
+    assert st == ops.DA_EINVAL and "non-NULL" in ops.last_error()
+    st = L.da_hbm_read_probe(ctypes.c_void_p(FAKE + 8), 1024, f(1), None)
+    assert st == ops.DA_EINVAL and "aligned" in ops.last_error()
+    st = L.da_hbm_read_probe(f(0), 1000, f(1), None)
+    assert st == ops.DA_EINVAL and "multiple of 16" in ops.last_error()
+    st = L.da_hbm_read_probe(f(0), 1024, ctypes.c_void_p(FAKE + 512), None)
+    assert st == ops.DA_EINVAL and "overlaps" in ops.last_error()
+    st = L.da_hbm_read_probe(f(0), (1 << 40) + 16, f(2000), None)
+    assert st == ops.DA_EINVAL and "1 TiB" in ops.last_error()

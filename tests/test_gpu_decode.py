@@ -197,3 +197,13 @@ def test_paged_caches_equal_contiguous(fp8, block_size):
     assert torch.equal(out, ref)  # same products in the same order
     want = fp8_oracle(inp, scales, 0.7, 0.4) if fp8 else oracle(inp, 0.7, 0.4)
     assert_parity(as64(out), want, "bf16", f"paged decode fp8={fp8} block {block_size}")
+
+
+def test_read_probe_reads_and_writes_nothing():
+    # the measurement helper behind the decode lines' streaming-read reference
+    buf = torch.arange(1 << 18, dtype=torch.int32, device="cuda")  # 1 MiB, words never hit the sink value
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    ops.hbm_read_probe(buf, sink)
+    ops.hbm_read_probe(buf[: (1 << 18) - 4], sink)  # a length that is not a multiple of the grid
+    torch.cuda.synchronize()
+    assert torch.all(sink == 0)
