@@ -57,10 +57,10 @@ MEASURED_TRAFFIC = {
         "gda3to1_varlen_bf16_8x4096": 152179 * 1024 * 2.0 + 101300 * 1024 * 1.0,
     },
     "decode": {
-        "sha256": {"decode_bf16.hip": "502d37531e4cb4d587db36e55a16fa8491dfcd698b141b93833394ee599bbaf2"},
+        "sha256": {"decode_bf16.hip": "5873c3eca83b3483545ec7c62fd1cfed7912ff5ead5b49a65959525053bb995c"},
         # one step: decode_partial_kernel + decode_combine_kernel
-        "gda_decode_bf16_b64_l8192": (586668 + 4885) * 1024 * 2.0 + (9678 + 288) * 1024 * 1.0,
-        "gda_decode_fp8_b64_l8192": (293421 + 2557) * 1024 * 2.0 + (5022 + 288) * 1024 * 1.0,
+        "gda_decode_bf16_b64_l8192": (586458 + 4885) * 1024 * 2.0 + (9680 + 288) * 1024 * 1.0,
+        "gda_decode_fp8_b64_l8192": (294487 + 2557) * 1024 * 2.0 + (5021 + 288) * 1024 * 1.0,
     },
     "backward": {
         "sha256": {"bwd_bf16.hip": "9cf7285a595b8c4b7468171251e3f2bc62aaeccfdae20dc5f755b3f393801f0c",
