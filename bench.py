@@ -57,7 +57,9 @@ MEASURED_TRAFFIC = {
         "gda3to1_varlen_bf16_8x4096": 152179 * 1024 * 2.0 + 101300 * 1024 * 1.0,
     },
     "decode": {
-        "sha256": {"decode_bf16.hip": "5873c3eca83b3483545ec7c62fd1cfed7912ff5ead5b49a65959525053bb995c"},
+        # the split size (abi.cpp) sets how many partials the combine reads
+        "sha256": {"decode_bf16.hip": "5873c3eca83b3483545ec7c62fd1cfed7912ff5ead5b49a65959525053bb995c",
+                   "abi.cpp": "0"},
         # one step: decode_partial_kernel + decode_combine_kernel
         "gda_decode_bf16_b64_l8192": (586458 + 4885) * 1024 * 2.0 + (9680 + 288) * 1024 * 1.0,
         "gda_decode_fp8_b64_l8192": (294487 + 2557) * 1024 * 2.0 + (5021 + 288) * 1024 * 1.0,

@@ -240,7 +240,9 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain, const Packing
 // decode
 // ---------------------------------------------------------------------------
 
-constexpr int kDefaultChunk = 512;
+// default split: about kDefaultPartials partial workgroups (two rounds of the ~768 that
+// run at once, 3 per CU), with the split between one sub-chunk and kMaxChunk positions
+constexpr int64_t kDefaultPartials = 1536;
 constexpr int kChunkQuantum = 128;  // positions per decode sub-chunk
 constexpr int kMaxChunk = 2048;
 constexpr int kDecodeMaxQueries = 8;  // g + 1 scored queries per noise group
@@ -324,7 +326,12 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool chec
   }
   if (a->chunk % quantum != 0)
     return fail(DA_EINVAL, "chunk must be 0 or a positive multiple of %lld for these caches", (long long)quantum);
-  int64_t chunk = a->chunk ? a->chunk : (fp8 ? 2 * kDefaultChunk : kDefaultChunk);  // same bytes per partial
+  int64_t chunk = a->chunk;
+  if (!chunk) {  // partials of B x H_n x (Lmax / chunk) ~ kDefaultPartials, rounded up to the quantum
+    const int64_t work = a->B * a->H_n * a->Lmax;
+    chunk = (work / kDefaultPartials + quantum - 1) / quantum * quantum;
+    chunk = std::min<int64_t>(std::max<int64_t>(chunk, quantum), kMaxChunk);
+  }
   int64_t lmax_r = (a->Lmax + quantum - 1) / quantum * quantum;
   if (chunk > lmax_r) chunk = std::max<int64_t>(quantum, lmax_r);
   p->chunk = (int)chunk;
