@@ -318,6 +318,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
   const float sgn = lambda_of(p.lam_dev, p.lam) > 0.f ? -1.f : 1.f;  // -lambda = sgn |lambda|
   const int qt0 = p.causal ? k0 / kTR : 0;
   const int ntile = (p.N + kTR - 1) / kTR;
+  const int vis_lo = p.causal ? key : 0;                 // first query that sees this lane's key
+  const uint32_t vrange = (uint32_t)(p.N - vis_lo);      // visible queries: [vis_lo, N)
 
   const __bf16* Q2 = (const __bf16*)p.q2 + b * p.sq2[0] + n * p.sq2[2];
   bf16x8 kf2[NS];
@@ -387,6 +389,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
       auto block = [&](auto mask, int sb) {
         constexpr bool MASK = decltype(mask)::value;
         const int qs0 = qt * kTR + sb * 32;
+        const int vd0 = qs0 + 4 * jg - vis_lo;
         f32x4 s1[2], s2[2], dp[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -399,6 +402,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
           for (int s = 0; s < NVS; ++s) dp[t] = mfma16(rd_rows16(tdo, sb * 32 + 16 * t, s, C::VCH, lane), vf[s], dp[t]);
         }
+        // the score and dP products are issued before the weights are formed: letting
+        // the scheduler interleave the two measured 5% slower
+        __builtin_amdgcn_sched_barrier(0);
         // k order of the B operands: slots 0-3 = tile 0 rows 4 (l/16) + r, slots 4-7 = tile 1
         bf16x8 bc, b1, b2;
 #pragma unroll
@@ -410,8 +416,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
             float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[t][r], p.sm_scale_log2, -st.x));
             float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[t][r], p.sm_scale_log2, -st.y));  // |lambda| P2
             if (MASK) {
-              const int qg = qs0 + 16 * t + 4 * jg + r;
-              const bool vis = qg < p.N && (!p.causal || qg >= key);
+              // query qs0 + 16 t + 4 jg + r is visible iff it lies in [vis_lo, N): one
+              // unsigned compare, no control flow (for keys past N the range wraps, and
+              // their sums are never stored)
+              const bool vis = (uint32_t)(vd0 + 16 * t + r) < vrange;
               p1 = vis ? p1 : 0.f;
               p2 = vis ? p2 : 0.f;
             }
