@@ -59,17 +59,17 @@ MEASURED_TRAFFIC = {
     "decode": {
         # the split size (abi.cpp) sets how many partials the combine reads
         "sha256": {"decode_bf16.hip": "5873c3eca83b3483545ec7c62fd1cfed7912ff5ead5b49a65959525053bb995c",
-                   "abi.cpp": "0"},
+                   "abi.cpp": "b991feb9cf3973273bf3bce8d959913a5b4680a373fa2ca61faadf7ab098195c"},
         # one step: decode_partial_kernel + decode_combine_kernel
-        "gda_decode_bf16_b64_l8192": (586458 + 4885) * 1024 * 2.0 + (9680 + 288) * 1024 * 1.0,
-        "gda_decode_fp8_b64_l8192": (294487 + 2557) * 1024 * 2.0 + (5021 + 288) * 1024 * 1.0,
+        "gda_decode_bf16_b64_l8192": (586330 + 1405) * 1024 * 2.0 + (2732 + 288) * 1024 * 1.0,
+        "gda_decode_fp8_b64_l8192": (294415 + 1405) * 1024 * 2.0 + (2730 + 288) * 1024 * 1.0,
     },
     "backward": {
-        "sha256": {"bwd_bf16.hip": "9cf7285a595b8c4b7468171251e3f2bc62aaeccfdae20dc5f755b3f393801f0c",
+        "sha256": {"bwd_bf16.hip": "56f1156519d3e6014cd1cd06f36b7d71afb7c85101757a885ebbe157df63c346",
                    "bwd_rows.hip": "10ca45ddf9f90b87d21211eb16910bcfbd2c6eebd9dc5fe721610504e8190ca7"},
         # one step: bwd_prep_kernel + bwd_dq_kernel + bwd_dkv_kernel + bwd_finalize_kernel
-        "diff3b_bf16_n4096": (258210 + 200407 + 201198 + 527) * 1024 * 2.0 + (119055 + 98304 + 196608) * 1024 * 1.0,
-        "gda3to1_bf16_n4096": (193674 + 292652 + 516835 + 527) * 1024 * 2.0 + (91395 + 49152 + 122882) * 1024 * 1.0,
+        "diff3b_bf16_n4096": (258211 + 200375 + 201964 + 527) * 1024 * 2.0 + (119058 + 98304 + 196609) * 1024 * 1.0,
+        "gda3to1_bf16_n4096": (193674 + 293694 + 509295 + 527) * 1024 * 2.0 + (91395 + 49152 + 122883) * 1024 * 1.0,
     },
 }
 
