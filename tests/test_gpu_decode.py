@@ -207,3 +207,20 @@ def test_read_probe_reads_and_writes_nothing():
     ops.hbm_read_probe(buf[: (1 << 18) - 4], sink)  # a length that is not a multiple of the grid
     torch.cuda.synchronize()
     assert torch.all(sink == 0)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_single_long_sequence_automatic_split(fp8):
+    # one sequence of 16384 cached positions: the automatic split takes the smallest
+    # partials (128 positions; 256 for e4m3), so the combine merges 128 or 64 of them
+    L = 16384
+    if fp8:
+        inp, scales = fp8_inputs(1, L, 6, 2, 2, [L - 5], seed=27)
+        out = run(inp, 0.7, 0.7, cache_scales=scales)
+        want = fp8_oracle(inp, scales, 0.7, 0.7)
+    else:
+        inp = decode_inputs(1, L, 6, 2, 2, [L - 5], seed=27)
+        out = run(inp, 0.7, 0.7)
+        want = oracle(inp, 0.7, 0.7)
+    ma, rel = assert_parity(as64(out), want, "bf16", f"one {L}-position sequence, fp8={fp8}")
+    print(f"long single decode fp8={fp8}: max-abs {ma:.3e} rel {rel:.3e}")
