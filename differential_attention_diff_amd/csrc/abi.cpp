@@ -240,9 +240,11 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain, const Packing
 // decode
 // ---------------------------------------------------------------------------
 
-// default split: about kDefaultPartials partial workgroups (two rounds of the ~768 that
-// run at once, 3 per CU), with the split between one sub-chunk and kMaxChunk positions
-constexpr int64_t kDefaultPartials = 1536;
+// default split: about kDefaultPartials partial workgroups (a little over three rounds of
+// the ~768 that run at once, 3 per CU; measured on 64 sequences of 4096..8192 positions,
+// where 2048 partials leave the last round a third full), with the split between one
+// sub-chunk and kMaxChunk positions
+constexpr int64_t kDefaultPartials = 2560;
 constexpr int kChunkQuantum = 128;  // positions per decode sub-chunk
 constexpr int kMaxChunk = 2048;
 constexpr int kDecodeMaxQueries = 8;  // g + 1 scored queries per noise group

@@ -215,7 +215,7 @@ da_status gda_bwd(const da_bwd_args* args, void* workspace, size_t workspace_byt
  *     0 <= L_b <= Lmax is the caller's contract (the kernels clamp to
  *     [0, Lmax]); L_b == 0 yields a zero output row.
  *   chunk: cached positions per split-K partial (a multiple of 128, of 256
- *     for e4m3 caches; at most 2048), 0 = automatic: about 1536 partials in
+ *     for e4m3 caches; at most 2048), 0 = automatic: about 2560 partials in
  *     all (B x H_n x Lmax / chunk), rounded up to that multiple and capped at
  *     2048.  The result does not depend on it beyond rounding order.
  *   block_table: device int32 [B][max_blocks] or NULL.  When given the caches

@@ -257,12 +257,12 @@ def base_dec(B=64, L_=8192, hs=18, hn=6, hkv=6, d=64, chunk=0):
 
 def test_decode_workspace_bytes(L):
     a = base_dec()
-    # automatic split: 64 x 6 x 8192 positions / 1536 partials -> chunks of 2048; per
-    # (b, group, chunk): g + u = 3 + 1 slots of (dv + 2) floats
-    assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 64 * 6 * 4 * 4 * 130 * 4
+    # automatic split: 64 x 6 x 8192 positions / 2560 partials -> chunks of 1280, 7 per
+    # sequence; per (b, group, chunk): g + u = 3 + 1 slots of (dv + 2) floats
+    assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 64 * 6 * 7 * 4 * 130 * 4
     a = base_dec(chunk=512)
     assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 64 * 6 * 16 * 4 * 130 * 4
-    a = base_dec(B=2)  # 2 x 6 x 8192 / 1536 = 64 -> one sub-chunk, 128 positions
+    a = base_dec(B=2)  # 2 x 6 x 8192 / 2560 = 38 -> one sub-chunk, 128 positions
     assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 2 * 6 * 64 * 4 * 130 * 4
     a = base_dec(chunk=1024)
     assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 64 * 6 * 8 * 4 * 130 * 4
@@ -342,7 +342,7 @@ def test_empty_with_null_pointers_is_noop(L):
 def test_decode_workspace_query_ignores_pointers(L):
     a = base_dec()
     a.q1 = a.q2 = a.k1_cache = a.k2_cache = a.v_cache = a.seq_lens = a.out = None
-    assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 64 * 6 * 4 * 4 * 130 * 4  # automatic split: 2048 positions
+    assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 64 * 6 * 7 * 4 * 130 * 4  # automatic split: 1280 positions
 
 
 def test_read_probe_validation(L):
