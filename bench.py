@@ -59,10 +59,10 @@ MEASURED_TRAFFIC = {
     "decode": {
         # the split size (abi.cpp) sets how many partials the combine reads
         "sha256": {"decode_bf16.hip": "5873c3eca83b3483545ec7c62fd1cfed7912ff5ead5b49a65959525053bb995c",
-                   "abi.cpp": "b991feb9cf3973273bf3bce8d959913a5b4680a373fa2ca61faadf7ab098195c"},
+                   "abi.cpp": "0768a351d846e2f3566c2c7aa6472fc6447d52744dfcee41205b54fe99b9b9d9"},
         # one step: decode_partial_kernel + decode_combine_kernel
-        "gda_decode_bf16_b64_l8192": (586330 + 1405) * 1024 * 2.0 + (2732 + 288) * 1024 * 1.0,
-        "gda_decode_fp8_b64_l8192": (294415 + 1405) * 1024 * 2.0 + (2730 + 288) * 1024 * 1.0,
+        "gda_decode_bf16_b64_l8192": (586212 + 2114) * 1024 * 2.0 + (4121 + 288) * 1024 * 1.0,
+        "gda_decode_fp8_b64_l8192": (294331 + 2114) * 1024 * 2.0 + (4119 + 288) * 1024 * 1.0,
     },
     "backward": {
         "sha256": {"bwd_bf16.hip": "56f1156519d3e6014cd1cd06f36b7d71afb7c85101757a885ebbe157df63c346",
