@@ -86,7 +86,7 @@ __device__ __forceinline__ T ld_cache(const T* a) {
 __device__ __forceinline__ u32x4 as_bf16(u32x2 c) { return fp8_to_bf16(c); }
 
 constexpr int kT = 256;       // threads per workgroup
-constexpr int kC = 128;       // cached positions per partial workgroup (the chunk)
+constexpr int kC = 128;       // cached positions per sub-chunk (bf16 caches; e4m3: 2 kC)
 constexpr int kD = 64;        // the kernels are specialised to d = 64, dv = 128
 constexpr int kDV = 128;
 constexpr int kMaxQ = 8;      // g + 1 scored queries per group (largest instantiation)
