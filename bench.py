@@ -59,7 +59,7 @@ MEASURED_TRAFFIC = {
     "decode": {
         # the split size (abi.cpp) sets how many partials the combine reads
         "sha256": {"decode_bf16.hip": "4b89d132702106c3594acb3240f54c47c6d6db2e902caaee50c29cf728a93480",
-                   "abi.cpp": "0768a351d846e2f3566c2c7aa6472fc6447d52744dfcee41205b54fe99b9b9d9"},
+                   "abi.cpp": "221effc1aa6f9b37382ca73815928a4795cd0b927731c7a3c20a51a123bfd645"},
         # one step: decode_partial_kernel + decode_combine_kernel
         "gda_decode_bf16_b64_l8192": (586212 + 2114) * 1024 * 2.0 + (4121 + 288) * 1024 * 1.0,
         "gda_decode_fp8_b64_l8192": (294331 + 2114) * 1024 * 2.0 + (4119 + 288) * 1024 * 1.0,

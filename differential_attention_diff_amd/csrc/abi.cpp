@@ -330,15 +330,21 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool chec
     return fail(DA_EINVAL, "chunk must be 0 or a positive multiple of %lld for these caches", (long long)quantum);
   int64_t chunk = a->chunk;
   if (!chunk) {  // partials of B x H_n x (Lmax / chunk) ~ kDefaultPartials, rounded up to the quantum
-    const int64_t work = a->B * a->H_n * a->Lmax;
-    chunk = (work / kDefaultPartials + quantum - 1) / quantum * quantum;
-    chunk = std::min<int64_t>(std::max<int64_t>(chunk, quantum), kMaxChunk);
+    // (128-bit: B and Lmax may each reach 2^31)
+    const __int128 work = (__int128)a->B * a->H_n * a->Lmax;
+    const __int128 c = (work / kDefaultPartials + quantum - 1) / quantum * quantum;
+    chunk = (int64_t)std::min<__int128>(std::max<__int128>(c, quantum), kMaxChunk);
   }
   int64_t lmax_r = (a->Lmax + quantum - 1) / quantum * quantum;
   if (chunk > lmax_r) chunk = std::max<int64_t>(quantum, lmax_r);
   p->chunk = (int)chunk;
   p->nchunks = (int)((a->Lmax + chunk - 1) / chunk);
   p->slots = g + umax;
+  {  // the workspace size must be representable (sizes near the int32 limits would wrap it)
+    const __int128 ws = (__int128)a->B * a->H_n * p->nchunks *
+                        (__int128)da::decode_ws_floats_per_chunk(p->slots, (int)a->dv) * (__int128)sizeof(float);
+    if (ws > ((__int128)1 << 62)) return fail(DA_EINVAL, "the decode workspace for these shapes exceeds 2^62 bytes");
+  }
   p->q1 = a->q1;
   p->q2 = a->q2;
   p->k1 = a->k1_cache;

@@ -268,6 +268,8 @@ def test_decode_workspace_bytes(L):
     assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 64 * 6 * 8 * 4 * 130 * 4
     a = base_dec(chunk=192)
     assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 0 and "multiple of 128" in ops.last_error()
+    a = base_dec(B=2**31 - 1, L_=2**31 - 1)  # valid on their own, but the workspace size would wrap
+    assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 0 and "2^62" in ops.last_error()
     a = base_dec(chunk=4096)
     assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 0 and "exceeds" in ops.last_error()
 
