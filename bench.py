@@ -326,6 +326,21 @@ def stream_read_probe(nbytes, steps, warmup):
             "kernel": "hbm_read_probe_kernel (non-temporal 16-B loads, 4 in flight per thread, 16384 x 256 threads)"}
 
 
+def device_info():
+    """The device the line was measured on, and the dense bf16 peak its CU count implies at
+    the published 2.4 GHz (4 SIMDs x 1024 FLOP per clock per CU); the clock the matrix cores
+    hold under load is lower (about 2.0 GHz in the counter profiles)."""
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    cus = int(getattr(pr, "multi_processor_count", 0))
+    info = {"name": torch.cuda.get_device_name(0), "arch": getattr(pr, "gcnArchName", None), "cus": cus,
+            "bf16_peak_at_2p4ghz_tflops": cus * 4 * 1024 * 2.4e9 / 1e12 if cus else None}
+    clk = getattr(pr, "clock_rate", None)  # kHz, where torch exposes it
+    if clk:
+        info["max_sclk_mhz"] = clk / 1000.0
+    return info
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 3):
     """Plain device-to-device copies of a known size: a profiler's FETCH_SIZE / WRITE_SIZE for
     these dispatches should read nbytes each; the ratio scales the counters of the kernels."""
@@ -411,6 +426,7 @@ def main():
     if "roofline_exec" in head:
         line["roofline_exec"] = head["roofline_exec"]
     line["cpu_baseline"] = cpu
+    line["device"] = device_info()
     line["extra"] = extra
     if args.copy_calibration:
         line["copy_calibration"] = copy_calibration()
