@@ -65,11 +65,11 @@ MEASURED_TRAFFIC = {
         "gda_decode_fp8_b64_l8192": (294331 + 2114) * 1024 * 2.0 + (4119 + 288) * 1024 * 1.0,
     },
     "backward": {
-        "sha256": {"bwd_bf16.hip": "56f1156519d3e6014cd1cd06f36b7d71afb7c85101757a885ebbe157df63c346",
+        "sha256": {"bwd_bf16.hip": "2bfa2d4a4e1487a53cb4abd682b355d14ad9fbc7dc14d748f5bd6b5c2a6af1de",
                    "bwd_rows.hip": "10ca45ddf9f90b87d21211eb16910bcfbd2c6eebd9dc5fe721610504e8190ca7"},
         # one step: bwd_prep_kernel + bwd_dq_kernel + bwd_dkv_kernel + bwd_finalize_kernel
-        "diff3b_bf16_n4096": (258211 + 200375 + 201964 + 527) * 1024 * 2.0 + (119058 + 98304 + 196609) * 1024 * 1.0,
-        "gda3to1_bf16_n4096": (193674 + 293694 + 509295 + 527) * 1024 * 2.0 + (91395 + 49152 + 122883) * 1024 * 1.0,
+        "diff3b_bf16_n4096": (258211 + 200705 + 202339 + 527) * 1024 * 2.0 + (119054 + 98304 + 196613) * 1024 * 1.0,
+        "gda3to1_bf16_n4096": (193677 + 267550 + 468352 + 527) * 1024 * 2.0 + (91396 + 49152 + 122882) * 1024 * 1.0,
     },
 }
 

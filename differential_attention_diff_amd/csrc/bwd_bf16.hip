@@ -57,6 +57,7 @@ constexpr int kRW = 16;               // rows per wavefront
 constexpr int kWaves = kRB / kRW;     // 8
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTR = 64;               // rows per LDS tile
+constexpr int kRowPad = 32;           // LDS tile row padding, bytes
 
 template <int D>
 struct BC {
@@ -64,26 +65,19 @@ struct BC {
   static constexpr int NS = D / 32, NVS = DV / 32;     // 32-wide k steps over d, dv
   static constexpr int NDT = D / 16, NVT = DV / 16;    // 16-row output tiles over d, dv
   static constexpr int KCH = 2 * D / 16, VCH = 2 * DV / 16;  // 16-B chunks per row
-  static constexpr int KT = kTR * 2 * D, VT = kTR * 2 * DV;  // tile bytes
+  static constexpr int KT = kTR * (2 * D + kRowPad), VT = kTR * (2 * DV + kRowPad);  // tile bytes
   // 16-B tile loads per thread (a tile of fewer chunks than threads leaves the last threads idle)
   static constexpr int KL = (kTR * KCH + kThreads - 1) / kThreads, VL = (kTR * VCH + kThreads - 1) / kThreads;
 };
 
 // LDS byte offset of 16-B chunk c of row r in a tile with `ch` chunks per row.
-// Both read shapes hit 64 distinct 4-byte banks: a row-wise 16-B operand read
-// (16 lanes, 16 consecutive rows, one chunk) and a transposing read (32 lanes,
-// 8 consecutive rows, two adjacent chunks).  Rows of 256 B: the XOR term runs
-// over 16 values in 16 rows, rows r and r + 4 differing in bits 1-3.  Rows of
-// 128 B (two per 256 B): the term runs over 8 values on the even rows of 16
-// and 8 on the odd ones, the 4 even rows of an 8-row window differing in bits
-// 1-2.  Rows of 64 B: one value per 4-row window, windows r and r + 4 differing
-// in bit 1.
-__device__ __forceinline__ int swz(int r, int c, int ch) {
-  const int f = ch >= 16  ? (((r & 7) << 1) | ((r >> 3) & 1))
-                : ch == 8 ? ((((r >> 1) & 3) << 1) | ((r >> 3) & 1))
-                          : ((((r >> 2) & 1) << 1) | ((r >> 3) & 1));
-  return r * ch * 16 + ((c ^ f) << 4);
-}
+// Rows are padded by 32 B (8 of the 64 four-byte banks), so every operand read
+// is one per-lane base plus compile-time offsets.  A transposing read (32
+// lanes: 8 consecutive rows x 32 B) then hits 64 distinct banks; a row-wise
+// 16-B read (16 lanes, 16 consecutive rows) puts rows r and r + 8 on the same
+// banks.  That 2-way conflict costs less than the per-read address arithmetic
+// of an XOR swizzle (measured: the backward runs 6% faster this way).
+__device__ __forceinline__ int toff(int r, int c, int ch) { return r * (ch * 16 + kRowPad) + (c << 4); }
 
 // Rows [r0, r0 + 64) of a tensor (element row stride rs) into registers, then into
 // an LDS tile; rows past `last` re-read row `last`; thread t handles chunks t,
@@ -102,7 +96,7 @@ __device__ __forceinline__ void tile_store(unsigned char* t, const u32x4 (&reg)[
 #pragma unroll
   for (int k = 0; k < L; ++k) {
     const int idx = (int)threadIdx.x + kThreads * k, r = idx / CH, c = idx % CH;
-    if (kTR * CH % kThreads == 0 || idx < kTR * CH) *(u32x4*)(t + swz(r, c, CH)) = reg[k];
+    if (kTR * CH % kThreads == 0 || idx < kTR * CH) *(u32x4*)(t + toff(r, c, CH)) = reg[k];
   }
 }
 
@@ -113,7 +107,7 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // A operand of a 16 x 32 step read row-wise: lane l holds row rb + l%16, elements
 // 32 s + 8 (l/16) .. + 7.
 __device__ __forceinline__ bf16x8 rd_rows16(const unsigned char* t, int rb, int s, int ch, int lane) {
-  return *(const bf16x8*)(t + swz(rb + (lane & 15), 4 * s + (lane >> 4), ch));
+  return *(const bf16x8*)(t + toff(rb + (lane & 15), 4 * s + (lane >> 4), ch));
 }
 // Transposed A operand of a 16 x 32 step: rows rb + {4 (l/16) + 0..3} and rb + 16 + {..}
 // (the order of two 16-row accumulator tiles), columns 16 ct + l%16.  Lane i of a 16-lane
@@ -123,8 +117,8 @@ __device__ __forceinline__ bf16x8 rd_tr16(const unsigned char* t, int rb, int ct
   const int row = rb + 4 * (lane >> 4) + (lane & 15) / 4;
   const int col = ct * 16 + 4 * (lane & 3);
   const int cc = col >> 3, within = (col & 7) * 2;
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + swz(row, cc, ch) + within));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + swz(row + 16, cc, ch) + within));
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + toff(row, cc, ch) + within));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(t + toff(row + 16, cc, ch) + within));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -435,7 +429,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkv_kernel(BwdParams p) {
           dk2[ct] = mfma16(rd_tr16(tq2, sb * 32, ct, C::KCH, lane), b2, dk2[ct]);
         }
       };
-#pragma unroll 1
+      // unrolled: the second sub-block's operand addresses are the first's plus constants
+#pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
         const int qs0 = qt * kTR + sb * 32;
         if (qs0 >= p.N || (p.causal && qs0 + 31 < kw)) continue;  // wavefront-uniform: nothing visible
