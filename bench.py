@@ -89,6 +89,22 @@ def measured_traffic(path: str, workload: str):
     return entry[workload]
 
 
+# The pages' own throughput figures, carried as context (not a target): model-level
+# tokens/s of a Diff Transformer against a standard Transformer of the same size.
+PAGES_CONTEXT = {
+    "diff_vs_transformer_throughput": [
+        {"source": "Differential Transformer (atlas.scime.ai), Measured effects / Limitations",
+         "figure": "6-12% (elsewhere on the same page 5-12%) lower throughput at 3B scale",
+         "hardware": "not stated"},
+        {"source": "llms.blog, Hardware Implementations and Serving Considerations",
+         "figure": "3B at 4K tokens, forward+backward training: 6,718 vs 7,491 tokens/s (12%); "
+                   "forward prefill: 44,521 vs 48,762 tokens/s (10%); 13B at 2K prefill: 5%",
+         "hardware": "NVIDIA H100"},
+    ],
+    "note": "model-level figures on other hardware; this line measures the attention kernel alone",
+}
+
+
 # ---------------------------------------------------------------------------
 # work accounting (algorithmic; independent of how the kernels execute it)
 # ---------------------------------------------------------------------------
@@ -154,11 +170,25 @@ def _oracle_unit(unit):
     return 1
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, inp, nrows: int):
     """Time the oracle on `nrows` query rows (spread over the sequence) for every (batch, signal head)
     of the workload, one process per core; report F_alg TFLOP/s of that sample."""
     import multiprocessing as mp
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16))
+    visible = len(os.sched_getaffinity(0))
+    # one process per core of the host share one GPU gets (16 cores per GPU on the
+    # MI355X boxes this runs on, whatever the affinity mask shows)
+    cores = max(1, min(visible, 16))
     rows = np.unique(np.linspace(0, w.N - 1, nrows).round().astype(np.int64))
     _CPU.clear()
     _CPU.update({k: inp[k].float().double().numpy() for k in ("q1", "q2", "k1", "k2", "v")})
@@ -174,7 +204,7 @@ def cpu_baseline(w, inp, nrows: int):
     flops = w.B * vis * (w.H_s * 2 * w.d + w.H_n * 2 * w.d + w.H_s * 2 * w.dv)
     _CPU.clear()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "seconds": round(dt, 3),
+            "seconds": round(dt, 3), "cores_visible": visible, "cpu_model": cpu_model(),
             "sample": f"{len(rows)} query rows evenly spaced over [0, {w.N}) x {w.B} batches x {w.H_s} signal heads "
                       f"of {w.name} (fp64 NumPy oracle, one process per core, BLAS 1 thread each); "
                       f"F_alg of the sampled causal pairs / wall time"}
@@ -310,17 +340,52 @@ def bench_decode(w, steps, warmup):
     }
 
 
-def stream_read_probe(nbytes, steps, warmup):
-    """Read rate of the library's plain streaming-read kernel (da_hbm_read_probe) over a
-    buffer of `nbytes`, the size of one decode step's reads: the measured reference beside
-    the published 8 TB/s."""
+PROBE_SRC = os.path.join(ROOT, "bench_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "bench_probe.so")
+_probe = None
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile bench_probe.hip (the streaming-read probe; not part of libdiffattn.so)."""
+    from differential_attention_diff_amd import build as B
+    return B.build_shared(PROBE_SRC, PROBE_LIB, verbose)
+
+
+def probe_lib():
+    global _probe
+    if _probe is None:
+        import ctypes
+        if not os.path.exists(PROBE_LIB):
+            raise RuntimeError(f"{PROBE_LIB} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(PROBE_LIB)
+        L.bench_hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+        L.bench_hbm_read_probe.restype = ctypes.c_int
+        _probe = L
+    return _probe
+
+
+def hbm_read_probe(buf, sink, stream=None):
+    """Read every byte of the device tensor `buf` once with the streaming-read probe;
+    `sink` is a device fp32 tensor (written only with negligible probability)."""
+    import ctypes
     import torch
-    from differential_attention_diff_amd import ops
+    s = torch.cuda.current_stream() if stream is None else stream
+    st = probe_lib().bench_hbm_read_probe(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                          ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(s.cuda_stream))
+    if st != 0:
+        raise RuntimeError(f"bench_hbm_read_probe returned {st}")
+
+
+def stream_read_probe(nbytes, steps, warmup):
+    """Read rate of a plain streaming-read kernel (bench_probe.hip) over a buffer of
+    `nbytes`, the size of one decode step's reads: the measured reference beside the
+    published 8 TB/s."""
+    import torch
     nb = (int(nbytes) + 15) // 16 * 16
     buf = torch.empty(nb, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
     sink = torch.zeros(1, dtype=torch.float32, device="cuda")
-    ms = time_steps(lambda: ops.hbm_read_probe(buf, sink), steps, warmup)
+    ms = time_steps(lambda: hbm_read_probe(buf, sink), steps, warmup)
     del buf
     return {"value": nb / (ms * 1e-3) / 1e9, "unit": "GB/s", "bytes": nb,
             "kernel": "hbm_read_probe_kernel (non-temporal 16-B loads, 4 in flight per thread, 16384 x 256 threads)"}
@@ -395,8 +460,8 @@ def main():
         head = (bench_varlen if w.kind == "varlen" else bench_decode)(w, args.steps, args.warmup)
     extra = []
     if not args.no_extra:
-        for name in ("gda3to1_bf16_n4096", "gda_decode_bf16_b64_l8192", "gda_decode_fp8_b64_l8192",
-                     "gda3to1_varlen_bf16_8x4096"):
+        for name in ("gda3to1_bf16_n4096", "gda4to1_gqa_bf16_n32768", "gda_decode_bf16_b64_l8192",
+                     "gda_decode_fp8_b64_l8192", "gda3to1_varlen_bf16_8x4096"):
             if name == w.name:
                 continue
             ew = W.WORKLOADS[name]
@@ -426,6 +491,7 @@ def main():
     if "roofline_exec" in head:
         line["roofline_exec"] = head["roofline_exec"]
     line["cpu_baseline"] = cpu
+    line["context"] = PAGES_CONTEXT
     line["device"] = device_info()
     line["extra"] = extra
     if args.copy_calibration:

@@ -53,6 +53,21 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def build_shared(src: str, lib: str, verbose: bool = False) -> str:
+    """Compile one HIP source outside the package (a measurement helper) into
+    its own shared library with the same flags; returns the library path."""
+    tmp = lib + ".tmp"
+    cmd = [hipcc()] + COMMON + ["-x", "hip", "-shared", src, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
+        raise RuntimeError(f"hipcc failed on {os.path.basename(src)}:\n{msgs}")
+    os.replace(tmp, lib)
+    return lib
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)

@@ -104,7 +104,9 @@ da_status check_common_shapes(int64_t B, int64_t N, int64_t Hs, int64_t Hn, int6
   if (dv != 2 * d) return fail(DA_EINVAL, "dv (%lld) must equal 2*d (d = %lld)", (long long)dv, (long long)d);
   if (d != 32 && d != 64) return fail(DA_EUNSUPPORTED, "d = %lld: kernels exist for d in {32, 64}", (long long)d);
   if (!isfinite(lam) || !isfinite(lam_init)) return fail(DA_EINVAL, "lambda and lambda_init must be finite");
-  if (!(eps >= 0.0f) || !isfinite(eps)) return fail(DA_EINVAL, "eps must be finite and >= 0");
+  // eps > 0 keeps the head norm finite on rows whose difference is exactly zero
+  // (identical maps with lambda = 1 give o = 0, and 0 / sqrt(0 + eps) = 0)
+  if (!(eps > 0.0f) || !isfinite(eps)) return fail(DA_EINVAL, "eps must be finite and > 0");
   return DA_OK;
 }
 
@@ -114,7 +116,11 @@ struct Packing {
   int64_t nseq, max_seqlen;
 };
 
-constexpr int kMaxGridYZ = 65535;  // grid y/z limit of the fp32 kernel's launch
+constexpr int kMaxGridYZ = 65535;  // grid y/z limit of the fp32 kernel's and the decode's launches
+// bf16 prefill: a tile or query block spans at most 128 rows; their byte offsets
+// from the block's first row (row x stride x 2 + the 256-byte row) stay below 2^32
+constexpr int64_t kMaxTileRows = 128;
+constexpr int64_t kMaxTokenStride = (((int64_t)1 << 32) - 256) / (2 * kMaxTileRows);
 
 da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain, const Packing* pk = nullptr) {
   if (!a) return fail(DA_EINVAL, "args is NULL");
@@ -157,6 +163,14 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain, const Packing
              {"v", a->v, a->s_v, a->H_kv, a->dv},    {"out", a->out, a->s_out, a->H_s, a->dv}};
   for (auto& t : ts)
     if ((st = check_strides(t.name, t.p, t.s, 3, es)) != DA_OK) return st;
+  if (a->dtype == DA_BF16) {
+    // the bf16 kernels address the rows of one tile or query block (at most
+    // kMaxTileRows rows) from a 64-bit base with 32-bit per-lane byte offsets
+    for (int i = 0; i < 5; ++i)
+      if (ts[i].s[1] > kMaxTokenStride)
+        return fail(DA_EUNSUPPORTED, "%s token stride %lld exceeds %lld elements", ts[i].name,
+                    (long long)ts[i].s[1], (long long)kMaxTokenStride);
+  }
   if (a->norm_w && ((uintptr_t)a->norm_w & 3u)) return fail(DA_EINVAL, "norm_w is not 4-byte aligned");
   if (a->lse && ((uintptr_t)a->lse & 3u)) return fail(DA_EINVAL, "lse is not 4-byte aligned");
   if (a->o_maps && !aligned16(a->o_maps)) return fail(DA_EINVAL, "o_maps is not 16-byte aligned");
@@ -271,6 +285,8 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool chec
   if (a->H_s / a->H_n + 1 > kDecodeMaxQueries)
     return fail(DA_EUNSUPPORTED, "gda_decode supports up to %d signal heads per noise head", kDecodeMaxQueries - 1);
   if (a->B == 0) return DA_OK;  // empty batch: nothing is validated further or touched
+  if (a->B > kMaxGridYZ)  // the batch is a grid dimension of both decode kernels
+    return fail(DA_EUNSUPPORTED, "gda_decode takes at most %d sequences per call", kMaxGridYZ);
   // the partial kernel addresses a chunk's rows with 32-bit byte offsets
   if (a->s_k1[2] > kMaxPosStride || a->s_k2[2] > kMaxPosStride || a->s_v[2] > kMaxPosStride)
     return fail(DA_EUNSUPPORTED, "cache position stride exceeds %d elements", kMaxPosStride);
@@ -390,6 +406,42 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool chec
 
 size_t decode_ws_bytes(const da::DecodeParams& p) {
   return (size_t)p.B * p.Hn * p.nchunks * da::decode_ws_floats_per_chunk(p.slots, p.dv) * sizeof(float);
+}
+
+// The decode's outputs (out, and the workspace when given) must not overlap
+// its inputs or each other.
+da_status decode_check_overlap(const da_decode_args* a, const void* ws, size_t ws_bytes) {
+  const bool fp8 = a->cache_dtype == DA_FP8_E4M3;
+  const int ces = fp8 ? 1 : 2;
+  const bool paged = a->block_table != nullptr;
+  auto cache = [&](const void* p, const int64_t* s, int64_t heads, int64_t width) {
+    int64_t dims[3] = {paged ? a->num_blocks : a->B, heads, paged ? a->block_size : a->Lmax};
+    return extent(p, dims, s, 3, width, ces);
+  };
+  int64_t dq1[2] = {a->B, a->H_s}, dq2[2] = {a->B, a->H_n}, dout[2] = {a->B, a->H_s};
+  const Extent in[8] = {extent(a->q1, dq1, a->s_q1, 2, a->d, 2),
+                        extent(a->q2, dq2, a->s_q2, 2, a->d, 2),
+                        cache(a->k1_cache, a->s_k1, a->H_kv, a->d),
+                        cache(a->k2_cache, a->s_k2, a->H_n, a->d),
+                        cache(a->v_cache, a->s_v, a->H_kv, a->dv),
+                        {(uintptr_t)a->seq_lens, (uintptr_t)(a->seq_lens + a->B)},
+                        {(uintptr_t)a->norm_w, (uintptr_t)(a->norm_w ? a->norm_w + a->dv : a->norm_w)},
+                        {(uintptr_t)a->block_table,
+                         (uintptr_t)(paged ? a->block_table + a->B * a->max_blocks : a->block_table)}};
+  const char* names[8] = {"q1", "q2", "k1_cache", "k2_cache", "v_cache", "seq_lens", "norm_w", "block_table"};
+  const Extent eo = extent(a->out, dout, a->s_out, 2, a->dv, 2);
+  const Extent ew{(uintptr_t)ws, (uintptr_t)ws + (ws ? ws_bytes : 0)};
+  for (int i = 0; i < 8; ++i) {
+    if (overlaps(eo, in[i])) return fail(DA_EINVAL, "out overlaps %s", names[i]);
+    if (ws && overlaps(ew, in[i])) return fail(DA_EINVAL, "workspace overlaps %s", names[i]);
+  }
+  if (a->lambda_dev) {
+    const Extent el{(uintptr_t)a->lambda_dev, (uintptr_t)(a->lambda_dev + 1)};
+    if (overlaps(eo, el)) return fail(DA_EINVAL, "out overlaps lambda_dev");
+    if (ws && overlaps(ew, el)) return fail(DA_EINVAL, "workspace overlaps lambda_dev");
+  }
+  if (ws && overlaps(ew, eo)) return fail(DA_EINVAL, "workspace overlaps out");
+  return DA_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -574,6 +626,7 @@ da_status gda_decode(const da_decode_args* args, void* workspace, size_t workspa
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(DA_EWORKSPACE, "workspace needs %zu bytes, got %zu", need, workspace ? workspace_bytes : (size_t)0);
   if (workspace && ((uintptr_t)workspace & 15u)) return fail(DA_EINVAL, "workspace is not 16-byte aligned");
+  if ((st = decode_check_overlap(args, workspace, need)) != DA_OK) return st;
   p.ws = (float*)workspace;
   hipError_t e = da::launch_decode(p, args->dtype, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -649,20 +702,6 @@ da_status da_lambda_reparam_bwd(const float* lq1, const float* lk1, const float*
   hipError_t e = da::launch_lambda_reparam_bwd(lq1, lk1, lq2, lk2, (int)dim, dlambda, dlq1, dlk1, dlq2, dlk2,
                                                (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "lambda backward launch");
-  return DA_OK;
-}
-
-da_status da_hbm_read_probe(const void* src, size_t nbytes, float* sink, void* stream) {
-  if (nbytes == 0) return DA_OK;
-  if (!src || !sink) return fail(DA_EINVAL, "src and sink must be non-NULL");
-  if ((uintptr_t)src % 16 != 0 || nbytes % 16 != 0)
-    return fail(DA_EINVAL, "src must be 16-byte aligned and nbytes a multiple of 16");
-  if ((uintptr_t)sink % 4 != 0) return fail(DA_EINVAL, "sink must be 4-byte aligned");
-  if (nbytes > ((size_t)1 << 40)) return fail(DA_EINVAL, "nbytes above 1 TiB");
-  const Extent es{(uintptr_t)sink, (uintptr_t)sink + sizeof(float)}, ei{(uintptr_t)src, (uintptr_t)src + nbytes};
-  if (overlaps(es, ei)) return fail(DA_EINVAL, "sink overlaps src");
-  hipError_t e = da::launch_hbm_read_probe(src, (int64_t)nbytes, sink, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "read probe launch");
   return DA_OK;
 }
 

@@ -120,7 +120,6 @@ hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_finalize(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_zero(const BwdParams& p, hipStream_t s);  // empty input: dlambda = 0, dw = 0
-hipError_t launch_hbm_read_probe(const void* src, int64_t nbytes, float* sink, hipStream_t s);
 hipError_t launch_lambda_reparam(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int dim,
                                  float lambda_init, float* out, hipStream_t s);
 hipError_t launch_lambda_reparam_bwd(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int dim,

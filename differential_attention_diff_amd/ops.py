@@ -123,8 +123,6 @@ def lib() -> ctypes.CDLL:
         L.da_lambda_reparam.restype = ctypes.c_int
         L.da_lambda_reparam_bwd.argtypes = [_fp, _fp, _fp, _fp, ctypes.c_int64, _fp, _fp, _fp, _fp, _fp, _fp]
         L.da_lambda_reparam_bwd.restype = ctypes.c_int
-        L.da_hbm_read_probe.argtypes = [_fp, ctypes.c_size_t, _fp, _fp]
-        L.da_hbm_read_probe.restype = ctypes.c_int
         L.da_status_str.argtypes = [ctypes.c_int]
         L.da_status_str.restype = ctypes.c_char_p
         L.da_last_error.argtypes = []
@@ -387,16 +385,6 @@ def lambda_from_params(lq1, lk1, lq2, lk2, lambda_init):
     return _LambdaFn.apply(lq1, lk1, lq2, lk2, lambda_init)
 
 
-def hbm_read_probe(buf, sink):
-    """Read every byte of the device tensor `buf` once with the library's streaming-read
-    probe (a measurement helper); `sink` is a device fp32 tensor of at least one element."""
-    if not (buf.is_cuda and sink.is_cuda and sink.dtype == torch.float32 and sink.numel() >= 1):
-        raise ValueError("buf and sink must be device tensors; sink fp32 with at least one element")
-    nbytes = buf.numel() * buf.element_size()
-    _check(lib().da_hbm_read_probe(ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(nbytes),
-                                   ctypes.c_void_p(sink.data_ptr()), _stream(None)))
-
-
 def decode_args(q1, q2, k1c, k2c, vc, seq_lens, out, lam, lam_init, *, eps=1e-5, norm_weight=None, normalize=True,
                 chunk=0, noise_of_signal=None, kv_of_signal=None, cache_scales=None, block_table=None):
     B, hs, d = q1.shape
@@ -451,3 +439,4 @@ def gda_decode(q1, q2, k1c, k2c, vc, seq_lens, lam, lam_init, *, out=None, works
                             _stream(stream)))
     del keep
     return out
+

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define DA_ABI_VERSION 2
+#define DA_ABI_VERSION 3
 #define DA_MAX_HEADS 256
 
 typedef enum {
@@ -289,16 +289,6 @@ da_status da_lambda_reparam(const float* lq1, const float* lk1, const float* lq2
 da_status da_lambda_reparam_bwd(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int64_t dim,
                                 const float* dlambda, float* dlq1, float* dlk1, float* dlq2, float* dlk2,
                                 void* stream);
-
-/* Measurement helper, not part of the method: reads nbytes of device memory at
- * src (16-byte aligned, nbytes a multiple of 16) once with a plain streaming
- * kernel, 16-byte vector loads four deep per thread, and writes nothing except,
- * with negligible probability, 1.0f to sink (device fp32 [1], not overlapping
- * src).  Timing it gives the read bandwidth a simple kernel reaches on the
- * device, the measured reference for the decode's HBM roofline.  DA_OK for
- * nbytes = 0; DA_EINVAL for NULL or misaligned pointers, overlap or nbytes
- * above 1 TiB; DA_EHIP on a launch failure. */
-da_status da_hbm_read_probe(const void* src, size_t nbytes, float* sink, void* stream);
 
 /* Static description of a status code. */
 const char* da_status_str(int status);

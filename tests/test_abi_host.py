@@ -27,13 +27,15 @@ def test_exports_every_declared_symbol(L):
     names = ops.header_functions()
     assert set(names) >= {"diffattn_fwd", "gda_fwd", "gda_fwd_varlen", "gda_bwd", "gda_bwd_workspace_bytes",
                           "gda_decode", "gda_decode_workspace_bytes", "da_lambda_reparam", "da_lambda_reparam_bwd",
-                          "da_status_str", "da_last_error", "da_abi_version", "da_hbm_read_probe"}
+                          "da_status_str", "da_last_error", "da_abi_version"}
     for n in names:
         assert hasattr(L, n), f"libdiffattn.so does not export {n}"
+    # the streaming-read probe is bench tooling, built into its own library
+    assert not hasattr(L, "da_hbm_read_probe")
 
 
 def test_version_and_status_strings(L):
-    assert L.da_abi_version() == 2
+    assert L.da_abi_version() == 3
     for s in range(5):
         assert ops.status_str(s).startswith("DA_")
     assert ops.status_str(99) == "unknown status"
@@ -75,6 +77,10 @@ def call(L, a, entry="gda_fwd"):
     (lambda a: a.s_q1.__setitem__(0, -8), ops.DA_EINVAL, "negative stride"),
     (lambda a: setattr(a, "flags", 8), ops.DA_EINVAL, "flag"),
     (lambda a: setattr(a, "eps", -1.0), ops.DA_EINVAL, "eps"),
+    (lambda a: setattr(a, "eps", 0.0), ops.DA_EINVAL, "eps must be finite and > 0"),
+    # 32-bit per-lane offsets inside a 128-row block: token strides above (2^32 - 256) / 256
+    (lambda a: a.s_k1.__setitem__(1, 16777216), ops.DA_EUNSUPPORTED, "k1 token stride"),
+    (lambda a: a.s_q2.__setitem__(1, 16777216), ops.DA_EUNSUPPORTED, "q2 token stride"),
     (lambda a: setattr(a, "lambda_", float("nan")), ops.DA_EINVAL, "finite"),
     (lambda a: setattr(a, "dtype", 7), ops.DA_EINVAL, "dtype"),
     (lambda a: setattr(a, "out", a.v), ops.DA_EINVAL, "overlaps v"),
@@ -268,8 +274,9 @@ def test_decode_workspace_bytes(L):
     assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 64 * 6 * 8 * 4 * 130 * 4
     a = base_dec(chunk=192)
     assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 0 and "multiple of 128" in ops.last_error()
-    a = base_dec(B=2**31 - 1, L_=2**31 - 1)  # valid on their own, but the workspace size would wrap
-    assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 0 and "2^62" in ops.last_error()
+    # the largest batch and cache the decode accepts still give a representable size
+    a = base_dec(B=65535, L_=2**31 - 1, hs=256, hn=128, hkv=128)
+    assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 65535 * 128 * ((2**31 - 1 + 2047) // 2048) * 3 * 130 * 4
     a = base_dec(chunk=4096)
     assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 0 and "exceeds" in ops.last_error()
 
@@ -347,16 +354,37 @@ def test_decode_workspace_query_ignores_pointers(L):
     assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 64 * 6 * 7 * 4 * 130 * 4  # automatic split: 1280 positions
 
 
-def test_read_probe_validation(L):
+def test_decode_batch_limit_and_overlap(L):
+    a = base_dec(B=70000)  # the batch is a grid dimension of the decode kernels
+    st = L.gda_decode(ctypes.byref(a), None, 0, None)
+    assert st == ops.DA_EUNSUPPORTED and "65535" in ops.last_error()
+    assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 0
+    a = base_dec()
+    need = L.gda_decode_workspace_bytes(ctypes.byref(a))
+    ws = ctypes.c_void_p(FAKE + 7 * 64 * GIB)
+    assert need > 0
+    for field, msg in (("q1", "out overlaps q1"), ("v_cache", "out overlaps v_cache"),
+                       ("seq_lens", "out overlaps seq_lens")):
+        a = base_dec()
+        a.out = getattr(a, field)
+        assert L.gda_decode(ctypes.byref(a), ws, need, None) == ops.DA_EINVAL and msg in ops.last_error()
+    a = base_dec()
+    st = L.gda_decode(ctypes.byref(a), ctypes.c_void_p(a.k2_cache + 4096), need, None)
+    assert st == ops.DA_EINVAL and "workspace overlaps k2_cache" in ops.last_error()
+    st = L.gda_decode(ctypes.byref(a), ctypes.c_void_p(a.out - 256), need, None)
+    assert st == ops.DA_EINVAL and "workspace overlaps out" in ops.last_error()
+
+
+def test_bench_probe_validation():
+    # the benchmark's streaming-read probe (bench_probe.so, not part of libdiffattn.so)
+    import bench
+    if not os.path.exists(bench.PROBE_LIB):
+        bench.build_probe()
+    P = bench.probe_lib()
     f = lambda i: ctypes.c_void_p(FAKE + i * GIB)
-    assert L.da_hbm_read_probe(None, 0, None, None) == ops.DA_OK  # nothing to read: no launch
-    st = L.da_hbm_read_probe(None, 1024, f(1), None)
-    assert st == ops.DA_EINVAL and "non-NULL" in ops.last_error()
-    st = L.da_hbm_read_probe(ctypes.c_void_p(FAKE + 8), 1024, f(1), None)
-    assert st == ops.DA_EINVAL and "aligned" in ops.last_error()
-    st = L.da_hbm_read_probe(f(0), 1000, f(1), None)
-    assert st == ops.DA_EINVAL and "multiple of 16" in ops.last_error()
-    st = L.da_hbm_read_probe(f(0), 1024, ctypes.c_void_p(FAKE + 512), None)
-    assert st == ops.DA_EINVAL and "overlaps" in ops.last_error()
-    st = L.da_hbm_read_probe(f(0), (1 << 40) + 16, f(2000), None)
-    assert st == ops.DA_EINVAL and "1 TiB" in ops.last_error()
+    assert P.bench_hbm_read_probe(None, 0, None, None) == 0  # nothing to read: no launch
+    assert P.bench_hbm_read_probe(None, 1024, f(1), None) == 1
+    assert P.bench_hbm_read_probe(ctypes.c_void_p(FAKE + 8), 1024, f(1), None) == 1
+    assert P.bench_hbm_read_probe(f(0), 1000, f(1), None) == 1
+    assert P.bench_hbm_read_probe(f(0), 1024, ctypes.c_void_p(FAKE + 512), None) == 1
+    assert P.bench_hbm_read_probe(f(0), (1 << 40) + 16, f(2000), None) == 1

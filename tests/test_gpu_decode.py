@@ -200,11 +200,12 @@ def test_paged_caches_equal_contiguous(fp8, block_size):
 
 
 def test_read_probe_reads_and_writes_nothing():
-    # the measurement helper behind the decode lines' streaming-read reference
+    # the benchmark's streaming-read probe behind the decode lines' measured reference
+    import bench
     buf = torch.arange(1 << 18, dtype=torch.int32, device="cuda")  # 1 MiB, words never hit the sink value
     sink = torch.zeros(4, dtype=torch.float32, device="cuda")
-    ops.hbm_read_probe(buf, sink)
-    ops.hbm_read_probe(buf[: (1 << 18) - 4], sink)  # a length that is not a multiple of the grid
+    bench.hbm_read_probe(buf, sink)
+    bench.hbm_read_probe(buf[: (1 << 18) - 4], sink)  # a length that is not a multiple of the grid
     torch.cuda.synchronize()
     assert torch.all(sink == 0)
 

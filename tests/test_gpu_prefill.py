@@ -135,7 +135,10 @@ def test_full_workload_sampled_rows(name):
     w = W.WORKLOADS[name]
     inp = W.make_prefill_inputs(w)
     print(f"[{name}] inputs ready", flush=True)
-    out = run(inp, w.lam, w.lam_init, entry="diff" if w.H_n == w.H_s and w.H_kv == w.H_s else "gda")
+    # completeness: every output element is written (a NaN sentinel must not survive anywhere)
+    out = torch.full((w.B, w.N, w.H_s, w.dv), float("nan"), dtype=torch.bfloat16, device="cuda")
+    run(inp, w.lam, w.lam_init, entry="diff" if w.H_n == w.H_s and w.H_kv == w.H_s else "gda", out=out)
+    assert bool(torch.isfinite(out).all()), f"{name}: some outputs were not written"
     rows = sample_rows(w.N, 12 if w.N > 8192 else 24, seed=w.seed)
     heads = list(range(w.H_s))
     want = O.diff_attention_rows(inp["q1"], inp["q2"], inp["k1"], inp["k2"], inp["v"], w.lam, w.lam_init,
@@ -143,3 +146,18 @@ def test_full_workload_sampled_rows(name):
     got = as64(out[:, rows])
     ma, rel = assert_parity(got, want, "bf16", name)
     print(f"[{name}] {len(rows)} rows x {w.B} x {w.H_s} heads: max-abs {ma:.3e} rel-L2 {rel:.3e}", flush=True)
+
+
+def test_gda3to1_whole_noise_group_element_by_element():
+    # every output of one (batch, noise group) slab of the 3:1 workload -- its three
+    # signal heads over all 4096 queries -- against the oracle, in the bench's launch
+    w = W.WORKLOADS["gda3to1_bf16_n4096"]
+    inp = W.make_prefill_inputs(w)
+    out = run(inp, w.lam, w.lam_init)
+    b, n = 2, 4  # batch 2, noise group 4: signal heads 12, 13, 14
+    heads = [3 * n, 3 * n + 1, 3 * n + 2]
+    want = O.diff_attention_rows(inp["q1"], inp["q2"], inp["k1"], inp["k2"], inp["v"], w.lam, w.lam_init,
+                                 rows=np.arange(w.N), heads=heads, batches=[b], eps=w.eps)
+    got = as64(out[b:b + 1, :, heads[0]:heads[-1] + 1])
+    ma, rel = assert_parity(got, want, "bf16", "3:1 slab")
+    print(f"[gda3to1 slab b={b} group={n}] {w.N} rows x 3 heads: max-abs {ma:.3e} rel-L2 {rel:.3e}", flush=True)
