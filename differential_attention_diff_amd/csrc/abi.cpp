@@ -633,6 +633,31 @@ da_status gda_decode(const da_decode_args* args, void* workspace, size_t workspa
   return DA_OK;
 }
 
+da_status gda_decode_noalloc(const da_decode_args* args, void* stream) {
+  da::DecodeParams p;
+  da_status st = decode_prepare(args, &p, /*check_pointers=*/true);
+  if (st != DA_OK) return st;
+  if (p.B == 0) return DA_OK;
+  const size_t need = decode_ws_bytes(p);
+  if (need > da::kDecodeScratchBytes)
+    return fail(DA_EUNSUPPORTED, "these shapes need %zu bytes of decode partials; the fixed scratch holds %zu",
+                need, (size_t)da::kDecodeScratchBytes);
+  if ((st = decode_check_overlap(args, nullptr, 0)) != DA_OK) return st;
+  // the scratch belongs to the current device: the stream must run on it
+  int dev = -1, sdev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "current device");
+  if (stream) {
+    if ((e = hipStreamGetDevice((hipStream_t)stream, &sdev)) != hipSuccess) return hip_fail(e, "stream device");
+    if (sdev != dev)
+      return fail(DA_EINVAL, "stream runs on device %d, the current device is %d", sdev, dev);
+  }
+  if ((e = da::decode_scratch(&p.ws)) != hipSuccess) return hip_fail(e, "decode scratch address");
+  e = da::launch_decode(p, args->dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return DA_OK;
+}
+
 size_t gda_bwd_workspace_bytes(const da_bwd_args* args) {
   da::BwdParams p;
   if (bwd_prepare(args, &p, /*check_pointers=*/false) != DA_OK) return 0;  // shapes only

@@ -41,6 +41,8 @@
 // order: results are deterministic.
 #include <math.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace da {
@@ -529,7 +531,36 @@ __global__ __launch_bounds__(kT) void decode_combine_kernel(DecodeParams p) {
   }
 }
 
+// Fixed device scratch for the allocation-free decode entry point: the chunk
+// partials live here instead of in a caller workspace.  One copy per GPU, held
+// until the process ends; every call on a GPU shares it and it keeps the last
+// call's contents (the combine reads only the partials the same call wrote, so
+// nothing needs clearing).  In host code `scratch` is only the runtime's handle
+// of the array: its device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
 }  // namespace
+
+hipError_t decode_scratch(float** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {  // first call on this device, with it current
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = (float*)addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t s) {
   (void)dtype;

@@ -115,6 +115,9 @@ constexpr int kBwdPrepBlocks = 8192;  // upper bound of BwdParams::nprep
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t s);
+// device address of the current device's fixed decode scratch (DA_DECODE_SCRATCH_BYTES)
+hipError_t decode_scratch(float** ptr);
+constexpr size_t kDecodeScratchBytes = DA_DECODE_SCRATCH_BYTES;
 hipError_t launch_bwd_prep(const BwdParams& p, int dtype, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s);

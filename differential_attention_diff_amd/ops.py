@@ -118,6 +118,8 @@ def lib() -> ctypes.CDLL:
         L.gda_decode_workspace_bytes.restype = ctypes.c_size_t
         L.gda_decode.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         L.gda_decode.restype = ctypes.c_int
+        L.gda_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.c_void_p]
+        L.gda_decode_noalloc.restype = ctypes.c_int
         _fp = ctypes.c_void_p
         L.da_lambda_reparam.argtypes = [_fp, _fp, _fp, _fp, ctypes.c_int64, ctypes.c_float, _fp, _fp]
         L.da_lambda_reparam.restype = ctypes.c_int
@@ -440,3 +442,12 @@ def gda_decode(q1, q2, k1c, k2c, vc, seq_lens, lam, lam_init, *, out=None, works
     del keep
     return out
 
+
+def gda_decode_noalloc(q1, q2, k1c, k2c, vc, seq_lens, lam, lam_init, *, out, stream=None, **kw):
+    """gda_decode with the partials in the library's fixed per-GPU scratch (no
+    workspace, nothing allocated by the call); `out` must be given.  See
+    include/diffattn.h for the size limit and the one-call-at-a-time rule."""
+    a, keep = decode_args(q1, q2, k1c, k2c, vc, seq_lens, out, lam, lam_init, **kw)
+    _check(lib().gda_decode_noalloc(ctypes.byref(a), _stream(stream)))
+    del keep
+    return out

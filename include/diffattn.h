@@ -271,6 +271,22 @@ size_t gda_decode_workspace_bytes(const da_decode_args* args);
  * head norm.  Returns DA_EWORKSPACE if the workspace is NULL or too small. */
 da_status gda_decode(const da_decode_args* args, void* workspace, size_t workspace_bytes, void* stream);
 
+/* gda_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same kernels and result, with the chunk partials in a fixed device array of
+ * DA_DECODE_SCRATCH_BYTES inside the library instead of a caller workspace.
+ * Nothing is allocated or freed by the call.  One array per GPU, created when
+ * the library is loaded on that GPU and held until the process ends; its
+ * address is looked up on the first call on each device.  The array belongs to
+ * the current device (hipGetDevice): `stream` must run on it (DA_EINVAL
+ * otherwise).  Calls on one GPU share the array, so calls that overlap in time
+ * on one GPU (different streams, or host threads) race and must be serialised
+ * by the caller; consecutive calls on one stream are safe.  Shapes whose
+ * partials exceed the array (gda_decode_workspace_bytes > DA_DECODE_SCRATCH_BYTES)
+ * return DA_EUNSUPPORTED before any HIP call.  Other errors as for gda_decode. */
+#define DA_DECODE_SCRATCH_BYTES (32u << 20)
+da_status gda_decode_noalloc(const da_decode_args* args, void* stream);
+
 /* lambda on the device ([DA-blog] "Learnable Lambda Re-parameterization",
  * lambda equation): lambda_out[0] = exp(lq1 . lk1) - exp(lq2 . lk2) +
  * lambda_init, with lq1, lk1, lq2, lk2 device fp32 vectors of `dim` entries
