@@ -244,8 +244,12 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain, const Packing
   p.sm_scale = (float)(1.0 / sqrt((double)a->d));
   p.sm_scale_log2 = (float)(1.4426950408889634 / sqrt((double)a->d));
 
-  hipError_t e = a->dtype == DA_BF16 ? da::launch_fwd_bf16(p, (hipStream_t)stream)
-                                     : da::launch_fwd_f32(p, (hipStream_t)stream);
+  hipError_t e;
+  if (a->dtype == DA_BF16)
+    e = da::gda3_applies(p) ? da::launch_fwd_gda3_bf16(p, (hipStream_t)stream)
+                            : da::launch_fwd_bf16(p, (hipStream_t)stream);
+  else
+    e = da::launch_fwd_f32(p, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
   return DA_OK;
 }

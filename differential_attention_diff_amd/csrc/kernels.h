@@ -114,6 +114,10 @@ constexpr int kBwdPrepBlocks = 8192;  // upper bound of BwdParams::nprep
 
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s);
+// per-noise-group prefill for three signal heads per noise head on distinct
+// key/value heads (d = 64); gda3_applies says whether a call has that layout
+bool gda3_applies(const FwdParams& p);
+hipError_t launch_fwd_gda3_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t s);
 // device address of the current device's fixed decode scratch (DA_DECODE_SCRATCH_BYTES)
 hipError_t decode_scratch(float** ptr);
