@@ -44,40 +44,26 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 
 # HBM bytes per launch of the dominant kernel (per step of the multi-kernel decode and
 # backward), from rocprofv3 FETCH_SIZE and WRITE_SIZE passes (KiB per dispatch, mean of
-# the workload's 3 calls) scaled by what the same counters read for a plain 1 GiB device
-# copy in the same run (FETCH x 2.0, WRITE x 1.0); see profiles/fwd_bf16_decode_hbm_counters.md.
-# Valid only for the kernel sources the counters were taken on (sha256 of each file);
-# reported as null otherwise.
+# the workload's calls) scaled by what the same counters read for a plain 1 GiB device
+# copy in the same run (FETCH x 2.0, WRITE x 1.0); see the HBM counter summaries under
+# profiles/.  Each entry is valid only for the kernel sources its counters were taken on
+# (sha256 of each file) and is reported as null otherwise.
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "differential_attention_diff_amd", "csrc")
-MEASURED_TRAFFIC = {
-    "prefill": {
-        "sha256": {"fwd_bf16.hip": "0a6937bd55e74110ff675d7491648cf440558541797e1691019c5811cdd4abcc"},
-        "diff3b_bf16_n4096": 147801 * 1024 * 2.0 + 98304 * 1024 * 1.0,
-        "gda3to1_bf16_n4096": 143109 * 1024 * 2.0 + 73729 * 1024 * 1.0,
-        "gda3to1_varlen_bf16_8x4096": 152179 * 1024 * 2.0 + 101300 * 1024 * 1.0,
-    },
-    "decode": {
-        # the split size (abi.cpp) sets how many partials the combine reads
-        "sha256": {"decode_bf16.hip": "4b89d132702106c3594acb3240f54c47c6d6db2e902caaee50c29cf728a93480",
-                   "abi.cpp": "221effc1aa6f9b37382ca73815928a4795cd0b927731c7a3c20a51a123bfd645"},
-        # one step: decode_partial_kernel + decode_combine_kernel
-        "gda_decode_bf16_b64_l8192": (586212 + 2114) * 1024 * 2.0 + (4121 + 288) * 1024 * 1.0,
-        "gda_decode_fp8_b64_l8192": (294331 + 2114) * 1024 * 2.0 + (4119 + 288) * 1024 * 1.0,
-    },
-    "backward": {
-        "sha256": {"bwd_bf16.hip": "2bfa2d4a4e1487a53cb4abd682b355d14ad9fbc7dc14d748f5bd6b5c2a6af1de",
-                   "bwd_rows.hip": "10ca45ddf9f90b87d21211eb16910bcfbd2c6eebd9dc5fe721610504e8190ca7"},
-        # one step: bwd_prep_kernel + bwd_dq_kernel + bwd_dkv_kernel + bwd_finalize_kernel
-        "diff3b_bf16_n4096": (258211 + 200705 + 202339 + 527) * 1024 * 2.0 + (119054 + 98304 + 196613) * 1024 * 1.0,
-        "gda3to1_bf16_n4096": (193677 + 267550 + 468352 + 527) * 1024 * 2.0 + (91396 + 49152 + 122882) * 1024 * 1.0,
-    },
-}
+MEASURED_TRAFFIC = {}
+
+
+def prefill_kernel(w) -> str:
+    """The prefill kernel gda_fwd runs for a workload: the per-noise-group kernel for three
+    signal heads per noise head on distinct key/value heads at d = 64, else the general one."""
+    if w.d == 64 and w.H_s == 3 * w.H_n and w.H_kv == w.H_s:
+        return "fwd_gda3_kernel"
+    return f"fwd_bf16_kernel<{w.d}>"
 
 
 def measured_traffic(path: str, workload: str):
     """Counter-derived HBM bytes per launch (or step), or None if absent or a kernel source changed."""
-    entry = MEASURED_TRAFFIC.get(path)
-    if entry is None or workload not in entry:
+    entry = MEASURED_TRAFFIC.get((path, workload))
+    if entry is None:
         return None
     for source, sha in entry["sha256"].items():
         try:
@@ -86,7 +72,7 @@ def measured_traffic(path: str, workload: str):
                     return None
         except OSError:
             return None
-    return entry[workload]
+    return entry["bytes"]
 
 
 # The pages' own throughput figures, carried as context (not a target): model-level
@@ -248,7 +234,7 @@ def bench_prefill(w, steps, warmup, inp=None):
                    "flop_convention": "F_alg"},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill", w.name),
-                     "flops_per_launch": fa, "kernel": "fwd_bf16_kernel<64>"},
+                     "flops_per_launch": fa, "kernel": prefill_kernel(w)},
         "roofline_exec": {"achieved": ache, "frac": ache / PEAK_BF16_TFLOPS, "flops_per_launch": fe},
         "algorithmic_bytes": prefill_bytes(w),
     }
@@ -276,7 +262,7 @@ def bench_varlen(w, steps, warmup):
                    "causal": True, "entry": "gda_fwd_varlen", "flop_convention": "F_alg"},
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic("prefill", w.name),
-                     "flops_per_launch": fa, "kernel": "fwd_bf16_kernel<64>"},
+                     "flops_per_launch": fa, "kernel": prefill_kernel(w)},
     }
 
 
@@ -306,7 +292,7 @@ def bench_backward(w, steps, warmup):
         "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic("backward", w.name),
                      "flops_per_launch": fb,
-                     "kernel": "bwd_prep + bwd_dq_kernel<64> + bwd_dkv_kernel<64> + bwd_finalize (step time)"},
+                     "kernel": "bwd_prep + bwd_dq_ring_kernel + bwd_dkv_ring_kernel + bwd_finalize (step time)"},
     }
 
 

@@ -545,6 +545,14 @@ da_status bwd_prepare(const da_bwd_args* a, da::BwdParams* p, bool check_pointer
     if ((st = check_strides(t.name, t.p, t.s, 3, es)) != DA_OK) return st;
   for (auto& t : outs)
     if ((st = check_strides(t.name, t.p, t.s, 3, es)) != DA_OK) return st;
+  if (a->dtype == DA_BF16) {
+    // the bf16 passes address the rows of one streamed block from a 64-bit base
+    // with 32-bit per-lane byte offsets (same bound as the prefill's)
+    for (int i = 0; i < 5; ++i)
+      if (ins[i].s[1] > kMaxTokenStride)
+        return fail(DA_EUNSUPPORTED, "%s token stride %lld exceeds %lld elements", ins[i].name,
+                    (long long)ins[i].s[1], (long long)kMaxTokenStride);
+  }
   if (!a->o_maps) return fail(DA_EINVAL, "o_maps is NULL");
   if (!aligned16(a->o_maps)) return fail(DA_EINVAL, "o_maps is not 16-byte aligned");
   if (!a->lse) return fail(DA_EINVAL, "lse is NULL");

@@ -1,6 +1,7 @@
-// bf16 backward score passes for gfx950 (MFMA): dQ1/dQ2 query-major, then
-// dK1/dK2/dV key-major, both recomputing scores and weights from the saved
-// log-sum-exps.
+// bf16 backward score passes for gfx950 (MFMA) at d = 32: dQ1/dQ2
+// query-major, then dK1/dK2/dV key-major, both recomputing scores and weights
+// from the saved log-sum-exps.  (d = 64 runs the LDS-ring passes of
+// bwd_ring_bf16.hip; launch_bwd_bf16 below dispatches.)
 //
 // Gradients of "Differential Attention in Large Language Models: How
 // Denoising Subtraction Eliminates Attention Noise and Outlier Activations"
@@ -453,13 +454,10 @@ hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s) {
   const int64_t nblk = (p.N + kRB - 1) / kRB;
   const int64_t grid = (int64_t)p.B * p.Hn * nblk;
   if (grid > INT32_MAX) return hipErrorInvalidValue;
-  if (p.d == 64) {
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL(bwd_dkv_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
-  } else {
-    hipLaunchKernelGGL(bwd_dq_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL(bwd_dkv_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
-  }
+  if (bwd_ring_applies(p)) return launch_bwd_ring_bf16(p, s);
+  if (p.d != 32) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_dq_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL(bwd_dkv_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

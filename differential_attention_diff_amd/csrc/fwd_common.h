@@ -1,7 +1,8 @@
-// Device helpers shared by the bf16 prefill kernels (fwd_bf16.hip and
-// fwd_gda3_bf16.hip): the global->LDS tile DMA, load-counter waits, the
-// transposed-score row reductions and the block weights of the lazy-reference
-// online softmax.  Internal to the library.
+// Device helpers shared by the bf16 kernels (the prefill in fwd_bf16.hip and
+// fwd_gda3_bf16.hip, the backward in bwd_ring_bf16.hip): the global->LDS tile
+// DMA, load-counter waits, opaque lane offsets, the transposed-score row
+// reductions and the block weights of the lazy-reference online softmax.
+// Internal to the library.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,12 +43,28 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t goff, uint32_t
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(goff), "s"(gbase), "s"(lds)
                : "memory");
 }
+// A per-step lane address made opaque to the compiler, so that the constant
+// parts of the reads that use it (row steps, tensors of a stage) stay in the
+// instructions' offset fields instead of being hoisted into one register each.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void wait_lds_and_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Entry i (wavefront-uniform) of a 4-byte-aligned int16 table in the kernel
+// arguments, through a 4-byte scalar load: a 2-byte element would be fetched
+// by a vector load, which the ring's load-counter waits would then include.
+__device__ __forceinline__ int arg16(const int16_t* table, int i) {
+  const int w = ((const int*)table)[i >> 1];
+  return (int)(int16_t)((i & 1) ? (w >> 16) : w);
 }
 
 // maxima are NaN-propagating (v_maximum3_f32): no operand canonicalisation

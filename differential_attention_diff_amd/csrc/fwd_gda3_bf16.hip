@@ -135,14 +135,6 @@ __device__ __forceinline__ void lane_offsets(Ctx& c, int lane) {
   }
 }
 
-// The per-step lane address is made opaque to the compiler so that the constant
-// parts (16-row and 8-row steps, member tiles) stay in the instruction's offset
-// field instead of being hoisted into one register per read.
-__device__ __forceinline__ uint32_t opaque(uint32_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
 __device__ __forceinline__ void read_k(bf16x8 (&kf)[NKS], const Ctx& c, int t) {
   const uint32_t slot = ((uint32_t)t % kKSlots) * KSTAGE;
 #pragma unroll

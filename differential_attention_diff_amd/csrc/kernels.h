@@ -125,6 +125,10 @@ constexpr size_t kDecodeScratchBytes = DA_DECODE_SCRATCH_BYTES;
 hipError_t launch_bwd_prep(const BwdParams& p, int dtype, hipStream_t s);
 hipError_t launch_bwd_f32(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_bf16(const BwdParams& p, hipStream_t s);
+// the score passes for d = 64 with the streamed side in LDS rings (launch_bwd_bf16 uses
+// them when bwd_ring_applies)
+bool bwd_ring_applies(const BwdParams& p);
+hipError_t launch_bwd_ring_bf16(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_finalize(const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_zero(const BwdParams& p, hipStream_t s);  // empty input: dlambda = 0, dw = 0
 hipError_t launch_lambda_reparam(const float* lq1, const float* lk1, const float* lq2, const float* lk2, int dim,

@@ -207,6 +207,9 @@ def test_bwd_workspace_bytes(L):
     (lambda a: a.s_gv.__setitem__(1, 100), ops.DA_EINVAL, "multiple of 16 bytes"),
     (lambda a: setattr(a, "flags", 4), ops.DA_EINVAL, "flag"),
     (lambda a: (setattr(a, "H_kv", 1)), ops.DA_EUNSUPPORTED, "not one run"),
+    # 32-bit per-lane offsets inside a streamed block (bf16)
+    (lambda a: a.s_v.__setitem__(1, 16777216), ops.DA_EUNSUPPORTED, "v token stride"),
+    (lambda a: a.s_q1.__setitem__(1, 16777216), ops.DA_EUNSUPPORTED, "q1 token stride"),
 ])
 def test_bwd_validation(L, mutate, status, msg):
     a = base_bwd()

@@ -10,13 +10,15 @@ the slice holds every head those gradients sum over).
 
 Bars (the forward's bars do not transfer to gradients, whose scale varies
 with the shape): fp32 max-abs <= 1e-5 max(1, max|ref|); bf16 relative L2
-<= 1e-2 and max-abs <= 4e-2 max|ref| per gradient; a gradient that is exactly
-zero (one visible key) within 1e-5.  The bf16 passes round
-three operands to bf16 on the way to each gradient (do, the weights and dS,
-relative error <= 2^-9 each) on top of bf16 inputs; the relative errors of
-such sums stay near 2^-8.  dlambda is one sum over every row whose terms
-cancel (each row's do . o2 carries the rounding of o = o1 - lambda o2 and of
-the norm's backward): within 1e-2 relative (fp32: 1e-4)."""
+<= 5e-3 and max-abs <= 4e-2 max|ref| per gradient; a gradient that is exactly
+zero (one visible key) within 1e-5.  The bf16 passes round three operands to
+bf16 on the way to each gradient (do, the weights and dS, relative error
+<= 2^-9 each) on top of bf16 inputs: the relative L2 error of such sums is
+about sqrt(3) 2^-9 = 3.4e-3 for independent roundings, and the cases here
+measure 2.6e-3 .. 3.4e-3 (fp32: below 1e-6).  dlambda is one sum over every
+row whose terms cancel (each row's do . o2 carries the rounding of o = o1 -
+lambda o2 and of the norm's backward): within 5e-3 relative (measured up to
+2.9e-3), fp32 within 5e-5 (measured up to 1.1e-5)."""
 
 import numpy as np
 import pytest
@@ -45,7 +47,7 @@ def check_grad(got, want, dtype, what):
     if dtype == "f32":
         assert maxabs <= 1e-5 * max(1.0, scale), f"{what}: fp32 max-abs {maxabs:.3e} (scale {scale:.3e})"
     else:
-        assert rel <= 1e-2 and maxabs <= 4e-2 * scale, \
+        assert rel <= 5e-3 and maxabs <= 4e-2 * scale, \
             f"{what}: bf16 rel-L2 {rel:.3e}, max-abs {maxabs:.3e} (scale {scale:.3e})"
     return maxabs, rel
 
@@ -95,10 +97,13 @@ def test_backward_small_every_element(dtype, shape, causal):
     _, grads, dw = run_fwd_bwd(inp, dout, lam, li, norm_weight=w, want_dw=True, causal=causal)
     want = O.diff_attention_backward(inp["q1"], inp["q2"], inp["k1"], inp["k2"], inp["v"], dout, lam, li,
                                      norm_weight=as64(w), causal=causal)
+    errs = []
     for name, g in zip(NAMES, grads[:5]):
-        check_grad(as64(g), want[name], dtype, f"{name} {dtype} {shape} causal={causal}")
+        errs.append(check_grad(as64(g), want[name], dtype, f"{name} {dtype} {shape} causal={causal}")[1])
     dl = float(grads[5].cpu()[0])
-    assert abs(dl - want["dlambda"]) <= (1e-4 if dtype == "f32" else 1e-2) * max(1.0, abs(want["dlambda"]))
+    dl_err = abs(dl - want["dlambda"]) / max(1.0, abs(want["dlambda"]))
+    print(f"[bwd {dtype} {shape} causal={causal}] max rel-L2 {max(errs):.3e}, dlambda rel {dl_err:.3e}", flush=True)
+    assert dl_err <= (5e-5 if dtype == "f32" else 5e-3)
     check_grad(as64(dw), want["dnorm_weight"], dtype, "dnorm_w")
 
 
@@ -128,7 +133,7 @@ def test_autograd_function(dtype, hkv):
     tag = "f32" if dtype == torch.float32 else "bf16"
     for name, key in zip(NAMES, ("q1", "q2", "k1", "k2", "v")):
         check_grad(as64(d[key].grad), want[name], tag, f"autograd {name}")
-    assert abs(float(lam.grad) - want["dlambda"]) <= (1e-4 if tag == "f32" else 1e-2) * max(1, abs(want["dlambda"]))
+    assert abs(float(lam.grad) - want["dlambda"]) <= (5e-5 if tag == "f32" else 5e-3) * max(1, abs(want["dlambda"]))
     check_grad(as64(w.grad), want["dnorm_weight"], tag, "autograd dw")
 
 
