@@ -126,14 +126,17 @@ __device__ __forceinline__ void store_row16(__bf16* row, const f32x4 (&acc)[NT],
 }
 
 // Work item `logical` of ngroups (batch, noise group) pairs x nblk blocks.
-// The pairs of one XCD's share (xcd_logical hands each XCD a contiguous range)
-// are walked block-major: block 0 of every pair, then block 1, ..., so the
-// longest causal blocks of all the XCD's pairs start first and its workgroups
-// finish together (walking each pair's blocks in turn left the longest blocks
-// of the last pairs to start late: 8-10% longer passes).  blk counts from the
-// first block walked.
+// Clusters of up to four pairs of one XCD's share (xcd_logical hands each XCD
+// a contiguous range) are walked block-major: block 0 of every pair of the
+// cluster, then block 1, ..., so the longest causal blocks start first and
+// the XCD's workgroups finish together (walking each pair's blocks in turn
+// left the longest blocks of an XCD's last pairs to start late: 8-10% longer
+// passes with three grouped pairs per XCD).  Four pairs keep their streamed
+// operands mostly in the XCD's L2: with all twelve pairs of the 24-head
+// layers in one cluster the passes fetched twice the bytes from beyond the
+// L2 and took 1% longer.  blk counts from the first block walked.
 __device__ __forceinline__ void bwd_item(int logical, int ngroups, int nblk, int& grp, int& blk) {
-  const int cl = (ngroups + 7) / 8;
+  const int cl = min((ngroups + 7) / 8, 4);
   const int per = cl * nblk, c = logical / per, idx = logical % per;
   const int cs = min(cl, ngroups - c * cl);  // the last cluster may be smaller
   blk = idx / cs;

@@ -320,29 +320,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gda3_kernel(FwdParams p) {
   const int l32 = lane & 31, hh = lane >> 5;
 
   // ---- work item: XCD-contiguous range, query block fastest (longest first)
-  const int nq = (p.max_seqlen + kQB - 1) / kQB;
-  const int total = p.nseq * p.Hn * nq;
-  const int logical = xcd_logical(blockIdx.x, total);
+  const int N = p.N;
+  const int nq = (N + kQB - 1) / kQB;
+  const int logical = xcd_logical(blockIdx.x, p.B * p.Hn * nq);
   const int qb = nq - 1 - logical % nq;
-  int n, sq;
-  if (p.cu_seqlens) {  // packed sequences: sequence fastest after the query block
-    sq = (logical / nq) % p.nseq;
-    n = logical / nq / p.nseq;
-  } else {
-    n = (logical / nq) % p.Hn;
-    sq = logical / nq / p.Hn;
-  }
-  int b = sq, tok0 = 0, N = p.N;
-  if (p.cu_seqlens) {
-    const int s0 = p.cu_seqlens[sq], s1 = p.cu_seqlens[sq + 1];
-    b = 0;
-    tok0 = min(max(s0, 0), p.N);
-    N = max(min(min(s1, p.N) - tok0, p.max_seqlen), 0);
-  }
+  const int n = (logical / nq) % p.Hn, b = logical / nq / p.Hn;
   const int q0 = qb * kQB;
-  if (q0 >= N) return;  // whole workgroup: no query row of this block exists
   const int qw0 = q0 + qg * kQW;
-  const int64_t t0 = tok0;
 
   const int kend = p.causal ? min(q0 + kQB, N) : N;
   const int nb = (kend + kKT - 1) / kKT;  // 32-key blocks (= tiles) every wavefront walks
@@ -359,10 +343,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gda3_kernel(FwdParams p) {
   int64_t krs;              // element stride of a K row
   if (kt < kG) {
     const int kh = p.kv[p.members[n * kG + kt]];
-    kg = (const char*)((const __bf16*)p.k1 + b * p.sk1[0] + t0 * p.sk1[1] + kh * p.sk1[2]);
+    kg = (const char*)((const __bf16*)p.k1 + b * p.sk1[0] + kh * p.sk1[2]);
     krs = p.sk1[1];
   } else {
-    kg = (const char*)((const __bf16*)p.k2 + b * p.sk2[0] + t0 * p.sk2[1] + n * p.sk2[2]);
+    kg = (const char*)((const __bf16*)p.k2 + b * p.sk2[0] + n * p.sk2[2]);
     krs = p.sk2[1];
   }
   const uint32_t kbs = (uint32_t)krs * 2u;  // bytes per K row
@@ -386,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gda3_kernel(FwdParams p) {
     const int i = VLOADS * wave + t, m = i / 8;
     vkk[t] = i % 8;
     const int vh = p.kv[p.members[n * kG + m]];
-    vg[t] = (const char*)((const __bf16*)p.v + b * p.sv[0] + (t0 + 4 * vkk[t]) * p.sv[1] + vh * p.sv[2]);
+    vg[t] = (const char*)((const __bf16*)p.v + b * p.sv[0] + (4 * vkk[t]) * p.sv[1] + vh * p.sv[2]);
     vdst[t] = (uint32_t)(m * VTILE + vkk[t] * 1024);
   }
   const uint32_t voff = (uint32_t)(lane / 16) * vbs + vch;
@@ -453,10 +437,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gda3_kernel(FwdParams p) {
       const __bf16* qsrc;
       int64_t qrs;
       if (m < kG) {
-        qsrc = (const __bf16*)p.q1 + b * p.sq1[0] + (t0 + q0) * p.sq1[1] + p.members[n * kG + m] * p.sq1[2];
+        qsrc = (const __bf16*)p.q1 + b * p.sq1[0] + q0 * p.sq1[1] + p.members[n * kG + m] * p.sq1[2];
         qrs = p.sq1[1];
       } else {
-        qsrc = (const __bf16*)p.q2 + b * p.sq2[0] + (t0 + q0) * p.sq2[1] + n * p.sq2[2];
+        qsrc = (const __bf16*)p.q2 + b * p.sq2[0] + q0 * p.sq2[1] + n * p.sq2[2];
         qrs = p.sq2[1];
       }
       const int r = kk * 8 + lane / 8;
@@ -554,7 +538,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gda3_kernel(FwdParams p) {
     const int q = qw0 + l32;
     if (p.lse && hh == 0 && q < N) {
       constexpr float kLn2 = 0.69314718055994531f;
-      p.lse[((int64_t)b * p.Hs + h) * p.N + tok0 + q] = (st.m + __log2f(lsum)) * kLn2;
+      p.lse[((int64_t)b * p.Hs + h) * p.N + q] = (st.m + __log2f(lsum)) * kLn2;
     }
     if (qw0 >= N) return;
     const lds_u8* xo = xo_base + (m * 2 * 16 * 64 * 4 + lane * 4);
@@ -564,7 +548,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gda3_kernel(FwdParams p) {
       return cb < 2 ? __fmul_rn(st.o2[cb & 1][r], inv2) : lds_ldf(xo + ((cb - 2) * 16 + r) * 64 * 4);
     };
     if (p.o_maps && q < N) {  // each map's own output, A1 V and A2 V, in fp32
-      float* om1 = p.o_maps + ((((int64_t)b * p.N + tok0 + q) * p.Hs + h) * DV);
+      float* om1 = p.o_maps + ((((int64_t)b * p.N + q) * p.Hs + h) * DV);
       float* om2 = om1 + (int64_t)p.B * p.N * p.Hs * DV;
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
@@ -598,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gda3_kernel(FwdParams p) {
       scale = (1.0f - p.lam_init) / sqrtf(ss * (1.0f / DV) + p.eps);
     }
     if (q < N) {
-      __bf16* out = (__bf16*)p.out + b * p.so[0] + (t0 + q) * p.so[1] + h * p.so[2];
+      __bf16* out = (__bf16*)p.out + b * p.so[0] + q * p.so[1] + h * p.so[2];
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -682,7 +666,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gda3_kernel(FwdParams p) {
       const float v = (st.m + __log2f(lsum)) * kLn2;
 #pragma unroll
       for (int m = 0; m < kG; ++m)
-        p.lse[(int64_t)p.B * p.Hs * p.N + ((int64_t)b * p.Hs + p.members[n * kG + m]) * p.N + tok0 + q] = v;
+        p.lse[(int64_t)p.B * p.Hs * p.N + ((int64_t)b * p.Hs + p.members[n * kG + m]) * p.N + q] = v;
     }
     wait_lds_and_barrier();  // hand-off written
   }
@@ -692,8 +676,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gda3_kernel(FwdParams p) {
 
 // The grouped kernel applies when every noise group has three signal heads on
 // three distinct key/value heads (d = 64); other layouts take fwd_bf16_kernel.
+// Fixed-length batches only: packed sequences of unequal lengths take the
+// general kernel, whose 128-query blocks of every (signal head, sequence)
+// spread each sequence over all XCDs; at this kernel's granularity an XCD's
+// contiguous share held 6 of the 8 sequences of a noise group and the XCDs'
+// work differed by 29% (packed 3:1 workload 0.78 ms here, 0.70 ms there).
 bool gda3_applies(const FwdParams& p) {
-  if (p.d != 64 || p.g != kG) return false;
+  if (p.d != 64 || p.g != kG || p.cu_seqlens) return false;
   for (int n = 0; n < p.Hn; ++n) {
     const int a = p.kv[p.members[n * kG]], b = p.kv[p.members[n * kG + 1]], c = p.kv[p.members[n * kG + 2]];
     if (a == b || a == c || b == c) return false;
@@ -702,8 +691,8 @@ bool gda3_applies(const FwdParams& p) {
 }
 
 hipError_t launch_fwd_gda3_bf16(const FwdParams& p, hipStream_t s) {
-  const int64_t nq = (p.max_seqlen + kQB - 1) / kQB;
-  const int64_t total = (int64_t)p.nseq * p.Hn * nq;
+  const int64_t nq = (p.N + kQB - 1) / kQB;
+  const int64_t total = (int64_t)p.B * p.Hn * nq;
   if (total > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fwd_gda3_kernel, dim3((unsigned)total), dim3(kThreads), 0, s, p);
   return hipGetLastError();

@@ -1,6 +1,7 @@
 """GPU parity of the per-noise-group bf16 prefill (three signal heads per noise
-head, each on its own key/value head: the 3:1 GDA layout), through gda_fwd and
-gda_fwd_varlen, against the fp64 oracle.
+head, each on its own key/value head: the 3:1 GDA layout), through gda_fwd,
+against the fp64 oracle.  (Packed sequences of that layout run the general
+kernel: tests/test_gpu_varlen.py.)
 
 This kernel computes each noise map once per group and hands its weights to
 the signal wavefronts through LDS, so the tests aim at what that hand-off can
@@ -8,7 +9,7 @@ get wrong: ragged query blocks (64 queries) and key tiles (32 keys), several
 groups and explicit head maps, the reference moves of the noise map (published
 with the weights and applied by the other wavefronts), the exact cancellation
 of identical maps (which needs both maps to take identical arithmetic), the
-per-map outputs and LSE the backward reads, and packed sequences.
+per-map outputs and LSE the backward reads.
 
 Pages: "Grouped Differential Attention" (mlsanity.com), "Abstract" (noise heads
 shared GQA-style); "Differential Attention in Large Language Models: How
@@ -16,14 +17,11 @@ Denoising Subtraction Eliminates Attention Noise and Outlier Activations"
 (llms.blog), "Differential Attention Architecture" (DiffAttn equation) and
 "Headwise Normalization" (head_bar_i)."""
 
-import dataclasses
-
 import numpy as np
 import pytest
 import torch
 
 from differential_attention_diff_amd import ops
-from differential_attention_diff_amd import workloads as W
 from oracle import diffattn_oracle as O
 from tests.helpers import as64, assert_parity, norm_scale, rand_inputs, to_dev
 
@@ -121,46 +119,3 @@ def test_both_maps_climbing(causal):
     got = fwd(inp, 0.6, 0.6, causal=causal)
     want = O.diff_attention(inp["q1"], inp["q2"], inp["k1"], inp["k2"], inp["v"], 0.6, 0.6, causal=causal)
     assert_parity(as64(got), want, "bf16", f"gda3 climbing causal={causal}")
-
-
-VW = W.WORKLOADS["gda3to1_varlen_bf16_8x4096"]
-
-
-@pytest.mark.parametrize("causal", [True, False])
-def test_varlen_every_token(causal):
-    w = dataclasses.replace(VW, H_s=6, H_n=2, H_kv=6, seed=56, causal=causal)
-    lengths = [0, 5, 1, 37, 64, 65, 300, 0, 129]
-    inp = W.make_varlen_inputs(w, lengths=[3] + lengths + [4])
-    cu = inp["cu_seqlens"][1:-1].clone()
-    d = {k: inp[k].cuda() for k in ("q1", "q2", "k1", "k2", "v")}
-    T = d["q1"].shape[0]
-    out = torch.full((T, w.H_s, w.dv), 3.0, dtype=torch.bfloat16, device="cuda")
-    lse = torch.full((2, w.H_s, T), -7.0, device="cuda")
-    ops.gda_fwd_varlen(d["q1"], d["q2"], d["k1"], d["k2"], d["v"], cu.cuda(), max(lengths), w.lam, w.lam_init,
-                       out=out, lse=lse, causal=causal)
-    torch.cuda.synchronize()
-    want = O.diff_attention_packed(inp["q1"], inp["q2"], inp["k1"], inp["k2"], inp["v"], cu.numpy(), w.lam,
-                                   w.lam_init, causal=causal)
-    cov = np.zeros(T, bool)
-    for a, b in zip(cu[:-1].tolist(), cu[1:].tolist()):
-        cov[a:b] = True
-    got = as64(out)
-    assert_parity(got[cov], want[cov], "bf16", f"gda3 varlen causal={causal}")
-    assert np.all(got[~cov] == 3.0)
-    want_lse = O.diff_attention_packed_lse(inp["q1"], inp["q2"], inp["k1"], inp["k2"], cu.numpy(), causal=causal)
-    got_lse = as64(lse).transpose(0, 2, 1)
-    assert np.max(np.abs(got_lse[:, cov] - want_lse[:, cov])) <= 2.0 ** -8
-    assert np.all(got_lse[:, ~cov] == -7.0)
-
-
-def test_varlen_equal_lengths_match_batched_bitwise():
-    B, N = 3, 200
-    w = dataclasses.replace(VW, H_s=6, H_n=2, H_kv=6, seed=57)
-    inp = W.make_prefill_inputs(w, B=B, N=N)
-    d = {k: v.cuda() for k, v in inp.items()}
-    batched = ops.gda_fwd(d["q1"], d["q2"], d["k1"], d["k2"], d["v"], w.lam, w.lam_init)
-    flat = {k: v.reshape((B * N,) + v.shape[2:]) for k, v in d.items()}
-    cu = torch.arange(0, B * N + 1, N, dtype=torch.int32, device="cuda")
-    out = ops.gda_fwd_varlen(flat["q1"], flat["q2"], flat["k1"], flat["k2"], flat["v"], cu, N, w.lam, w.lam_init)
-    torch.cuda.synchronize()
-    assert torch.equal(out.reshape(batched.shape), batched)
