@@ -49,7 +49,41 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 # profiles/.  Each entry is valid only for the kernel sources its counters were taken on
 # (sha256 of each file) and is reported as null otherwise.
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "differential_attention_diff_amd", "csrc")
-MEASURED_TRAFFIC = {}
+_PREFILL_SRC = {"fwd_bf16.hip": "0a6937bd55e74110ff675d7491648cf440558541797e1691019c5811cdd4abcc",
+           "fwd_gda3_bf16.hip": "b4b2ccfaa19e97cdbf6ea78d56b51f24e740f6ac27f80068a4e477b1a8248e05",
+           "fwd_common.h": "bb6ae20a6225278b019d48ff544959515d34ac3ce94bf0133686525236becee1"}
+_DECODE_SRC = {"decode_bf16.hip": "c7e9a334551ec5bfb54b0d9ccc36ffbbbe1058d4e5b2908b122b53542a0952b8",
+           "abi.cpp": "c5a30288bf7a67a52f7ddba3a7c46d537e50e1db227319a9acd7a8c3ae5ab5a7"}
+_BACKWARD_SRC = {"bwd_ring_bf16.hip": "b3338ed779f698888144e88b8efcdb0f1357702eead62eb14d5a12ab01bc8ed6",
+           "bwd_rows.hip": "10ca45ddf9f90b87d21211eb16910bcfbd2c6eebd9dc5fe721610504e8190ca7",
+           "fwd_common.h": "bb6ae20a6225278b019d48ff544959515d34ac3ce94bf0133686525236becee1"}
+_KIB = 1024
+
+
+def _hbm(fetch_kib, write_kib):
+    """Calibrated bytes from counter KiB: FETCH x 2.0, WRITE x 1.0."""
+    return (fetch_kib * 2.0 + write_kib) * _KIB
+
+
+MEASURED_TRAFFIC = {
+    # prefill: the one kernel of the step
+    ("prefill", "diff3b_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(148095.6, 98304.0)},
+    ("prefill", "gda3to1_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(114314.4, 73728.0)},
+    ("prefill", "gda4to1_gqa_bf16_n32768"): {"sha256": _PREFILL_SRC, "bytes": _hbm(641679.4, 131072.0)},
+    ("prefill", "gda3to1_varlen_bf16_8x4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(152200.4, 101299.5)},
+    # decode: decode_partial_kernel + decode_combine_kernel
+    ("decode", "gda_decode_bf16_b64_l8192"): {"sha256": _DECODE_SRC,
+                                              "bytes": _hbm(586215.1 + 2114.4, 4121.2 + 288.0)},
+    ("decode", "gda_decode_fp8_b64_l8192"): {"sha256": _DECODE_SRC,
+                                             "bytes": _hbm(294347.8 + 2114.4, 4119.4 + 288.0)},
+    # backward: bwd_prep + bwd_dq_ring + bwd_dkv_ring + bwd_finalize
+    ("backward", "diff3b_bf16_n4096"): {"sha256": _BACKWARD_SRC,
+                                        "bytes": _hbm(258211.2 + 310697.8 + 311940.3 + 526.6,
+                                                      119054.1 + 110590.6 + 245867.1)},
+    ("backward", "gda3to1_bf16_n4096"): {"sha256": _BACKWARD_SRC,
+                                         "bytes": _hbm(193673.1 + 466092.4 + 660189.1 + 526.6,
+                                                       91395.7 + 52227.2 + 135181.7)},
+}
 
 
 def prefill_kernel(w) -> str:
