@@ -86,11 +86,26 @@ MEASURED_TRAFFIC = {
 }
 
 
+def shared_combo_size(w) -> int:
+    """Heads per (noise head, key/value head) combo under the default head maps (0: not uniform)."""
+    g, gk = w.H_s // w.H_n, w.H_s // w.H_kv
+    combos = {}
+    for h in range(w.H_s):
+        combos[(h // g, h // gk)] = combos.get((h // g, h // gk), 0) + 1
+    sizes = set(combos.values())
+    return sizes.pop() if len(sizes) == 1 else 0
+
+
 def prefill_kernel(w) -> str:
-    """The prefill kernel gda_fwd runs for a workload: the per-noise-group kernel for three
-    signal heads per noise head on distinct key/value heads at d = 64, else the general one."""
-    if w.d == 64 and w.H_s == 3 * w.H_n and w.H_kv == w.H_s:
-        return "fwd_gda3_kernel"
+    """The prefill kernels gda_fwd runs for a fixed-length workload at d = 64: the map-2 and
+    map-1 launches for combos of 2, 4 or 8 signal heads on one noise and one key/value head,
+    the per-noise-group kernel for three signal heads per noise head on distinct key/value
+    heads, else the general kernel (always for packed sequences and d = 32)."""
+    if w.d == 64 and w.kind != "varlen":
+        if shared_combo_size(w) in (2, 4, 8):
+            return "fwd_shared_kernel<64, false> + fwd_shared_kernel<64, true> (step time)"
+        if w.H_s == 3 * w.H_n and w.H_kv == w.H_s:
+            return "fwd_gda3_kernel"
     return f"fwd_bf16_kernel<{w.d}>"
 
 

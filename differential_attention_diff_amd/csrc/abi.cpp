@@ -246,8 +246,9 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain, const Packing
 
   hipError_t e;
   if (a->dtype == DA_BF16)
-    e = da::gda3_applies(p) ? da::launch_fwd_gda3_bf16(p, (hipStream_t)stream)
-                            : da::launch_fwd_bf16(p, (hipStream_t)stream);
+    e = da::shared_kv_plan(p)    ? da::launch_fwd_shared_bf16(p, (hipStream_t)stream)
+        : da::gda3_applies(p)    ? da::launch_fwd_gda3_bf16(p, (hipStream_t)stream)
+                                 : da::launch_fwd_bf16(p, (hipStream_t)stream);
   else
     e = da::launch_fwd_f32(p, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill launch");

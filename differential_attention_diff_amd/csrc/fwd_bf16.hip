@@ -109,6 +109,14 @@ struct Cfg {
   static_assert(kGroups * kQW * DV * 4 <= 2 * STAGE, "O2 hand-off fits in two ring slots");
 };
 
+// A ring slot: NK key tiles (K1 and K2 for the general kernel, one map's keys
+// for the shared-value kernels) followed by the V tile.
+template <int D, int NK>
+struct Lay {
+  static constexpr int VOFF = NK * Cfg<D>::KBYTES;
+  static constexpr int STAGE = VOFF + Cfg<D>::VBYTES;
+};
+
 // LDS byte offset of 16-B chunk c of row r (XOR swizzle).  K (and Q): chunk ^
 // ((r >> KSH) mod 8) -- an MFMA operand read takes one chunk of 16 consecutive
 // rows per 16 lanes, and with rows of 128 B (two per 256-B bank window) the
@@ -196,16 +204,16 @@ struct Ctx {
   float sc;     // log2(e)/sqrt(d)
 };
 
-template <int D>
+template <int D, int NK>
 __device__ __forceinline__ const unsigned char* slot_of(const Ctx& c, int tile) {
-  return c.ring + (tile % kSlots) * Cfg<D>::STAGE;
+  return c.ring + (tile % kSlots) * Lay<D, NK>::STAGE;
 }
 
 // K operands of block jj: A operand of S^T = K Q^T, lane (k, half) holds
 // K[k][16 s + 8 half + 0..7].
-template <int D>
+template <int D, int NK>
 __device__ __forceinline__ void read_k(bf16x8 (&kf)[Cfg<D>::NKS], const Ctx& c, int jj) {
-  const unsigned char* t = slot_of<D>(c, jj >> 1) + c.koff;
+  const unsigned char* t = slot_of<D, NK>(c, jj >> 1) + c.koff;
   const int kr = (jj & 1) * kKB + c.l32;
 #pragma unroll
   for (int s = 0; s < Cfg<D>::NKS; ++s) kf[s] = *(const bf16x8*)(t + k_off<D>(kr, 2 * s + c.hh));
@@ -214,10 +222,10 @@ __device__ __forceinline__ void read_k(bf16x8 (&kf)[Cfg<D>::NKS], const Ctx& c, 
 // V^T operands of block jj (32 channels x 16 keys per (cb, ks)): lane j of a
 // 16-lane group reads row (4 half + j/4) at channels c0 + 4 (j%4); the
 // transposing read hands lane i the 4 keys of channel c0 + i.
-template <int D>
+template <int D, int NK>
 __device__ __forceinline__ void read_v(St<D>& st, const Ctx& c, int jj) {
   using C = Cfg<D>;
-  const unsigned char* vs = slot_of<D>(c, jj >> 1) + 2 * C::KBYTES;
+  const unsigned char* vs = slot_of<D, NK>(c, jj >> 1) + Lay<D, NK>::VOFF;
   const int r0 = (jj & 1) * kKB + (c.vt_lane >> 8);
 #pragma unroll
   for (int cb = 0; cb < C::NCB; ++cb)
@@ -305,16 +313,16 @@ __device__ __forceinline__ void step_schedule() {
 // block j - 1, softmax of block j, LDS reads of K(j + 2) and V(j).  Past the
 // last block the score products and K reads work on stale ring data and their
 // results are never used; before the first block P(-1) and V(-1) are zero.
-template <int D, int PAR, bool MASK>
+template <int D, int NK, int PAR, bool MASK>
 __device__ __forceinline__ void step(St<D>& st, const Ctx& c, int j) {
   constexpr int NCB = Cfg<D>::NCB;
   st.s[PAR ^ 1] = score_products<D>(st.kf, st.qf);
-  read_k<D>(st.kf, c, j + 2);
+  read_k<D, NK>(st.kf, c, j + 2);
   pv_products<D, PAR ^ 1>(st);
   f32x16 sj = st.s[PAR];
   if (MASK) mask_scores(sj, j * kKB, c);
   float sum = block_weights(sj, c.sc, st.m, st.p[PAR][0], st.p[PAR][1]);
-  read_v<D>(st, c, j);
+  read_v<D, NK>(st, c, j);
   step_schedule<D>();
   // keep the weights in this block (they would otherwise sink past the branch below)
   asm volatile("" ::"v"(st.p[PAR][0]), "v"(st.p[PAR][1]), "v"(sum));
@@ -325,7 +333,7 @@ __device__ __forceinline__ void step(St<D>& st, const Ctx& c, int j) {
   if (__builtin_amdgcn_ballot_w64(!(sum <= kSumLimit))) {
     asm volatile("" ::: "memory");  // re-read the K operands from LDS
     bf16x8 kj[Cfg<D>::NKS];
-    read_k<D>(kj, c, j);
+    read_k<D, NK>(kj, c, j);
     f32x16 s = score_products<D>(kj, st.qf);
     if (MASK) mask_scores(s, j * kKB, c);
     const float mu = vmax(st.m, half_swap_max(max16(s)) * c.sc);
@@ -514,9 +522,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   st.p[1][0] = st.p[1][1] = bf16x8{};
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) st.vf[cb][0] = st.vf[cb][1] = bf16x8{};
-  read_k<D>(st.kf, c, 0);
+  read_k<D, 2>(st.kf, c, 0);
   st.s[0] = score_products<D>(st.kf, st.qf);
-  read_k<D>(st.kf, c, 1);
+  read_k<D, 2>(st.kf, c, 1);
 
   // ---- the pipeline; tile t's sync precedes block 2t.  Blocks before this
   // wavefront's first masked block run unmasked; every wavefront runs the same
@@ -525,12 +533,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   int j = 0;
   for (; j + 1 < jm; j += 2) {
     tile_sync(j >> 1);
-    step<D, 0, false>(st, c, j);
-    step<D, 1, false>(st, c, j + 1);
+    step<D, 2, 0, false>(st, c, j);
+    step<D, 2, 1, false>(st, c, j + 1);
   }
   if (j < jm) {  // jm odd: one more unmasked (even) block
     tile_sync(j >> 1);
-    step<D, 0, false>(st, c, j);
+    step<D, 2, 0, false>(st, c, j);
     ++j;
   }
   // the masked blocks recompute the lane constants from an opaque lane index, so
@@ -545,13 +553,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
     cm.kmax = p.causal ? qw0 + cm.l32 : N - 1;
   }
   if ((j & 1) && j < nb) {  // first masked block is odd
-    step<D, 1, true>(st, cm, j);
+    step<D, 2, 1, true>(st, cm, j);
     ++j;
   }
   for (; j < nb; j += 2) {
     tile_sync(j >> 1);
-    step<D, 0, true>(st, cm, j);
-    if (j + 1 < nb) step<D, 1, true>(st, cm, j + 1);
+    step<D, 2, 0, true>(st, cm, j);
+    if (j + 1 < nb) step<D, 2, 1, true>(st, cm, j + 1);
   }
   // drain: P(nb-1) V(nb-1)
   if ((nb - 1) & 1)
@@ -638,6 +646,301 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   }
 }
 
+// ---- layers whose signal heads share noise and key/value heads
+//
+// Signal heads with the same noise head and the same key/value head (a
+// "combo": with GQA key/value heads under GDA noise heads, e.g. 16 signal, 4
+// noise and 8 key/value heads, each noise group holds two combos of two) have
+// the same map 2 output softmax(Q2 K2^T/sqrt(d)) V ("Grouped Differential
+// Attention" (mlsanity.com), "Abstract": noise heads shared GQA-style), so A2 V
+// is one product per combo, and the combo's members share their K1 and V
+// tiles.  Two launches:
+//   * the noise kernel (SIG = false): a workgroup owns 256 queries (8 query
+//     groups of 32, one wavefront each) of one (batch, combo) and forms
+//     A2 V / l2 in fp32.  With no workspace in the prefill's arguments, it
+//     parks these rows in the combo's own output rows: channels 0-63 in the
+//     bf16 row of its first member, 64-127 in its second's (256 bytes each);
+//     it also writes each member's map-2 LSE and A2 V when asked.
+//   * the signal kernel (SIG = true): a workgroup owns 256 / gs queries of one
+//     (batch, combo of gs heads) and runs one wavefront per (member, query
+//     group of 32); every K1 and V tile in LDS serves all members.  Its epilogue reads
+//     the parked A2 V rows of its queries into registers, meets the other
+//     wavefronts at a barrier (so no parked row is overwritten before every
+//     wavefront has read it) and then forms o = A1 V - lambda A2 V, the head
+//     norm and the stores, in the same operations as the general kernel.
+// The pipeline, the ring (four slots of one K tile and the V tile, filled by
+// DMA: each wavefront loads one KiB of K and two of V per tile) and the block
+// walk are the general kernel's; only the wavefront-to-work map differs.
+constexpr int kSharedRows = 256;  // Q rows staged per workgroup (either kernel)
+
+template <int D, bool SIG>
+__global__ __launch_bounds__(kThreads, 1) void fwd_shared_kernel(FwdParams p) {
+  using C = Cfg<D>;
+  using Lo = Lay<D, 1>;
+  constexpr int DV = C::DV, NCB = C::NCB, NKS = C::NKS;
+  static_assert(D == 64, "one K KiB and two V KiB per wavefront and tile");
+  static_assert(kKT * C::KROW == kWaves * 1024 && kKT * C::VROW == 2 * kWaves * 1024, "tile split over waves");
+  constexpr int QREG = kSharedRows * C::KROW;  // staged Q rows
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kSlots * Lo::STAGE + QREG];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int g = p.gs;                        // heads per combo: 2, 4 or 8 (host-checked)
+  const int qpw = SIG ? kSharedRows / g : kSharedRows;  // queries per workgroup
+  const int mi = SIG ? wave % g : 0;         // this wavefront's member (signal kernel)
+  const int qg = SIG ? wave / g : wave;      // its query group
+
+  // ---- work item: XCD-contiguous ranges, (batch, combo) pairs in turn, each
+  // pair's query blocks longest first
+  const int N = p.N;
+  const int nq = (N + qpw - 1) / qpw;
+  const int total = p.B * p.ncombo * nq;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, q8 = total >> 3, r8 = total & 7;
+  const int logical = xcd * q8 + min(xcd, r8) + (bid >> 3);
+  const int qb = nq - 1 - logical % nq;
+  const int cmb = (logical / nq) % p.ncombo;
+  const int b = logical / nq / p.ncombo;
+  const int m0 = __builtin_amdgcn_readfirstlane(p.cmem[cmb * g]);
+  const int m1 = __builtin_amdgcn_readfirstlane(p.cmem[cmb * g + 1]);
+  const int n = __builtin_amdgcn_readfirstlane(p.nz[m0]);
+  const int kh = __builtin_amdgcn_readfirstlane(p.kv[m0]);
+  const int q0 = qb * qpw;  // < N
+  const int qw0 = q0 + qg * kQW;
+
+  const __bf16* K = SIG ? (const __bf16*)p.k1 + b * p.sk1[0] + kh * p.sk1[2]
+                        : (const __bf16*)p.k2 + b * p.sk2[0] + n * p.sk2[2];
+  const __bf16* V = (const __bf16*)p.v + b * p.sv[0] + kh * p.sv[2];
+  const int64_t krow = SIG ? p.sk1[1] : p.sk2[1], vrow = p.sv[1];  // element strides of a token
+  const uint32_t krs = (uint32_t)krow * 2u, vrs = (uint32_t)vrow * 2u;
+
+  const int kend = p.causal ? min(q0 + qpw, N) : N;
+  const int nb = (kend + kKB - 1) / kKB;
+  const int ntiles = (nb + 1) / 2;
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_u8*)ring;
+
+  // ---- tile DMA: wave w loads K rows [8 w, 8 w + 8) (one KiB) and V rows
+  // [8 w, 8 w + 8) (two KiB) of the 64-key tile.  The lane's global chunk
+  // implements the swizzle of k_off / v_off; rows past N re-read row N - 1.
+  const int lrk = lane >> 3, lrv = lane >> 4;
+  const uint32_t kch = (uint32_t)(((lane & 7) ^ (((8 * wave + lrk) >> 1) & 7)) << 4);
+  const uint32_t vch = (uint32_t)(((lane & 15) ^ (lrv << 2)) << 4);
+  const uint32_t kl = (uint32_t)(8 * wave + lrk) * krs + kch;
+  const uint32_t vl = (uint32_t)(8 * wave + lrv) * vrs + vch;
+  auto issue_tile = [&](int tile) {
+    const uint32_t dst = ring_lds + (tile % kSlots) * Lo::STAGE;
+    const int key0 = tile * kKT;  // < N for every tile issued
+    const char* gk = (const char*)(K + (int64_t)key0 * krow);
+    const char* gv = (const char*)(V + (int64_t)key0 * vrow);
+    if (key0 + kKT <= N) {
+      dma16(gk, kl, dst + wave * 1024);
+      dma16(gv, vl, dst + Lo::VOFF + 2 * wave * 1024);
+      dma16(gv, vl + 4 * vrs, dst + Lo::VOFF + (2 * wave + 1) * 1024);
+    } else {
+      const int lim = N - 1 - key0;
+      dma16(gk, (uint32_t)min(8 * wave + lrk, lim) * krs + kch, dst + wave * 1024);
+      dma16(gv, (uint32_t)min(8 * wave + lrv, lim) * vrs + vch, dst + Lo::VOFF + 2 * wave * 1024);
+      dma16(gv, (uint32_t)min(8 * wave + 4 + lrv, lim) * vrs + vch, dst + Lo::VOFF + (2 * wave + 1) * 1024);
+    }
+  };
+  constexpr int TL = 3;  // DMA instructions per wave and tile
+  auto tile_sync = [&](int tt) {
+    if (tt + 1 >= ntiles) return;
+    wait_tiles_in_flight<TL>(min(kSlots - 3, ntiles - tt - 2));
+    wait_lds_and_barrier();
+    if (tt + kSlots - 1 < ntiles) issue_tile(tt + kSlots - 1);
+  };
+
+  // ---- prologue: the workgroup's Q rows after the ring (row r: signal kernel
+  // member r / qpw at query q0 + r % qpw; noise kernel query q0 + r), wave w
+  // loading rows [32 w, 32 w + 32); then tiles 0..kSlots-2
+  {
+    const int r0 = kQW * wave;
+    const int src_m = SIG ? r0 / qpw : 0, qo = SIG ? r0 % qpw : r0;
+    const int hq = __builtin_amdgcn_readfirstlane(SIG ? p.cmem[cmb * g + src_m] : n);
+    const __bf16* qsrc = SIG ? (const __bf16*)p.q1 + b * p.sq1[0] + hq * p.sq1[2]
+                             : (const __bf16*)p.q2 + b * p.sq2[0] + hq * p.sq2[2];
+    const int64_t qrow = SIG ? p.sq1[1] : p.sq2[1];
+    const uint32_t qrs = (uint32_t)qrow * 2u;
+    const int qfirst = min(q0 + qo, N - 1), lim = N - 1 - qfirst;  // rows past N re-read row N - 1
+    const char* gq = (const char*)(qsrc + (int64_t)qfirst * qrow);
+    const uint32_t qdst = ring_lds + kSlots * Lo::STAGE + r0 * C::KROW;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // rows r0 + 8 i + lrk: swizzle term ((8 i + lrk) >> 1) & 7, r0 a multiple of 32
+      const uint32_t ch = (uint32_t)(((lane & 7) ^ ((4 * (i & 1)) | (lrk >> 1))) << 4);
+      dma16(gq, (uint32_t)min(8 * i + lrk, lim) * qrs + ch, qdst + i * 1024);
+    }
+  }
+  for (int tt = 0; tt < min(ntiles, kSlots - 1); ++tt) issue_tile(tt);
+  wait_tiles_in_flight<TL>(min(ntiles, kSlots - 1) - 1);  // the Q rows and tile 0 have landed
+  wait_lds_and_barrier();
+
+  Ctx c;
+  c.ring = ring;
+  c.koff = 0;
+  c.l32 = l32;
+  c.hh = hh;
+  c.vt_lane = ((4 * hh + (lane & 15) / 4) << 8) | (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  c.kmax = p.causal ? qw0 + l32 : N - 1;
+  c.jmask = p.causal ? qw0 / kKB : N / kKB;
+  c.sc = p.sm_scale_log2;
+
+  St<D> st;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) st.o[cb] = f32x16{};
+  st.m = -1e30f;
+  st.l = 0.f;
+  {
+    const unsigned char* qs = ring + kSlots * Lo::STAGE;
+    const int qr = mi * qpw + qg * kQW + l32;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) st.qf[s] = *(const bf16x8*)(qs + k_off<D>(qr, 2 * s + hh));
+  }
+  st.p[1][0] = st.p[1][1] = bf16x8{};
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) st.vf[cb][0] = st.vf[cb][1] = bf16x8{};
+  read_k<D, 1>(st.kf, c, 0);
+  st.s[0] = score_products<D>(st.kf, st.qf);
+  read_k<D, 1>(st.kf, c, 1);
+
+  const int jm = min(c.jmask, nb);
+  int j = 0;
+  for (; j + 1 < jm; j += 2) {
+    tile_sync(j >> 1);
+    step<D, 1, 0, false>(st, c, j);
+    step<D, 1, 1, false>(st, c, j + 1);
+  }
+  if (j < jm) {
+    tile_sync(j >> 1);
+    step<D, 1, 0, false>(st, c, j);
+    ++j;
+  }
+  Ctx cm = c;
+  {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    cm.l32 = ln & 31;
+    cm.hh = ln >> 5;
+    cm.vt_lane = ((4 * cm.hh + (ln & 15) / 4) << 8) | (16 * ((ln >> 4) & 1) + 4 * (ln & 3));
+    cm.kmax = p.causal ? qw0 + cm.l32 : N - 1;
+  }
+  if ((j & 1) && j < nb) {
+    step<D, 1, 1, true>(st, cm, j);
+    ++j;
+  }
+  for (; j < nb; j += 2) {
+    tile_sync(j >> 1);
+    step<D, 1, 0, true>(st, cm, j);
+    if (j + 1 < nb) step<D, 1, 1, true>(st, cm, j + 1);
+  }
+  if ((nb - 1) & 1)
+    pv_products<D, 1>(st);
+  else
+    pv_products<D, 0>(st);
+
+  // ---- epilogue
+  const float lsum = half_swap_sum(st.l);
+  const float inv = 1.0f / lsum;
+  const int q = qw0 + l32;
+  constexpr float kLn2 = 0.69314718055994531f;
+  const int64_t orow = (int64_t)b * p.so[0] + (int64_t)q * p.so[1];  // + head * so[2]: a bf16 output row
+  if (!SIG) {
+    if (q < N) {
+      const float lse = (st.m + __log2f(lsum)) * kLn2;
+      float* par0 = (float*)((__bf16*)p.out + orow + m0 * p.so[2]);  // channels 0-63
+      float* par1 = (float*)((__bf16*)p.out + orow + m1 * p.so[2]);  // channels 64-127
+      for (int i = 0; i < g; ++i) {
+        const int h = p.cmem[cmb * g + i];
+        if (p.lse && hh == 0) p.lse[(int64_t)p.B * p.Hs * p.N + ((int64_t)b * p.Hs + h) * p.N + q] = lse;
+      }
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int ch = cb * 32 + 8 * g4 + 4 * hh;
+          f32x4 z;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) z[e] = __fmul_rn(st.o[cb][4 * g4 + e], inv);
+          *(f32x4*)(ch < DV / 2 ? par0 + ch : par1 + (ch - DV / 2)) = z;
+          if (p.o_maps)
+            for (int i = 0; i < g; ++i) {
+              const int h = p.cmem[cmb * g + i];
+              float* om2 = p.o_maps + (int64_t)p.B * p.N * p.Hs * DV + (((int64_t)b * p.N + q) * p.Hs + h) * DV;
+              *(f32x4*)(om2 + ch) = z;
+            }
+        }
+    }
+    return;
+  }
+
+  const int h = __builtin_amdgcn_readfirstlane(p.cmem[cmb * g + mi]);
+  if (p.lse && hh == 0 && q < N)
+    p.lse[((int64_t)b * p.Hs + h) * p.N + q] = (st.m + __log2f(lsum)) * kLn2;
+  // the parked A2 V / l2 of this lane's query and channels
+  f32x4 z[NCB][4];
+  if (q < N) {
+    const float* par0 = (const float*)((const __bf16*)p.out + orow + m0 * p.so[2]);
+    const float* par1 = (const float*)((const __bf16*)p.out + orow + m1 * p.so[2]);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int ch = cb * 32 + 8 * g4 + 4 * hh;
+        z[cb][g4] = *(const f32x4*)(ch < DV / 2 ? par0 + ch : par1 + (ch - DV / 2));
+      }
+  }
+  // every parked row of the workgroup's queries has been read (the loads have
+  // returned) before any wavefront stores an output row
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (q >= N) return;
+
+  if (p.o_maps) {
+    float* om1 = p.o_maps + (((int64_t)b * p.N + q) * p.Hs + h) * DV;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = __fmul_rn(st.o[cb][4 * g4 + e], inv);
+        *(f32x4*)(om1 + cb * 32 + 8 * g4 + 4 * hh) = a;
+      }
+  }
+  const float lam = lambda_of(p.lam_dev, p.lam);
+  float ss = 0.f;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x = __builtin_fmaf(-lam, z[cb][r / 4][r % 4], __fmul_rn(st.o[cb][r], inv));
+      st.o[cb][r] = x;
+      ss = __builtin_fmaf(x, x, ss);
+    }
+  float scale = 1.0f;
+  if (p.normalize) {
+    ss = half_swap_sum(ss);
+    scale = (1.0f - p.lam_init) / sqrtf(ss * (1.0f / DV) + p.eps);
+  }
+  __bf16* out = (__bf16*)p.out + orow + h * p.so[2];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int ch = cb * 32 + 8 * g4 + 4 * hh;
+      f32x4 wv = {1.f, 1.f, 1.f, 1.f};
+      if (p.normalize && p.norm_w) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wv[e] = p.norm_w[ch + e];
+      }
+      f32x4 y = {st.o[cb][4 * g4] * scale * wv[0], st.o[cb][4 * g4 + 1] * scale * wv[1],
+                 st.o[cb][4 * g4 + 2] * scale * wv[2], st.o[cb][4 * g4 + 3] * scale * wv[3]};
+      *(bf16x4*)(out + ch) = __builtin_convertvector(y, bf16x4);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s) {
@@ -648,6 +951,50 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s) {
     hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((unsigned)total), dim3(kThreads), 0, s, p);
   else
     hipLaunchKernelGGL(fwd_bf16_kernel<32>, dim3((unsigned)total), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+bool shared_kv_plan(FwdParams& p) {
+  if (p.d != 64 || p.cu_seqlens) return false;
+  // combos in noise-group order (the combos of a noise group share its K2 in L2),
+  // members in head order; every combo must hold the same number of heads
+  int gs = 0, nc = 0, fill = 0;
+  bool used[DA_MAX_HEADS] = {};
+  for (int i = 0; i < p.Hn * p.g; ++i) {
+    const int h0 = p.members[i];
+    if (used[h0]) continue;
+    int cnt = 0;
+    for (int j = i; j < (i / p.g + 1) * p.g; ++j) {  // the rest of i's noise group
+      const int h = p.members[j];
+      if (!used[h] && p.kv[h] == p.kv[h0]) {
+        used[h] = true;
+        p.cmem[fill++] = (int16_t)h;
+        ++cnt;
+      }
+    }
+    if (gs == 0) gs = cnt;
+    if (cnt != gs) return false;
+    ++nc;
+  }
+  if (!(gs == 2 || gs == 4 || gs == 8)) return false;
+  // A2 V is parked in the output rows of each combo's first two members, so the
+  // output's (batch, token, head) rows must not overlap: nested row-major strides
+  const int64_t dv = p.dv;
+  if (p.so[2] < dv || p.so[1] < (int64_t)(p.Hs - 1) * p.so[2] + dv) return false;
+  if (p.B > 1 && p.so[0] < (int64_t)(p.N - 1) * p.so[1] + (int64_t)(p.Hs - 1) * p.so[2] + dv) return false;
+  p.gs = gs;
+  p.ncombo = nc;
+  return true;
+}
+
+hipError_t launch_fwd_shared_bf16(const FwdParams& p, hipStream_t s) {
+  const int64_t pairs = (int64_t)p.B * p.ncombo;
+  const int64_t noise = pairs * ((p.N + kSharedRows - 1) / kSharedRows);
+  const int qs = kSharedRows / p.gs;
+  const int64_t sig = pairs * ((p.N + qs - 1) / qs);
+  if (sig > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fwd_shared_kernel<64, false>), dim3((unsigned)noise), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((fwd_shared_kernel<64, true>), dim3((unsigned)sig), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

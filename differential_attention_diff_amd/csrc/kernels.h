@@ -35,6 +35,10 @@ struct FwdParams {
   int16_t nz[DA_MAX_HEADS];      // signal head -> noise head
   int16_t kv[DA_MAX_HEADS];      // signal head -> key/value head
   int16_t members[DA_MAX_HEADS]; // noise group n's signal heads at [n*g, n*g+g)
+  // shared-value prefill only: signal heads with the same noise head and the
+  // same key/value head form combos of gs heads, combo c at [c*gs, c*gs+gs)
+  int gs, ncombo;
+  int16_t cmem[DA_MAX_HEADS];
 };
 
 struct DecodeParams {
@@ -118,6 +122,12 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s);
 // key/value heads (d = 64); gda3_applies says whether a call has that layout
 bool gda3_applies(const FwdParams& p);
 hipError_t launch_fwd_gda3_bf16(const FwdParams& p, hipStream_t s);
+// bf16 prefill for layers whose signal heads share noise and key/value heads
+// in combos of 2, 4 or 8 (d = 64, fixed-length batches, nested output
+// strides): A2 V formed once per combo (fwd_bf16.hip).  shared_kv_plan fills
+// gs, ncombo and cmem and says whether a call has that layout.
+bool shared_kv_plan(FwdParams& p);
+hipError_t launch_fwd_shared_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t s);
 // device address of the current device's fixed decode scratch (DA_DECODE_SCRATCH_BYTES)
 hipError_t decode_scratch(float** ptr);
