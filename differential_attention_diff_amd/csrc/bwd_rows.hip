@@ -26,21 +26,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// 8 consecutive values as floats
-__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
-  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[e] = a[e];
-    x[4 + e] = b[e];
-  }
-}
-__device__ __forceinline__ void load8(const __bf16* p, float (&x)[8]) {
-  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-  const bf16x8 a = *(const bf16x8*)p;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
-}
 __device__ __forceinline__ void store8(float* p, const float (&x)[8], float (&r)[8]) {
   f32x4 a, b;
 #pragma unroll
@@ -72,7 +57,16 @@ __device__ __forceinline__ float group_sum(float x) {
 
 // Each row's dv channels are spread over L = dv / 8 lanes, 8 channels per lane
 // (16-byte loads); a wavefront holds 64 / L rows at a time and walks the rows
-// grid-stride.
+// grid-stride, with the loads of its next rows (do, both o_maps planes and the
+// two log-sum-exps) issued before the current rows are processed.
+template <typename T>
+struct PrepRow {
+  typedef T t8 __attribute__((ext_vector_type(8)));
+  t8 y;            // do
+  f32x4 a[2], z[2];  // o1, o2
+  float l1, l2;    // lse of both maps
+};
+
 template <typename T, int DV>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   constexpr int L = DV / 8, RPW = 64 / L;
@@ -80,6 +74,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   const int sub = lane % L, c0 = sub * 8;
   const int64_t rows = (int64_t)p.B * p.N * p.Hs;
   const int64_t plane = rows * DV;  // one map of o_maps
+  const int64_t lplane = (int64_t)p.B * p.Hs * p.N;  // one map of lse
   const float cst = 1.0f - p.lam_init;
   const float lam = lambda_of(p.lam_dev, p.lam);
   const float sgn = lam > 0.f ? -1.f : 1.f, llam = log2f(fabsf(lam));  // log2 0 = -inf
@@ -87,19 +82,58 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   float w[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) w[e] = (p.normalize && p.norm_w) ? p.norm_w[c0 + e] : 1.0f;
+  // (batch, token, head) of a row (clamped to the last row) and its lse index
+  const bool narrow = rows <= (int64_t)UINT32_MAX;  // 32-bit index division suffices
+  auto coords = [&](int64_t row, int& b, int& i, int& h) {
+    const int64_t rr = row < rows ? row : rows - 1;
+    if (narrow) {
+      const uint32_t r32 = (uint32_t)rr, t = r32 / (uint32_t)p.Hs;
+      h = (int)(r32 - t * (uint32_t)p.Hs);
+      b = (int)(t / (uint32_t)p.N);
+      i = (int)(t - (uint32_t)b * (uint32_t)p.N);
+    } else {
+      h = (int)(rr % p.Hs);
+      const int64_t t = rr / p.Hs;
+      i = (int)(t % p.N);
+      b = (int)(t / p.N);
+    }
+    return rr;
+  };
+  auto fetch = [&](int64_t row, PrepRow<T>& f) {
+    int b, i, h;
+    const int64_t rr = coords(row, b, i, h);
+    f.y = *(const typename PrepRow<T>::t8*)((const T*)p.dout + b * p.sdo[0] + (int64_t)i * p.sdo[1] +
+                                            h * p.sdo[2] + c0);
+    const float* o1 = p.o_maps + rr * DV + c0;
+    f.a[0] = *(const f32x4*)o1;
+    f.a[1] = *(const f32x4*)(o1 + 4);
+    f.z[0] = *(const f32x4*)(o1 + plane);
+    f.z[1] = *(const f32x4*)(o1 + plane + 4);
+    const int64_t li = ((int64_t)b * p.Hs + h) * p.N + i;
+    f.l1 = p.lse[li];
+    f.l2 = p.lse[lplane + li];
+  };
   const int64_t step = (int64_t)gridDim.x * 4 * RPW;
-  for (int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * RPW; row0 < rows; row0 += step) {
+  int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * RPW;
+  PrepRow<T> cur;
+  if (row0 < rows) fetch(row0 + lane / L, cur);
+  for (; row0 < rows; row0 += step) {
+    PrepRow<T> nxt;
+    if (row0 + step < rows) fetch(row0 + step + lane / L, nxt);
     const int64_t row = row0 + lane / L;
     const bool valid = row < rows;
-    const int64_t rr = valid ? row : rows - 1;
-    const int h = (int)(rr % p.Hs);
-    const int64_t t = rr / p.Hs;
-    const int i = (int)(t % p.N);
-    const int b = (int)(t / p.N);
+    int b, i, h;
+    const int64_t rr = coords(row, b, i, h);
     float y[8], a[8], z[8], o[8], dd[8], e8[8];
-    load8((const T*)p.dout + b * p.sdo[0] + (int64_t)i * p.sdo[1] + h * p.sdo[2] + c0, y);
-    load8(p.o_maps + rr * DV + c0, a);
-    load8(p.o_maps + plane + rr * DV + c0, z);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = cur.a[0][e];
+      a[4 + e] = cur.a[1][e];
+      z[e] = cur.z[0][e];
+      z[4 + e] = cur.z[1][e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = (float)cur.y[e];
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -139,11 +173,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
     const float D1 = group_sum<L>(s1), D2 = group_sum<L>(s2);
     if (valid && sub == 0) {
       const int64_t li = ((int64_t)b * p.Hs + h) * p.N + i;
-      const float l1 = p.lse[li], l2 = p.lse[(int64_t)p.B * p.Hs * p.N + li];
       // map 2 folded with lambda: 2^(s - (lse2' - log2|lambda|)) = |lambda| P2 (0 for
       // lambda = 0), and sgn D2 with -lambda = sgn |lambda|
-      *(float4*)(p.rowstat + 4 * li) = make_float4(l1 * kLog2e, l2 * kLog2e - llam, D1, sgn * D2);
+      *(float4*)(p.rowstat + 4 * li) = make_float4(cur.l1 * kLog2e, cur.l2 * kLog2e - llam, D1, sgn * D2);
     }
+    cur = nxt;
   }
   // sums over the wavefront's row slots, then over the 4 wavefronts, into this
   // workgroup's row of `partial`

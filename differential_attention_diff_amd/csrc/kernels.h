@@ -114,7 +114,10 @@ struct BwdParams {
   int16_t kvmembers[DA_MAX_HEADS]; // key/value head k's signal heads at [k*gk, k*gk+gk)
 };
 
-constexpr int kBwdPrepBlocks = 8192;  // upper bound of BwdParams::nprep
+// upper bound of BwdParams::nprep: two rounds of three 4-wavefront workgroups
+// per compute unit, each wavefront walking many row groups (its next rows'
+// loads in flight while it processes the current ones)
+constexpr int kBwdPrepBlocks = 1536;
 
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s);
