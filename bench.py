@@ -49,13 +49,14 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 # profiles/.  Each entry is valid only for the kernel sources its counters were taken on
 # (sha256 of each file) and is reported as null otherwise.
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "differential_attention_diff_amd", "csrc")
-_PREFILL_SRC = {"fwd_bf16.hip": "0a6937bd55e74110ff675d7491648cf440558541797e1691019c5811cdd4abcc",
+_PREFILL_SRC = {"fwd_bf16.hip": "9f47356f6a32e3c5b2dac21dbd0d02254bdfbe2b544af0a60899c287ae538cef",
            "fwd_gda3_bf16.hip": "b4b2ccfaa19e97cdbf6ea78d56b51f24e740f6ac27f80068a4e477b1a8248e05",
-           "fwd_common.h": "bb6ae20a6225278b019d48ff544959515d34ac3ce94bf0133686525236becee1"}
+           "fwd_common.h": "bb6ae20a6225278b019d48ff544959515d34ac3ce94bf0133686525236becee1",
+           "abi.cpp": "b1ed8a5788ca3196abc4eeecd3b09aa88fe6bc1e480c0c6692c64160ceb2c7c0"}
 _DECODE_SRC = {"decode_bf16.hip": "c7e9a334551ec5bfb54b0d9ccc36ffbbbe1058d4e5b2908b122b53542a0952b8",
-           "abi.cpp": "c5a30288bf7a67a52f7ddba3a7c46d537e50e1db227319a9acd7a8c3ae5ab5a7"}
+           "abi.cpp": "b1ed8a5788ca3196abc4eeecd3b09aa88fe6bc1e480c0c6692c64160ceb2c7c0"}
 _BACKWARD_SRC = {"bwd_ring_bf16.hip": "b3338ed779f698888144e88b8efcdb0f1357702eead62eb14d5a12ab01bc8ed6",
-           "bwd_rows.hip": "10ca45ddf9f90b87d21211eb16910bcfbd2c6eebd9dc5fe721610504e8190ca7",
+           "bwd_rows.hip": "5fcb2e7c9d1de27467041285c83fc0866eda7e55c9463d69e2401f8423138335",
            "fwd_common.h": "bb6ae20a6225278b019d48ff544959515d34ac3ce94bf0133686525236becee1"}
 _KIB = 1024
 
@@ -66,23 +67,24 @@ def _hbm(fetch_kib, write_kib):
 
 
 MEASURED_TRAFFIC = {
-    # prefill: the one kernel of the step
-    ("prefill", "diff3b_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(148095.6, 98304.0)},
-    ("prefill", "gda3to1_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(114314.4, 73728.0)},
-    ("prefill", "gda4to1_gqa_bf16_n32768"): {"sha256": _PREFILL_SRC, "bytes": _hbm(641679.4, 131072.0)},
-    ("prefill", "gda3to1_varlen_bf16_8x4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(152200.4, 101299.5)},
+    # prefill: the step's kernel (the map-2 and map-1 launches for shared combos)
+    ("prefill", "diff3b_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(147782.3, 98304.0)},
+    ("prefill", "gda3to1_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(114427.4, 73728.0)},
+    ("prefill", "gda4to1_gqa_bf16_n32768"): {"sha256": _PREFILL_SRC,
+                                            "bytes": _hbm(143191.9 + 317299.1, 131602.8 + 131072.0)},
+    ("prefill", "gda3to1_varlen_bf16_8x4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(152157.6, 101299.7)},
     # decode: decode_partial_kernel + decode_combine_kernel
     ("decode", "gda_decode_bf16_b64_l8192"): {"sha256": _DECODE_SRC,
-                                              "bytes": _hbm(586215.1 + 2114.4, 4121.2 + 288.0)},
+                                              "bytes": _hbm(586223.9 + 2114.4, 4120.9 + 288.0)},
     ("decode", "gda_decode_fp8_b64_l8192"): {"sha256": _DECODE_SRC,
-                                             "bytes": _hbm(294347.8 + 2114.4, 4119.4 + 288.0)},
+                                             "bytes": _hbm(294346.0 + 2114.4, 4118.9 + 288.0)},
     # backward: bwd_prep + bwd_dq_ring + bwd_dkv_ring + bwd_finalize
     ("backward", "diff3b_bf16_n4096"): {"sha256": _BACKWARD_SRC,
-                                        "bytes": _hbm(258211.2 + 310697.8 + 311940.3 + 526.6,
-                                                      119054.1 + 110590.6 + 245867.1)},
+                                        "bytes": _hbm(258282.0 + 309595.0 + 307539.0 + 111.0,
+                                                      112562.0 + 110590.0 + 245882.0)},
     ("backward", "gda3to1_bf16_n4096"): {"sha256": _BACKWARD_SRC,
-                                         "bytes": _hbm(193673.1 + 466092.4 + 660189.1 + 526.6,
-                                                       91395.7 + 52227.2 + 135181.7)},
+                                         "bytes": _hbm(193933.0 + 467486.0 + 671428.0 + 111.0,
+                                                       84647.0 + 52226.0 + 135185.0)},
 }
 
 

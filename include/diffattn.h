@@ -118,7 +118,12 @@ da_status diffattn_fwd(const da_fwd_args* args, void* stream);
 
 /* Grouped differential attention ([GDA] Abstract, GQA-style repetition of the
  * noise heads; GQA key/value heads for K1/V): requires H_s % H_n == 0 and
- * H_s % H_kv == 0.  With H_n == H_kv == H_s it equals diffattn_fwd. */
+ * H_s % H_kv == 0.  With H_n == H_kv == H_s it equals diffattn_fwd.
+ * Signal heads that share a noise head and a key/value head have one map-2
+ * output; for bf16 at d = 64 with such heads in combos of 2, 4 or 8 and
+ * nested row-major `out` strides, the call runs as two launches and `out`
+ * holds intermediate values (each combo's A2 V) between them: its contents
+ * are defined only once the stream has passed the call. */
 da_status gda_fwd(const da_fwd_args* args, void* stream);
 
 /* Packed variable-length GDA prefill: the same operation as gda_fwd applied
