@@ -349,6 +349,94 @@ __device__ __forceinline__ void step(St<D>& st, const Ctx& c, int j) {
   st.l += sum;
 }
 
+// Epilogue of a map-1 wavefront: o = O1/l1 - lambda O2/l2 from this lane's O1
+// accumulators (times inv = 1/l1) and map 2's value o2(cb, r) of the same
+// accumulator slot (both maps take identical operations: identical maps with
+// lambda = 1 give exact zeros), the head RMS norm over dv (in-lane + one
+// swap), times (1 - lambda_init) w, rounded to bf16 and stored to `out` (the
+// lane's output row; nullptr: not stored).  Channels ch..ch+3, ch = 32 cb +
+// 8 g4 + 4 hh, live in o[cb][4 g4 .. 4 g4 + 3].
+template <int D, typename O2>
+__device__ __forceinline__ void combine_store(St<D>& st, float inv, O2 o2, const FwdParams& p, __bf16* out, int hh) {
+  constexpr int NCB = Cfg<D>::NCB, DV = Cfg<D>::DV;
+  const float lam = lambda_of(p.lam_dev, p.lam);
+  float ss = 0.f;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x = __builtin_fmaf(-lam, o2(cb, r), __fmul_rn(st.o[cb][r], inv));
+      st.o[cb][r] = x;
+      ss = __builtin_fmaf(x, x, ss);
+    }
+  float scale = 1.0f;
+  if (p.normalize) {
+    ss = half_swap_sum(ss);
+    scale = (1.0f - p.lam_init) / sqrtf(ss * (1.0f / DV) + p.eps);
+  }
+  if (!out) return;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int ch = cb * 32 + 8 * g4 + 4 * hh;
+      f32x4 wv = {1.f, 1.f, 1.f, 1.f};
+      if (p.normalize && p.norm_w) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wv[e] = p.norm_w[ch + e];
+      }
+      f32x4 y = {st.o[cb][4 * g4] * scale * wv[0], st.o[cb][4 * g4 + 1] * scale * wv[1],
+                 st.o[cb][4 * g4 + 2] * scale * wv[2], st.o[cb][4 * g4 + 3] * scale * wv[3]};
+      *(bf16x4*)(out + ch) = __builtin_convertvector(y, bf16x4);
+    }
+}
+
+// The block walk of a wavefront: tile t's sync precedes block 2t; blocks
+// before the wavefront's first masked block run unmasked, every wavefront runs
+// the same sequence of syncs; then the last block's P.V.  qw0 is the
+// wavefront's first query when causal, else -1 (keys past N - 1 are masked).
+template <int D, int NK, typename Sync>
+__device__ __forceinline__ void walk_blocks(St<D>& st, const Ctx& c, int nb, Sync& tile_sync, int lane, int qw0,
+                                            int N) {
+  const int jm = min(c.jmask, nb);
+  int j = 0;
+  for (; j + 1 < jm; j += 2) {
+    tile_sync(j >> 1);
+    step<D, NK, 0, false>(st, c, j);
+    step<D, NK, 1, false>(st, c, j + 1);
+  }
+  if (j < jm) {  // jm odd: one more unmasked (even) block
+    tile_sync(j >> 1);
+    step<D, NK, 0, false>(st, c, j);
+    ++j;
+  }
+  // the masked blocks recompute the lane constants from an opaque lane index, so
+  // nothing derived for the loop above has to stay live across it
+  Ctx cm = c;
+  {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    cm.l32 = ln & 31;
+    cm.hh = ln >> 5;
+    cm.vt_lane = ((4 * cm.hh + (ln & 15) / 4) << 8) | (16 * ((ln >> 4) & 1) + 4 * (ln & 3));
+    cm.kmax = qw0 >= 0 ? qw0 + cm.l32 : N - 1;
+  }
+  if ((j & 1) && j < nb) {  // first masked block is odd
+    step<D, NK, 1, true>(st, cm, j);
+    ++j;
+  }
+  for (; j < nb; j += 2) {
+    tile_sync(j >> 1);
+    step<D, NK, 0, true>(st, cm, j);
+    if (j + 1 < nb) step<D, NK, 1, true>(st, cm, j + 1);
+  }
+  // drain: P(nb-1) V(nb-1)
+  if ((nb - 1) & 1)
+    pv_products<D, 1>(st);
+  else
+    pv_products<D, 0>(st);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   using C = Cfg<D>;
@@ -526,46 +614,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
   st.s[0] = score_products<D>(st.kf, st.qf);
   read_k<D, 2>(st.kf, c, 1);
 
-  // ---- the pipeline; tile t's sync precedes block 2t.  Blocks before this
-  // wavefront's first masked block run unmasked; every wavefront runs the same
-  // sequence of syncs.
-  const int jm = min(c.jmask, nb);
-  int j = 0;
-  for (; j + 1 < jm; j += 2) {
-    tile_sync(j >> 1);
-    step<D, 2, 0, false>(st, c, j);
-    step<D, 2, 1, false>(st, c, j + 1);
-  }
-  if (j < jm) {  // jm odd: one more unmasked (even) block
-    tile_sync(j >> 1);
-    step<D, 2, 0, false>(st, c, j);
-    ++j;
-  }
-  // the masked blocks recompute the lane constants from an opaque lane index, so
-  // nothing derived for the loop above has to stay live across it
-  Ctx cm = c;
-  {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    cm.l32 = ln & 31;
-    cm.hh = ln >> 5;
-    cm.vt_lane = ((4 * cm.hh + (ln & 15) / 4) << 8) | (16 * ((ln >> 4) & 1) + 4 * (ln & 3));
-    cm.kmax = p.causal ? qw0 + cm.l32 : N - 1;
-  }
-  if ((j & 1) && j < nb) {  // first masked block is odd
-    step<D, 2, 1, true>(st, cm, j);
-    ++j;
-  }
-  for (; j < nb; j += 2) {
-    tile_sync(j >> 1);
-    step<D, 2, 0, true>(st, cm, j);
-    if (j + 1 < nb) step<D, 2, 1, true>(st, cm, j + 1);
-  }
-  // drain: P(nb-1) V(nb-1)
-  if ((nb - 1) & 1)
-    pv_products<D, 1>(st);
-  else
-    pv_products<D, 0>(st);
+  walk_blocks<D, 2>(st, c, nb, tile_sync, lane, p.causal ? qw0 : -1, N);
 
   // ---- epilogue.  The ring is free once every wave is past its last read (all
   // tile loads were awaited before their tiles were read).
@@ -609,41 +658,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
       }
   }
 
-  // o = O1/l1 - lambda O2/l2, then the head RMS norm
-  const float lam = lambda_of(p.lam_dev, p.lam);
-  float ss = 0.f;
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      // both maps take identical operations: identical maps with lambda = 1 give exact zeros
-      const float o2 = xo[((grp * NCB + cb) * 16 + r) * 64 + lane];
-      const float x = __builtin_fmaf(-lam, o2, __fmul_rn(st.o[cb][r], inv));
-      st.o[cb][r] = x;
-      ss = __builtin_fmaf(x, x, ss);
-    }
-  float scale = 1.0f;
-  if (p.normalize) {
-    ss = half_swap_sum(ss);
-    scale = (1.0f - p.lam_init) / sqrtf(ss * (1.0f / DV) + p.eps);
-  }
-  if (q < N) {
-    __bf16* out = (__bf16*)p.out + b * p.so[0] + (t0 + q) * p.so[1] + h * p.so[2];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int ch = cb * 32 + 8 * g4 + 4 * hh;  // channels ch..ch+3 live in o[cb][4 g4 .. 4 g4 + 3]
-        f32x4 wv = {1.f, 1.f, 1.f, 1.f};
-        if (p.normalize && p.norm_w) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) wv[e] = p.norm_w[ch + e];
-        }
-        f32x4 y = {st.o[cb][4 * g4] * scale * wv[0], st.o[cb][4 * g4 + 1] * scale * wv[1],
-                   st.o[cb][4 * g4 + 2] * scale * wv[2], st.o[cb][4 * g4 + 3] * scale * wv[3]};
-        *(bf16x4*)(out + ch) = __builtin_convertvector(y, bf16x4);
-      }
-  }
+  combine_store<D>(st, inv, [&](int cb, int r) { return xo[((grp * NCB + cb) * 16 + r) * 64 + lane]; }, p,
+                   q < N ? (__bf16*)p.out + b * p.so[0] + (t0 + q) * p.so[1] + h * p.so[2] : nullptr, hh);
 }
 
 // ---- layers whose signal heads share noise and key/value heads
@@ -805,40 +821,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_shared_kernel(FwdParams p) {
   st.s[0] = score_products<D>(st.kf, st.qf);
   read_k<D, 1>(st.kf, c, 1);
 
-  const int jm = min(c.jmask, nb);
-  int j = 0;
-  for (; j + 1 < jm; j += 2) {
-    tile_sync(j >> 1);
-    step<D, 1, 0, false>(st, c, j);
-    step<D, 1, 1, false>(st, c, j + 1);
-  }
-  if (j < jm) {
-    tile_sync(j >> 1);
-    step<D, 1, 0, false>(st, c, j);
-    ++j;
-  }
-  Ctx cm = c;
-  {
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    cm.l32 = ln & 31;
-    cm.hh = ln >> 5;
-    cm.vt_lane = ((4 * cm.hh + (ln & 15) / 4) << 8) | (16 * ((ln >> 4) & 1) + 4 * (ln & 3));
-    cm.kmax = p.causal ? qw0 + cm.l32 : N - 1;
-  }
-  if ((j & 1) && j < nb) {
-    step<D, 1, 1, true>(st, cm, j);
-    ++j;
-  }
-  for (; j < nb; j += 2) {
-    tile_sync(j >> 1);
-    step<D, 1, 0, true>(st, cm, j);
-    if (j + 1 < nb) step<D, 1, 1, true>(st, cm, j + 1);
-  }
-  if ((nb - 1) & 1)
-    pv_products<D, 1>(st);
-  else
-    pv_products<D, 0>(st);
+  walk_blocks<D, 1>(st, c, nb, tile_sync, lane, p.causal ? qw0 : -1, N);
 
   // ---- epilogue
   const float lsum = half_swap_sum(st.l);
@@ -909,36 +892,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_shared_kernel(FwdParams p) {
         *(f32x4*)(om1 + cb * 32 + 8 * g4 + 4 * hh) = a;
       }
   }
-  const float lam = lambda_of(p.lam_dev, p.lam);
-  float ss = 0.f;
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float x = __builtin_fmaf(-lam, z[cb][r / 4][r % 4], __fmul_rn(st.o[cb][r], inv));
-      st.o[cb][r] = x;
-      ss = __builtin_fmaf(x, x, ss);
-    }
-  float scale = 1.0f;
-  if (p.normalize) {
-    ss = half_swap_sum(ss);
-    scale = (1.0f - p.lam_init) / sqrtf(ss * (1.0f / DV) + p.eps);
-  }
-  __bf16* out = (__bf16*)p.out + orow + h * p.so[2];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int ch = cb * 32 + 8 * g4 + 4 * hh;
-      f32x4 wv = {1.f, 1.f, 1.f, 1.f};
-      if (p.normalize && p.norm_w) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) wv[e] = p.norm_w[ch + e];
-      }
-      f32x4 y = {st.o[cb][4 * g4] * scale * wv[0], st.o[cb][4 * g4 + 1] * scale * wv[1],
-                 st.o[cb][4 * g4 + 2] * scale * wv[2], st.o[cb][4 * g4 + 3] * scale * wv[3]};
-      *(bf16x4*)(out + ch) = __builtin_convertvector(y, bf16x4);
-    }
+  combine_store<D>(st, inv, [&](int cb, int r) { return z[cb][r / 4][r % 4]; }, p,
+                   (__bf16*)p.out + orow + h * p.so[2], hh);
 }
 
 }  // namespace

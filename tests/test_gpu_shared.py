@@ -158,3 +158,20 @@ def test_climbing_scores():
         got = fwd(inp, 0.6, 0.6, causal=causal)
         want = O.diff_attention(inp["q1"], inp["q2"], inp["k1"], inp["k2"], inp["v"], 0.6, 0.6, causal=causal)
         assert_parity(as64(got), want, "bf16", f"shared climbing causal={causal}")
+
+
+def test_full_gqa_workload_bitwise_equal_to_general_kernel():
+    # the 32k-token 4:1 GDA layer on 2:1 GQA key/value heads (the benchmark's
+    # launch): every output element of the two-launch path equals the general
+    # kernel's.  The parked A2 V rows are finite numbers when read as bf16, so a
+    # NaN sentinel alone could not show that every output row was rewritten; the
+    # general kernel's output is sentinel-checked and the two must agree bit for bit
+    # (sampled rows of both against the oracle: tests/test_gpu_prefill.py).
+    from differential_attention_diff_amd import workloads as W
+    w = W.WORKLOADS["gda4to1_gqa_bf16_n32768"]
+    inp = W.make_prefill_inputs(w)
+    shared = fwd(inp, w.lam, w.lam_init)
+    gen = torch.full((w.B, w.H_s, w.N, w.dv), float("nan"), dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    fwd(inp, w.lam, w.lam_init, out=gen)
+    assert bool(torch.isfinite(gen).all()), "general kernel: some outputs were not written"
+    assert torch.equal(shared, gen.contiguous())
