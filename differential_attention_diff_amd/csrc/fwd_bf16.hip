@@ -437,23 +437,18 @@ __device__ __forceinline__ void walk_blocks(St<D>& st, const Ctx& c, int nb, Syn
     pv_products<D, 0>(st);
 }
 
+// One work item of the general kernel: index `logical` of the item order below
+// (query block fastest, longest first); `ring` is the workgroup's LDS.
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
+__device__ __forceinline__ void fwd_item(const FwdParams& p, unsigned char* ring, int logical) {
   using C = Cfg<D>;
   constexpr int DV = C::DV, NCB = C::NCB, NKS = C::NKS;
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[kSlots * C::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave % kGroups, map = wave / kGroups;  // map 0: Q1/K1, map 1: Q2/K2
   const int l32 = lane & 31, hh = lane >> 5;
-
-  // ---- work item: XCD-contiguous, query block fastest (longest first)
   const int nq = (p.max_seqlen + kQB - 1) / kQB;
-  const int total = p.nseq * p.Hs * nq;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, q8 = total >> 3, r8 = total & 7;
-  const int logical = xcd * q8 + min(xcd, r8) + (bid >> 3);
   int qb, member, n, sq;  // sq: sequence
   if (p.cu_seqlens) {
     // packed sequences of unequal lengths: sequence fastest, so the contiguous
@@ -660,6 +655,35 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
 
   combine_store<D>(st, inv, [&](int cb, int r) { return xo[((grp * NCB + cb) * 16 + r) * 64 + lane]; }, p,
                    q < N ? (__bf16*)p.out + b * p.so[0] + (t0 + q) * p.so[1] + h * p.so[2] : nullptr, hh);
+}
+
+// Work items are numbered so that each XCD (workgroup ids congruent mod 8) owns
+// a contiguous range of them.  With one workgroup per item the hardware
+// dispatcher hands an XCD's items out in that order as its compute units free
+// up.  For fixed-length batches with at least two items per compute unit the
+// launcher sizes a persistent grid instead (one workgroup per compute unit,
+// which the 128 KiB of LDS of a d = 64 workgroup ensures): the workgroups of
+// an XCD take its items in a snake over rounds -- round r gives rank r w + w'
+// (w workgroups on the XCD; w' = this one's index within it, or w - 1 minus
+// it for odd r) -- so pairs of rounds even out the causal lengths, and the
+// items running at once are the ones the dispatcher would run.  With one item
+// per workgroup the loop runs once.
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(FwdParams p) {
+  using C = Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kSlots * C::STAGE];
+  const int nq = (p.max_seqlen + kQB - 1) / kQB;
+  const int total = p.nseq * p.Hs * nq;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, q8 = total >> 3, r8 = total & 7;
+  const int xstart = xcd * q8 + min(xcd, r8), xcount = q8 + (xcd < r8 ? 1 : 0);
+  const int nw = ((int)gridDim.x - xcd + 7) >> 3, w = bid >> 3;  // the XCD's workgroups, this one's index
+  for (int r = 0;; ++r) {
+    const int rank = r * nw + ((r & 1) ? nw - 1 - w : w);
+    if (rank >= xcount) break;
+    fwd_item<D>(p, ring, xstart + rank);
+    __syncthreads();  // every wavefront is past this item's LDS reads before the next item's loads
+  }
 }
 
 // ---- layers whose signal heads share noise and key/value heads
@@ -896,16 +920,42 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_shared_kernel(FwdParams p) {
                    (__bf16*)p.out + orow + h * p.so[2], hh);
 }
 
+// Compute units of the current device, queried once per device.
+hipError_t compute_units(int* n) {
+  constexpr int kMaxDevices = 64;
+  static int count[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (count[dev] == 0) {
+    int c = 0;
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    count[dev] = c;
+  }
+  *n = count[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s) {
   const int64_t nq = (p.max_seqlen + kQB - 1) / kQB;
   const int64_t total = (int64_t)p.nseq * p.Hs * nq;
   if (total > INT32_MAX) return hipErrorInvalidValue;
+  // persistent grid for fixed-length batches at d = 64 with at least two items per compute unit
+  int64_t grid = total;
+  if (p.d == 64 && !p.cu_seqlens) {
+    int cus = 0;
+    const hipError_t e = compute_units(&cus);
+    if (e != hipSuccess) return e;
+    if (cus > 0 && total >= 2 * (int64_t)cus) grid = cus;
+  }
   if (p.d == 64)
-    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((unsigned)total), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(fwd_bf16_kernel<32>, dim3((unsigned)total), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(fwd_bf16_kernel<32>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
