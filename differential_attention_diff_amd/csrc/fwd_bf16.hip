@@ -375,18 +375,29 @@ __device__ __forceinline__ void combine_store(St<D>& st, float inv, O2 o2, const
     scale = (1.0f - p.lam_init) / sqrtf(ss * (1.0f / DV) + p.eps);
   }
   if (!out) return;
+  // all weights first: a wait for a load between the stores would also wait
+  // for every store before it (one counter), serialising them
+  f32x4 wv[NCB][4];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) wv[cb][g4] = f32x4{1.f, 1.f, 1.f, 1.f};
+  if (p.normalize && p.norm_w) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wv[cb][g4][e] = p.norm_w[cb * 32 + 8 * g4 + 4 * hh + e];
+  }
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int ch = cb * 32 + 8 * g4 + 4 * hh;
-      f32x4 wv = {1.f, 1.f, 1.f, 1.f};
-      if (p.normalize && p.norm_w) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) wv[e] = p.norm_w[ch + e];
-      }
-      f32x4 y = {st.o[cb][4 * g4] * scale * wv[0], st.o[cb][4 * g4 + 1] * scale * wv[1],
-                 st.o[cb][4 * g4 + 2] * scale * wv[2], st.o[cb][4 * g4 + 3] * scale * wv[3]};
+      const f32x4 w = wv[cb][g4];
+      f32x4 y = {st.o[cb][4 * g4] * scale * w[0], st.o[cb][4 * g4 + 1] * scale * w[1],
+                 st.o[cb][4 * g4 + 2] * scale * w[2], st.o[cb][4 * g4 + 3] * scale * w[3]};
       *(bf16x4*)(out + ch) = __builtin_convertvector(y, bf16x4);
     }
 }

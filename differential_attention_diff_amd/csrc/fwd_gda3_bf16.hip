@@ -583,18 +583,29 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_gda3_kernel(FwdParams p) {
     }
     if (q < N) {
       __bf16* out = (__bf16*)p.out + b * p.so[0] + q * p.so[1] + h * p.so[2];
+      // all weights first: a wait for a load between the stores would also wait
+      // for every store before it (one counter), serialising them
+      f32x4 wv[NCB][4];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) wv[cb][g4] = f32x4{1.f, 1.f, 1.f, 1.f};
+      if (p.normalize && p.norm_w) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[cb][g4][e] = p.norm_w[cb * 32 + 8 * g4 + 4 * hh + e];
+      }
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int ch = cb * 32 + 8 * g4 + 4 * hh;  // channels ch..ch+3 live in o1[cb][4 g4 .. 4 g4 + 3]
-          f32x4 wv = {1.f, 1.f, 1.f, 1.f};
-          if (p.normalize && p.norm_w) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) wv[e] = p.norm_w[ch + e];
-          }
-          f32x4 y = {st.o1[cb][4 * g4] * scale * wv[0], st.o1[cb][4 * g4 + 1] * scale * wv[1],
-                     st.o1[cb][4 * g4 + 2] * scale * wv[2], st.o1[cb][4 * g4 + 3] * scale * wv[3]};
+          const f32x4 w = wv[cb][g4];
+          f32x4 y = {st.o1[cb][4 * g4] * scale * w[0], st.o1[cb][4 * g4 + 1] * scale * w[1],
+                     st.o1[cb][4 * g4 + 2] * scale * w[2], st.o1[cb][4 * g4 + 3] * scale * w[3]};
           *(bf16x4*)(out + ch) = __builtin_convertvector(y, bf16x4);
         }
     }
