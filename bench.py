@@ -49,8 +49,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 # profiles/.  Each entry is valid only for the kernel sources its counters were taken on
 # (sha256 of each file) and is reported as null otherwise.
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "differential_attention_diff_amd", "csrc")
-_PREFILL_SRC = {"fwd_bf16.hip": "9f47356f6a32e3c5b2dac21dbd0d02254bdfbe2b544af0a60899c287ae538cef",
-           "fwd_gda3_bf16.hip": "b4b2ccfaa19e97cdbf6ea78d56b51f24e740f6ac27f80068a4e477b1a8248e05",
+_PREFILL_SRC = {"fwd_bf16.hip": "d47272efd7ac7857523abeaf9b939ef93dd82175fb2d6133f5627b7e5cc5aa5e",
+           "fwd_gda3_bf16.hip": "6e12ddf0799d1e53927c36c30a0c36bafc4e32723051557589df3d36876b2a43",
            "fwd_common.h": "bb6ae20a6225278b019d48ff544959515d34ac3ce94bf0133686525236becee1",
            "abi.cpp": "b1ed8a5788ca3196abc4eeecd3b09aa88fe6bc1e480c0c6692c64160ceb2c7c0"}
 _DECODE_SRC = {"decode_bf16.hip": "c7e9a334551ec5bfb54b0d9ccc36ffbbbe1058d4e5b2908b122b53542a0952b8",
@@ -68,23 +68,23 @@ def _hbm(fetch_kib, write_kib):
 
 MEASURED_TRAFFIC = {
     # prefill: the step's kernel (the map-2 and map-1 launches for shared combos)
-    ("prefill", "diff3b_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(147782.3, 98304.0)},
-    ("prefill", "gda3to1_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(114427.4, 73728.0)},
+    ("prefill", "diff3b_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(147769.8, 98304.0)},
+    ("prefill", "gda3to1_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(114732.5, 73728.1)},
     ("prefill", "gda4to1_gqa_bf16_n32768"): {"sha256": _PREFILL_SRC,
-                                            "bytes": _hbm(143191.9 + 317299.1, 131602.8 + 131072.0)},
-    ("prefill", "gda3to1_varlen_bf16_8x4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(152157.6, 101299.7)},
+                                            "bytes": _hbm(143358.4 + 317265.9, 131150.0 + 131072.0)},
+    ("prefill", "gda3to1_varlen_bf16_8x4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(152183.5, 101299.5)},
     # decode: decode_partial_kernel + decode_combine_kernel
     ("decode", "gda_decode_bf16_b64_l8192"): {"sha256": _DECODE_SRC,
-                                              "bytes": _hbm(586223.9 + 2114.4, 4120.9 + 288.0)},
+                                              "bytes": _hbm(586205.8 + 2114.4, 4121.3 + 288.0)},
     ("decode", "gda_decode_fp8_b64_l8192"): {"sha256": _DECODE_SRC,
-                                             "bytes": _hbm(294346.0 + 2114.4, 4118.9 + 288.0)},
+                                             "bytes": _hbm(294355.9 + 2114.4, 4119.4 + 288.0)},
     # backward: bwd_prep + bwd_dq_ring + bwd_dkv_ring + bwd_finalize
     ("backward", "diff3b_bf16_n4096"): {"sha256": _BACKWARD_SRC,
-                                        "bytes": _hbm(258282.0 + 309595.0 + 307539.0 + 111.0,
-                                                      112562.0 + 110590.0 + 245882.0)},
+                                        "bytes": _hbm(258277.2 + 306228.7 + 307149.4 + 110.6,
+                                                      112548.0 + 110592.4 + 245863.4)},
     ("backward", "gda3to1_bf16_n4096"): {"sha256": _BACKWARD_SRC,
-                                         "bytes": _hbm(193933.0 + 467486.0 + 671428.0 + 111.0,
-                                                       84647.0 + 52226.0 + 135185.0)},
+                                         "bytes": _hbm(193934.7 + 466981.2 + 661650.0 + 110.6,
+                                                       84646.2 + 52225.8 + 135183.1)},
 }
 
 
