@@ -143,6 +143,15 @@ __device__ __forceinline__ void bwd_item(int logical, int ngroups, int nblk, int
   grp = c * cl + idx % cs;
 }
 
+// s_waitcnt vmcnt(0) as an instruction the compiler's own counter tracking
+// sees (simm16: expcnt 7, lgkmcnt 15, vmcnt 0).  The operand rows a wavefront
+// loads into registers before walking the ring are drained with it: the
+// compiler does not see the inline-assembly waits of the ring, so it would
+// otherwise guard their uses in every block with vmcnt waits of its own, and
+// those count the ring's DMA loads too (one counter), holding each block until
+// the block issued at its own barrier had landed.
+__device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Wait until at most `after` blocks' loads (PER per wavefront each) are in flight.
 template <int PER>
 __device__ __forceinline__ void wait_blocks(int after) {
@@ -184,19 +193,30 @@ __device__ __forceinline__ void dq_block(f32x4 (&dq1)[NDT], f32x4 (&dq2)[NDT], c
                                          const bf16x8 (&q2f)[NS], const bf16x8 (&dof)[NVS], const float4& rs,
                                          const lds_u8* lds, const DqLane& L, uint32_t sb, float sc, float sgn,
                                          int key0, int kvis, int jg) {
+  // product i of the first phase, 8 per 16-key half t = i / 8: S1^T and S2^T
+  // of step 0, of step 1, then the four dP^T steps; each product's LDS operand
+  // is read one product ahead (two reads in flight)
   f32x4 s1[2], s2[2], dp[2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    s1[t] = s2[t] = dp[t] = f32x4{};
+  for (int t = 0; t < 2; ++t) s1[t] = s2[t] = dp[t] = f32x4{};
+  auto rop = [&](int i) -> bf16x8 {
+    const int t = i >> 3, k = i & 7;
+    if (k < 4) return lds_ld16(lds + ((sb + L.kr) ^ ((k >> 1) << 6)) + t * 16 * KROW + ((k & 1) ? KBLK : 0));
+    return lds_ld16(lds + ((sb + L.vr) ^ ((k - 4) << 6)) + t * 16 * VROW);
+  };
+  bf16x8 rc = rop(0);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const lds_u8* a = lds + ((sb + L.kr) ^ (s << 6)) + t * 16 * KROW;
-      s1[t] = mfma16(lds_ld16(a), q1f[s], s1[t]);
-      s2[t] = mfma16(lds_ld16(a + KBLK), q2f[s], s2[t]);
-    }
-#pragma unroll
-    for (int s = 0; s < NVS; ++s)
-      dp[t] = mfma16(lds_ld16(lds + ((sb + L.vr) ^ (s << 6)) + t * 16 * VROW), dof[s], dp[t]);
+  for (int i = 0; i < 16; ++i) {
+    bf16x8 rn;
+    if (i + 1 < 16) rn = rop(i + 1);
+    const int t = i >> 3, k = i & 7;
+    if (k >= 4)
+      dp[t] = mfma16(rc, dof[k - 4], dp[t]);
+    else if (k & 1)
+      s2[t] = mfma16(rc, q2f[k >> 1], s2[t]);
+    else
+      s1[t] = mfma16(rc, q1f[k >> 1], s1[t]);
+    rc = rn;
   }
   // k order of the dS^T operand: slots 0-3 = keys 4 (l/16) + r, slots 4-7 = + 16
   bf16x8 b1, b2;
@@ -214,11 +234,19 @@ __device__ __forceinline__ void dq_block(f32x4 (&dq1)[NDT], f32x4 (&dq2)[NDT], c
       b1[4 * t + r] = (__bf16)(p1 * (dp[t][r] - rs.z));
       b2[4 * t + r] = (__bf16)(p2 * __builtin_fmaf(sgn, dp[t][r], -rs.w));
     }
+  // product i of the second phase: K1^T (even i) or K2^T (odd i) of column
+  // tile i / 2, read one product ahead
+  auto top = [&](int i) -> bf16x8 { return rd_tr(lds + ((sb + L.kt) ^ ((i >> 1) << 5)) + ((i & 1) ? KBLK : 0), 16 * KROW); };
+  bf16x8 tc = top(0);
 #pragma unroll
-  for (int ct = 0; ct < NDT; ++ct) {
-    const lds_u8* a = lds + ((sb + L.kt) ^ (ct << 5));
-    dq1[ct] = mfma16(rd_tr(a, 16 * KROW), b1, dq1[ct]);
-    dq2[ct] = mfma16(rd_tr(a + KBLK, 16 * KROW), b2, dq2[ct]);
+  for (int i = 0; i < 2 * NDT; ++i) {
+    bf16x8 tn;
+    if (i + 1 < 2 * NDT) tn = top(i + 1);
+    if (i & 1)
+      dq2[i >> 1] = mfma16(tc, b2, dq2[i >> 1]);
+    else
+      dq1[i >> 1] = mfma16(tc, b1, dq1[i >> 1]);
+    tc = tn;
   }
 }
 
@@ -326,6 +354,7 @@ __global__ __launch_bounds__(kQThreads, 4) void bwd_dq_ring_kernel(BwdParams p) 
       for (int s = 0; s < NVS; ++s) dof[s] = *(const bf16x8*)(DO + 32 * s + 8 * jg);
     }
     const float4 rs = *(const float4*)(p.rowstat + 4 * (((int64_t)b * p.Hs + h) * N + qc));
+    vm_drain();  // the member's operands (and the ring's blocks in flight) have landed
     f32x4 dq1[NDT];
 #pragma unroll
     for (int ct = 0; ct < NDT; ++ct) dq1[ct] = f32x4{};
@@ -383,19 +412,30 @@ template <bool MASK>
 __device__ __forceinline__ void dkv_block(DkvAcc& A, const bf16x8 (&kf1)[NS], const bf16x8 (&kf2)[NS],
                                           const bf16x8 (&vf)[NVS], const lds_u8* lds, const DkvLane& L,
                                           uint32_t sb, float sc, float sgn, int vd0, uint32_t vrange, int jg) {
+  // product i of the first phase, 8 per 16-query half t = i / 8: S1 and S2 of
+  // step 0, of step 1, then the four dP steps; each product's LDS operand is
+  // read one product ahead (two reads in flight)
   f32x4 s1[2], s2[2], dp[2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    s1[t] = s2[t] = dp[t] = f32x4{};
+  for (int t = 0; t < 2; ++t) s1[t] = s2[t] = dp[t] = f32x4{};
+  auto rop = [&](int i) -> bf16x8 {
+    const int t = i >> 3, k = i & 7;
+    if (k < 4) return lds_ld16(lds + ((sb + L.qr) ^ ((k >> 1) << 6)) + t * 16 * KROW + ((k & 1) ? KBLK : 0));
+    return lds_ld16(lds + ((sb + L.orow) ^ ((k - 4) << 6)) + t * 16 * VROW);
+  };
+  bf16x8 rc = rop(0);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const lds_u8* a = lds + ((sb + L.qr) ^ (s << 6)) + t * 16 * KROW;
-      s1[t] = mfma16(lds_ld16(a), kf1[s], s1[t]);
-      s2[t] = mfma16(lds_ld16(a + KBLK), kf2[s], s2[t]);
-    }
-#pragma unroll
-    for (int s = 0; s < NVS; ++s)
-      dp[t] = mfma16(lds_ld16(lds + ((sb + L.orow) ^ (s << 6)) + t * 16 * VROW), vf[s], dp[t]);
+  for (int i = 0; i < 16; ++i) {
+    bf16x8 rn;
+    if (i + 1 < 16) rn = rop(i + 1);
+    const int t = i >> 3, k = i & 7;
+    if (k >= 4)
+      dp[t] = mfma16(rc, vf[k - 4], dp[t]);
+    else if (k & 1)
+      s2[t] = mfma16(rc, kf2[k >> 1], s2[t]);
+    else
+      s1[t] = mfma16(rc, kf1[k >> 1], s1[t]);
+    rc = rn;
   }
   // k order of the B operands: slots 0-3 = queries 4 (l/16) + r, slots 4-7 = + 16
   const lds_u8* rsb = lds + (sb + RSOFF + 64 * jg);
@@ -416,14 +456,26 @@ __device__ __forceinline__ void dkv_block(DkvAcc& A, const bf16x8 (&kf1)[NS], co
       b1[4 * t + r] = (__bf16)(p1 * (dp[t][r] - st[2]));
       b2[4 * t + r] = (__bf16)(p2 * __builtin_fmaf(sgn, dp[t][r], -st[3]));
     }
+  // product i of the second phase: do^T column tiles 0-7 for dV, then Q1^T
+  // (even) and Q2^T (odd) of column tiles 0-3 for dK1 and dK2, read one
+  // product ahead
+  auto top = [&](int i) -> bf16x8 {
+    if (i < NVT) return rd_tr(lds + ((sb + L.ot) ^ (i << 5)), 16 * VROW);
+    const int ct = (i - NVT) >> 1;
+    return rd_tr(lds + ((sb + L.qt) ^ (ct << 5)) + ((i & 1) ? KBLK : 0), 16 * KROW);
+  };
+  bf16x8 tc = top(0);
 #pragma unroll
-  for (int vt = 0; vt < NVT; ++vt)
-    A.dv[vt] = mfma16(rd_tr(lds + ((sb + L.ot) ^ (vt << 5)), 16 * VROW), bc, A.dv[vt]);
-#pragma unroll
-  for (int ct = 0; ct < NDT; ++ct) {
-    const lds_u8* a = lds + ((sb + L.qt) ^ (ct << 5));
-    A.dk1[ct] = mfma16(rd_tr(a, 16 * KROW), b1, A.dk1[ct]);
-    A.dk2[ct] = mfma16(rd_tr(a + KBLK, 16 * KROW), b2, A.dk2[ct]);
+  for (int i = 0; i < NVT + 2 * NDT; ++i) {
+    bf16x8 tn;
+    if (i + 1 < NVT + 2 * NDT) tn = top(i + 1);
+    if (i < NVT)
+      A.dv[i] = mfma16(tc, bc, A.dv[i]);
+    else if (i & 1)
+      A.dk2[(i - NVT) >> 1] = mfma16(tc, b2, A.dk2[(i - NVT) >> 1]);
+    else
+      A.dk1[(i - NVT) >> 1] = mfma16(tc, b1, A.dk1[(i - NVT) >> 1]);
+    tc = tn;
   }
 }
 
@@ -520,28 +572,38 @@ __global__ __launch_bounds__(kKThreads, 3) void bwd_dkv_ring_kernel(BwdParams p)
   L.orow = 2 * KBLK + row_off(lane, 0, VROW, true);
   L.ot = 2 * KBLK + tr_off(lane, 0, VROW, true);
 
-  bf16x8 kf2[NS];
+  for (int t = 0; t < min(F, kKSlots - 1); ++t) issue();  // blocks 0 .. kKSlots - 2
+
+  // key-side operands: K2 of the noise head, K1 and V of the run's key/value head
+  bf16x8 kf2[NS], kf1[NS], vf[NVS];
+  auto load_kv = [&](int kh) {
+    const __bf16* K1 = (const __bf16*)p.k1 + b * p.sk1[0] + (int64_t)kc * p.sk1[1] + kh * p.sk1[2];
+    const __bf16* V = (const __bf16*)p.v + b * p.sv[0] + (int64_t)kc * p.sv[1] + kh * p.sv[2];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kf1[s] = *(const bf16x8*)(K1 + 32 * s + 8 * jg);
+#pragma unroll
+    for (int s = 0; s < NVS; ++s) vf[s] = *(const bf16x8*)(V + 32 * s + 8 * jg);
+  };
   {
     const __bf16* K2 = (const __bf16*)p.k2 + b * p.sk2[0] + (int64_t)kc * p.sk2[1] + n * p.sk2[2];
 #pragma unroll
     for (int s = 0; s < NS; ++s) kf2[s] = *(const bf16x8*)(K2 + 32 * s + 8 * jg);
   }
+  int cur = arg16(p.kv, arg16(p.members, n * g));  // key/value head of the accumulating run
+  load_kv(cur);
+  vm_drain();
   DkvAcc A;
 #pragma unroll
   for (int ct = 0; ct < NDT; ++ct) A.dk2[ct] = A.dk1[ct] = f32x4{};
 #pragma unroll
   for (int vt = 0; vt < NVT; ++vt) A.dv[vt] = f32x4{};
 
-  for (int t = 0; t < min(F, kKSlots - 1); ++t) issue();  // blocks 0 .. kKSlots - 2
-
-  bf16x8 kf1[NS], vf[NVS];
-  int cur = -1;     // key/value head of the accumulating run
   uint32_t sl = 0;  // slot offset of the next block walked
   int f0 = 0;
   for (int mem = 0; mem < g; ++mem, f0 += nb) {
     const int kh = arg16(p.kv, arg16(p.members, n * g + mem));
     if (kh != cur) {
-      if (cur >= 0 && key < N) {
+      if (key < N) {
         store_row16((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)key * p.sgk1[1] + cur * p.sgk1[2], A.dk1, p.sm_scale,
                     jg);
         store_row16((__bf16*)p.gv + b * p.sgv[0] + (int64_t)key * p.sgv[1] + cur * p.sgv[2], A.dv, 1.0f, jg);
@@ -551,12 +613,8 @@ __global__ __launch_bounds__(kKThreads, 3) void bwd_dkv_ring_kernel(BwdParams p)
 #pragma unroll
       for (int vt = 0; vt < NVT; ++vt) A.dv[vt] = f32x4{};
       cur = kh;
-      const __bf16* K1 = (const __bf16*)p.k1 + b * p.sk1[0] + (int64_t)kc * p.sk1[1] + kh * p.sk1[2];
-      const __bf16* V = (const __bf16*)p.v + b * p.sv[0] + (int64_t)kc * p.sv[1] + kh * p.sv[2];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) kf1[s] = *(const bf16x8*)(K1 + 32 * s + 8 * jg);
-#pragma unroll
-      for (int s = 0; s < NVS; ++s) vf[s] = *(const bf16x8*)(V + 32 * s + 8 * jg);
+      load_kv(kh);
+      vm_drain();
     }
     // ring block f0 + i is query block j0 + i of this head
     int j = j0;
