@@ -187,7 +187,10 @@ struct DqLane {
 };
 
 // One 32-key block in slot offset sb (keys key0 ..): S1^T, S2^T, dP^T, the
-// weights and dS^T, then dQ1^T += K1^T dS1^T and dQ2^T += K2^T dS2^T.
+// weights and dS^T, then dQ1^T += K1^T dS1^T and dQ2^T += K2^T dS2^T.  rs
+// holds the lane's query statistics as {lse1', lse2', -D1, sgn (D1 - D2)}: the
+// dP^T products accumulate onto -D1, so dS1 = P1 (dP - D1) takes one multiply
+// and sgn (dP - D2) = sgn (dP - D1) + sgn (D1 - D2) one FMA.
 template <bool MASK>
 __device__ __forceinline__ void dq_block(f32x4 (&dq1)[NDT], f32x4 (&dq2)[NDT], const bf16x8 (&q1f)[NS],
                                          const bf16x8 (&q2f)[NS], const bf16x8 (&dof)[NVS], const float4& rs,
@@ -198,7 +201,10 @@ __device__ __forceinline__ void dq_block(f32x4 (&dq1)[NDT], f32x4 (&dq2)[NDT], c
   // is read one product ahead (two reads in flight)
   f32x4 s1[2], s2[2], dp[2];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) s1[t] = s2[t] = dp[t] = f32x4{};
+  for (int t = 0; t < 2; ++t) {
+    s1[t] = s2[t] = f32x4{};
+    dp[t] = f32x4{rs.z, rs.z, rs.z, rs.z};  // -D1: the products accumulate dP - D1
+  }
   auto rop = [&](int i) -> bf16x8 {
     const int t = i >> 3, k = i & 7;
     if (k < 4) return lds_ld16(lds + ((sb + L.kr) ^ ((k >> 1) << 6)) + t * 16 * KROW + ((k & 1) ? KBLK : 0));
@@ -231,8 +237,8 @@ __device__ __forceinline__ void dq_block(f32x4 (&dq1)[NDT], f32x4 (&dq2)[NDT], c
         p1 = vis ? p1 : 0.f;
         p2 = vis ? p2 : 0.f;
       }
-      b1[4 * t + r] = (__bf16)(p1 * (dp[t][r] - rs.z));
-      b2[4 * t + r] = (__bf16)(p2 * __builtin_fmaf(sgn, dp[t][r], -rs.w));
+      b1[4 * t + r] = (__bf16)(p1 * dp[t][r]);
+      b2[4 * t + r] = (__bf16)(p2 * __builtin_fmaf(sgn, dp[t][r], rs.w));  // sgn (dP - D2)
     }
   // product i of the second phase: K1^T (even i) or K2^T (odd i) of column
   // tile i / 2, read one product ahead
@@ -344,16 +350,21 @@ __global__ __launch_bounds__(kQThreads, 4) void bwd_dq_ring_kernel(BwdParams p) 
   int f0 = 0;
   for (int mem = 0; mem < g; ++mem, f0 += nb) {
     const int h = arg16(p.members, n * g + mem);
+    // the lane's row index made opaque: its row addresses are formed here for
+    // each member rather than held (in registers the walk needs) across the walk
+    const int qm = (int)opaque((uint32_t)qc);
     bf16x8 q1f[NS], dof[NVS];
     {
-      const __bf16* Q1 = (const __bf16*)p.q1 + b * p.sq1[0] + (int64_t)qc * p.sq1[1] + h * p.sq1[2];
-      const __bf16* DO = (const __bf16*)p.dop + (((int64_t)b * N + qc) * p.Hs + h) * DV;
+      const __bf16* Q1 = (const __bf16*)p.q1 + b * p.sq1[0] + (int64_t)qm * p.sq1[1] + h * p.sq1[2];
+      const __bf16* DO = (const __bf16*)p.dop + (((int64_t)b * N + qm) * p.Hs + h) * DV;
 #pragma unroll
       for (int s = 0; s < NS; ++s) q1f[s] = *(const bf16x8*)(Q1 + 32 * s + 8 * jg);
 #pragma unroll
       for (int s = 0; s < NVS; ++s) dof[s] = *(const bf16x8*)(DO + 32 * s + 8 * jg);
     }
-    const float4 rs = *(const float4*)(p.rowstat + 4 * (((int64_t)b * p.Hs + h) * N + qc));
+    float4 rs = *(const float4*)(p.rowstat + 4 * (((int64_t)b * p.Hs + h) * N + qm));
+    rs.w = __builtin_fmaf(sgn, rs.z, -rs.w);  // sgn (D1 - D2)
+    rs.z = -rs.z;
     vm_drain();  // the member's operands (and the ring's blocks in flight) have landed
     f32x4 dq1[NDT];
 #pragma unroll
@@ -374,11 +385,13 @@ __global__ __launch_bounds__(kQThreads, 4) void bwd_dq_ring_kernel(BwdParams p) 
       sync(f0 + j);
       sl = next_slot(sl);
     }
-    if (q < N)
-      store_row16((__bf16*)p.gq1 + b * p.sgq1[0] + (int64_t)q * p.sgq1[1] + h * p.sgq1[2], dq1, p.sm_scale, jg);
+    const int qs = (int)opaque((uint32_t)q);
+    if (qs < N)
+      store_row16((__bf16*)p.gq1 + b * p.sgq1[0] + (int64_t)qs * p.sgq1[1] + h * p.sgq1[2], dq1, p.sm_scale, jg);
   }
-  if (q < N)
-    store_row16((__bf16*)p.gq2 + b * p.sgq2[0] + (int64_t)q * p.sgq2[1] + n * p.sgq2[2], dq2, p.sm_scale, jg);
+  const int qs = (int)opaque((uint32_t)q);
+  if (qs < N)
+    store_row16((__bf16*)p.gq2 + b * p.sgq2[0] + (int64_t)qs * p.sgq2[1] + n * p.sgq2[2], dq2, p.sm_scale, jg);
 }
 
 // ---------------------------------------------------------------------------
@@ -577,8 +590,9 @@ __global__ __launch_bounds__(kKThreads, 3) void bwd_dkv_ring_kernel(BwdParams p)
   // key-side operands: K2 of the noise head, K1 and V of the run's key/value head
   bf16x8 kf2[NS], kf1[NS], vf[NVS];
   auto load_kv = [&](int kh) {
-    const __bf16* K1 = (const __bf16*)p.k1 + b * p.sk1[0] + (int64_t)kc * p.sk1[1] + kh * p.sk1[2];
-    const __bf16* V = (const __bf16*)p.v + b * p.sv[0] + (int64_t)kc * p.sv[1] + kh * p.sv[2];
+    const int km = (int)opaque((uint32_t)kc);  // row address formed here, not held across the walk
+    const __bf16* K1 = (const __bf16*)p.k1 + b * p.sk1[0] + (int64_t)km * p.sk1[1] + kh * p.sk1[2];
+    const __bf16* V = (const __bf16*)p.v + b * p.sv[0] + (int64_t)km * p.sv[1] + kh * p.sv[2];
 #pragma unroll
     for (int s = 0; s < NS; ++s) kf1[s] = *(const bf16x8*)(K1 + 32 * s + 8 * jg);
 #pragma unroll
@@ -603,10 +617,11 @@ __global__ __launch_bounds__(kKThreads, 3) void bwd_dkv_ring_kernel(BwdParams p)
   for (int mem = 0; mem < g; ++mem, f0 += nb) {
     const int kh = arg16(p.kv, arg16(p.members, n * g + mem));
     if (kh != cur) {
-      if (key < N) {
-        store_row16((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)key * p.sgk1[1] + cur * p.sgk1[2], A.dk1, p.sm_scale,
+      const int ks = (int)opaque((uint32_t)key);
+      if (ks < N) {
+        store_row16((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)ks * p.sgk1[1] + cur * p.sgk1[2], A.dk1, p.sm_scale,
                     jg);
-        store_row16((__bf16*)p.gv + b * p.sgv[0] + (int64_t)key * p.sgv[1] + cur * p.sgv[2], A.dv, 1.0f, jg);
+        store_row16((__bf16*)p.gv + b * p.sgv[0] + (int64_t)ks * p.sgv[1] + cur * p.sgv[2], A.dv, 1.0f, jg);
       }
 #pragma unroll
       for (int ct = 0; ct < NDT; ++ct) A.dk1[ct] = f32x4{};
@@ -634,10 +649,11 @@ __global__ __launch_bounds__(kKThreads, 3) void bwd_dkv_ring_kernel(BwdParams p)
     walk(std::false_type{}, max(jm1, j));
     walk(std::true_type{}, nbq);
   }
-  if (key < N) {
-    store_row16((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)key * p.sgk1[1] + cur * p.sgk1[2], A.dk1, p.sm_scale, jg);
-    store_row16((__bf16*)p.gv + b * p.sgv[0] + (int64_t)key * p.sgv[1] + cur * p.sgv[2], A.dv, 1.0f, jg);
-    store_row16((__bf16*)p.gk2 + b * p.sgk2[0] + (int64_t)key * p.sgk2[1] + n * p.sgk2[2], A.dk2, p.sm_scale, jg);
+  const int ks = (int)opaque((uint32_t)key);
+  if (ks < N) {
+    store_row16((__bf16*)p.gk1 + b * p.sgk1[0] + (int64_t)ks * p.sgk1[1] + cur * p.sgk1[2], A.dk1, p.sm_scale, jg);
+    store_row16((__bf16*)p.gv + b * p.sgv[0] + (int64_t)ks * p.sgv[1] + cur * p.sgv[2], A.dv, 1.0f, jg);
+    store_row16((__bf16*)p.gk2 + b * p.sgk2[0] + (int64_t)ks * p.sgk2[1] + n * p.sgk2[2], A.dk2, p.sm_scale, jg);
   }
 }
 
