@@ -359,8 +359,9 @@ def diff_attention_backward(q1, q2, k1, k2, v, dout, lam: float, lambda_init: fl
                             normalize: bool = True) -> dict:
     """Gradients of L = sum(dout * out) for the forward ``diff_attention``
     (same arguments; dout [B,N,H_s,dv]).  Returns float64 arrays dq1, dq2,
-    dk1, dk2, dv (shapes of the inputs), the scalar dlambda and, when a norm
-    weight is given, dnorm_weight [dv].
+    dk1, dk2, dv (shapes of the inputs), the scalar dlambda, the L2 norm of
+    the terms dlambda sums (dlambda_scale: the scale of its rounding error,
+    whose terms cancel) and, when a norm weight is given, dnorm_weight [dv].
 
     Steps, per batch b and signal head h (n = nz(h), k = kv(h)):
       forward pieces: s1 = q1 k1^T / sqrt(d), s2 = q2 k2^T / sqrt(d), a1 =
@@ -384,6 +385,7 @@ def diff_attention_backward(q1, q2, k1, k2, v, dout, lam: float, lambda_init: fl
     scale = 1.0 / math.sqrt(d)
     g = {k: np.zeros_like(x) for k, x in (("dq1", q1), ("dq2", q2), ("dk1", k1), ("dk2", k2), ("dv", v))}
     dlam = 0.0
+    dlam_sq = 0.0
     dw = np.zeros(dv_)
     hidden = np.triu(np.ones((N, N), bool), 1) if causal else np.zeros((N, N), bool)
     for b in range(B):
@@ -404,6 +406,7 @@ def diff_attention_backward(q1, q2, k1, k2, v, dout, lam: float, lambda_init: fl
             else:
                 do = gy
             dlam -= float(np.sum(do * o2))
+            dlam_sq += float(np.sum((do * o2) ** 2))
             dp = do @ vv.T
             g["dv"][b, :, k] += (a1 - lam * a2).T @ do
             ds1 = a1 * (dp - np.sum(a1 * dp, axis=-1, keepdims=True))
@@ -414,6 +417,7 @@ def diff_attention_backward(q1, q2, k1, k2, v, dout, lam: float, lambda_init: fl
             g["dq2"][b, :, n] += ds2 @ k2[b, :, n] * scale
             g["dk2"][b, :, n] += ds2.T @ q2[b, :, n] * scale
     g["dlambda"] = dlam
+    g["dlambda_scale"] = math.sqrt(dlam_sq)
     if norm_weight is not None and normalize:
         g["dnorm_weight"] = dw
     return g

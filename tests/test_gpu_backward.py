@@ -15,10 +15,15 @@ zero (one visible key) within 1e-5.  The bf16 passes round three operands to
 bf16 on the way to each gradient (do, the weights and dS, relative error
 <= 2^-9 each) on top of bf16 inputs: the relative L2 error of such sums is
 about sqrt(3) 2^-9 = 3.4e-3 for independent roundings, and the cases here
-measure 2.6e-3 .. 3.4e-3 (fp32: below 1e-6).  dlambda is one sum over every
-row whose terms cancel (each row's do . o2 carries the rounding of o = o1 -
-lambda o2 and of the norm's backward): within 5e-3 relative (measured up to
-2.9e-3), fp32 within 5e-5 (measured up to 1.1e-5)."""
+measure 2.6e-3 .. 3.4e-3 (fp32: below 1e-6).  dlambda = -sum(do . o2) is one
+sum of B N H_s dv terms whose signs cancel, so its value can be far smaller
+than its terms: each term carries the forward's rounding of the attention
+weights to bf16 (2^-9 relative), and those errors add like a random walk, so
+the bf16 bar is set against the L2 norm of the terms (the oracle's
+dlambda_scale), not against |dlambda|: |error| <= 2^-7 dlambda_scale (seeded
+sweeps of 160 random layers measured up to 4.1e-3 dlambda_scale, about 2^-8,
+with |dlambda| down to 0.4% of the scale); fp32 within 5e-5 relative
+(measured up to 1.1e-5)."""
 
 import numpy as np
 import pytest
@@ -50,6 +55,16 @@ def check_grad(got, want, dtype, what):
         assert rel <= 5e-3 and maxabs <= 4e-2 * scale, \
             f"{what}: bf16 rel-L2 {rel:.3e}, max-abs {maxabs:.3e} (scale {scale:.3e})"
     return maxabs, rel
+
+
+def check_dlambda(got, want, dtype, what):
+    err = abs(got - want["dlambda"])
+    if dtype == "f32":
+        assert err <= 5e-5 * max(1.0, abs(want["dlambda"])), f"{what}: dlambda {got} against {want['dlambda']}"
+    else:
+        assert err <= 2.0 ** -7 * want["dlambda_scale"], \
+            f"{what}: dlambda {got} against {want['dlambda']} (terms' L2 norm {want['dlambda_scale']:.3e})"
+    return err / max(want["dlambda_scale"], 1e-30)
 
 
 def run_fwd_bwd(inp, dout, lam, li, norm_weight=None, want_dw=False, **kw):
@@ -100,10 +115,9 @@ def test_backward_small_every_element(dtype, shape, causal):
     errs = []
     for name, g in zip(NAMES, grads[:5]):
         errs.append(check_grad(as64(g), want[name], dtype, f"{name} {dtype} {shape} causal={causal}")[1])
-    dl = float(grads[5].cpu()[0])
-    dl_err = abs(dl - want["dlambda"]) / max(1.0, abs(want["dlambda"]))
-    print(f"[bwd {dtype} {shape} causal={causal}] max rel-L2 {max(errs):.3e}, dlambda rel {dl_err:.3e}", flush=True)
-    assert dl_err <= (5e-5 if dtype == "f32" else 5e-3)
+    dl_err = check_dlambda(float(grads[5].cpu()[0]), want, dtype, f"{dtype} {shape} causal={causal}")
+    print(f"[bwd {dtype} {shape} causal={causal}] max rel-L2 {max(errs):.3e}, dlambda error / terms' L2 norm "
+          f"{dl_err:.3e}", flush=True)
     check_grad(as64(dw), want["dnorm_weight"], dtype, "dnorm_w")
 
 
@@ -133,7 +147,7 @@ def test_autograd_function(dtype, hkv):
     tag = "f32" if dtype == torch.float32 else "bf16"
     for name, key in zip(NAMES, ("q1", "q2", "k1", "k2", "v")):
         check_grad(as64(d[key].grad), want[name], tag, f"autograd {name}")
-    assert abs(float(lam.grad) - want["dlambda"]) <= (5e-5 if tag == "f32" else 5e-3) * max(1, abs(want["dlambda"]))
+    check_dlambda(float(lam.grad), want, tag, "autograd")
     check_grad(as64(w.grad), want["dnorm_weight"], tag, "autograd dw")
 
 

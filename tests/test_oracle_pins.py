@@ -471,6 +471,19 @@ def test_backward_gda_sums_the_repeated_plain_gradients():
     assert g["dlambda"] == pytest.approx(p["dlambda"], rel=1e-12)
 
 
+def test_backward_dlambda_and_its_scale_without_norm():
+    # without the head norm do = dout, so dlambda = -sum(dout . o2) with o2 the
+    # second stream's attention output (torch's SDPA here), and dlambda_scale is
+    # the L2 norm of those terms
+    q1, q2, k1, k2, v = tiny(B=2, N=9, hs=4, hn=2, hkv=2, d=4, dv=8, seed=63)
+    dout = rnd((2, 9, 4, 8), 64)
+    g = O.diff_attention_backward(q1, q2, k1, k2, v, dout, 0.6, 0.3, normalize=False)
+    rep = lambda x: np.repeat(x, 2, axis=2)
+    terms = dout * sdpa(rep(q2), rep(k2), rep(v), True)
+    assert g["dlambda"] == pytest.approx(-terms.sum(), rel=1e-12, abs=1e-12)
+    assert g["dlambda_scale"] == pytest.approx(np.sqrt((terms ** 2).sum()), rel=1e-12)
+
+
 def test_maps_are_sdpa_of_each_stream():
     q1, q2, k1, k2, v = tiny(B=1, N=10, hs=2, hn=2, hkv=2, d=4, dv=8, seed=61)
     m = O.diff_attention_maps(q1, q2, k1, k2, v)
