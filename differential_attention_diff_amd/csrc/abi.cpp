@@ -267,6 +267,7 @@ constexpr int64_t kDefaultPartials = 2560;
 constexpr int kChunkQuantum = 128;  // positions per decode sub-chunk
 constexpr int kMaxChunk = 2048;
 constexpr int kDecodeMaxQueries = 8;  // g + 1 scored queries per noise group
+constexpr int kDecodeMaxOutputs = 8;  // g + u outputs per noise group (u: its distinct key/value heads)
 constexpr int64_t kMaxPosStride = 1 << 19;  // elements; 2048 positions x 2 B x 2^19 < 2^31
 
 da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool check_pointers) {
@@ -334,6 +335,11 @@ da_status decode_prepare(const da_decode_args* a, da::DecodeParams* p, bool chec
     p->nu[n] = (int16_t)u;
     umax = std::max(umax, u);
   }
+  if (g + umax > kDecodeMaxOutputs)
+    return fail(DA_EUNSUPPORTED,
+                "gda_decode keeps at most %d outputs per noise group: its %d signal heads plus the %d distinct "
+                "key/value heads they read",
+                kDecodeMaxOutputs, g, umax);
   // fp8 caches are walked in sub-chunks of 2 x 128 positions
   const int64_t quantum = fp8 ? 2 * kChunkQuantum : kChunkQuantum;
   if (a->block_table) {  // paged caches: every sub-chunk inside one block

@@ -77,7 +77,9 @@ enum {
  *   v   [B,N,H_kv,dv] out [B,N,H_s,dv]   (dtype `dtype`, device)
  *   s_* element strides of dims (b, n, head) of each tensor.
  *   noise_of_signal / kv_of_signal: host int32[H_s] or NULL (consecutive
- *     grouping).  Each noise head must serve exactly H_s/H_n signal heads.
+ *     grouping).  H_s must be a multiple of H_n and of H_kv (DA_EINVAL
+ *     otherwise), with explicit maps too; each noise head must serve exactly
+ *     H_s/H_n signal heads.
  *   lambda: the folded per-layer scalar of [DA-blog] "Learnable Lambda
  *     Re-parameterization" (any real value).  lambda_init: the same section's
  *     per-layer constant, used only by the head norm.  eps > 0: added to the
@@ -239,7 +241,12 @@ da_status gda_bwd(const da_bwd_args* args, void* workspace, size_t workspace_byt
  *     other value (0 included) means the caches are in `dtype` and the scales
  *     are ignored.
  *   Everything else as in da_fwd_args (the causal flag is implied; lambda_dev
- *     included). */
+ *     included).
+ *   Limits (DA_EUNSUPPORTED otherwise, before any HIP call): d = 64, bf16
+ *     queries, bf16 or e4m3 caches; per noise group at most 7 signal heads
+ *     and at most 8 outputs, its g signal heads plus the u distinct key/value
+ *     heads they read (g + u <= 8: 3:1 GDA on distinct key/value heads is
+ *     3 + 3, 4:1 GDA on 2:1 GQA 4 + 2); at most 65535 sequences. */
 typedef struct da_decode_args {
   const void* q1;
   const void* q2;

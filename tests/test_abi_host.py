@@ -331,6 +331,12 @@ def test_decode_validation(L):
     assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EUNSUPPORTED
     a = base_dec(hs=18, hn=2, hkv=2)  # 9 signal heads per noise head
     assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EUNSUPPORTED
+    # 5 signal heads per noise head on 5 distinct key/value heads: g + u = 10 outputs
+    a = base_dec(hs=10, hn=2, hkv=10)
+    assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EUNSUPPORTED and "outputs" in ops.last_error()
+    assert L.gda_decode_workspace_bytes(ctypes.byref(a)) == 0
+    a = base_dec(hs=12, hn=2, hkv=4)  # g = 6 on u = 2 key/value heads: 8 outputs, accepted
+    assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EWORKSPACE, ops.last_error()
     a = base_dec()
     a.seq_lens = None
     assert L.gda_decode(ctypes.byref(a), None, 0, None) == ops.DA_EINVAL
