@@ -52,6 +52,33 @@ Extent extent(const void* p, const int64_t* dims, const int64_t* strides, int nl
 
 bool overlaps(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
 
+// A strided [B, N, heads, last] view (last dim contiguous, strides of (b, n, head) in elements).
+struct View {
+  const void* p;
+  int64_t dims[3];
+  const int64_t* s;
+  int64_t last;
+  int es;
+};
+
+// Whether two views may share a byte.  Disjoint byte extents never do.  Nor do
+// two views that repeat with the same token stride (batch strides multiples
+// of it) when their footprints within one token row -- heads and channels --
+// are disjoint intervals modulo that stride: the interleaved views of one
+// packed buffer, e.g. the projections of a fused QKV layer and their
+// gradients.  Otherwise they are taken to overlap.
+bool views_overlap(const View& x, const View& y) {
+  if (!overlaps(extent(x.p, x.dims, x.s, 3, x.last, x.es), extent(y.p, y.dims, y.s, 3, y.last, y.es))) return false;
+  const int64_t ts = x.s[1];
+  if (x.es != y.es || ts <= 0 || y.s[1] != ts) return true;
+  if ((x.dims[0] > 1 && x.s[0] % ts) || (y.dims[0] > 1 && y.s[0] % ts)) return true;
+  const int64_t R = ts * x.es;  // bytes per token row
+  const int64_t fx = ((x.dims[2] - 1) * x.s[2] + x.last) * x.es, fy = ((y.dims[2] - 1) * y.s[2] + y.last) * y.es;
+  if (fx > R || fy > R) return true;
+  const int64_t x0 = (int64_t)((uintptr_t)x.p % (uint64_t)R), y0 = (int64_t)((uintptr_t)y.p % (uint64_t)R);
+  return !(((y0 - x0 + R) % R) >= fx && ((x0 - y0 + R) % R) >= fy);
+}
+
 da_status check_strides(const char* name, const void* p, const int64_t* s, int n, int esize) {
   if (!p) return fail(DA_EINVAL, "%s is NULL", name);
   if (!aligned16(p)) return fail(DA_EINVAL, "%s is not 16-byte aligned", name);
@@ -180,11 +207,10 @@ da_status fwd_impl(const da_fwd_args* a, void* stream, bool plain, const Packing
     int64_t dims[3] = {a->B, a->N, a->H_s};
     eo = extent(a->out, dims, a->s_out, 3, a->dv, es);
   }
-  for (int i = 0; i < 5; ++i) {
-    int64_t dims[3] = {a->B, a->N, ts[i].heads};
-    if (overlaps(eo, extent(ts[i].p, dims, ts[i].s, 3, ts[i].last, es)))
+  const View vo{a->out, {a->B, a->N, a->H_s}, a->s_out, a->dv, es};
+  for (int i = 0; i < 5; ++i)
+    if (views_overlap(vo, View{ts[i].p, {a->B, a->N, ts[i].heads}, ts[i].s, ts[i].last, es}))
       return fail(DA_EINVAL, "out overlaps %s", ts[i].name);
-  }
   if (a->lse) {
     Extent el{(uintptr_t)a->lse, (uintptr_t)(a->lse + 2 * a->B * a->H_s * a->N)};
     if (overlaps(el, eo)) return fail(DA_EINVAL, "lse overlaps out");
@@ -564,21 +590,18 @@ da_status bwd_prepare(const da_bwd_args* a, da::BwdParams* p, bool check_pointer
   if (!aligned16(a->o_maps)) return fail(DA_EINVAL, "o_maps is not 16-byte aligned");
   if (!a->lse) return fail(DA_EINVAL, "lse is NULL");
   if ((uintptr_t)a->lse & 3u) return fail(DA_EINVAL, "lse is not 4-byte aligned");
-  Extent ein[8], eout[5];
-  for (int i = 0; i < 6; ++i) {
-    int64_t dims[3] = {a->B, a->N, ins[i].heads};
-    ein[i] = extent(ins[i].p, dims, ins[i].s, 3, ins[i].last, es);
-  }
-  ein[6] = {(uintptr_t)a->o_maps, (uintptr_t)a->o_maps + (uintptr_t)(2 * a->B * a->N * a->H_s * a->dv * 4)};
-  ein[7] = {(uintptr_t)a->lse, (uintptr_t)(a->lse + 2 * a->B * a->H_s * a->N)};
-  const char* in_names[8] = {"q1", "q2", "k1", "k2", "v", "dout", "o_maps", "lse"};
+  auto view = [&](const T& t) { return View{t.p, {a->B, a->N, t.heads}, t.s, t.last, es}; };
+  const Extent e_maps{(uintptr_t)a->o_maps, (uintptr_t)a->o_maps + (uintptr_t)(2 * a->B * a->N * a->H_s * a->dv * 4)};
+  const Extent e_lse{(uintptr_t)a->lse, (uintptr_t)(a->lse + 2 * a->B * a->H_s * a->N)};
   for (int i = 0; i < 5; ++i) {
-    int64_t dims[3] = {a->B, a->N, outs[i].heads};
-    eout[i] = extent(outs[i].p, dims, outs[i].s, 3, outs[i].last, es);
-    for (int j = 0; j < 8; ++j)
-      if (overlaps(eout[i], ein[j])) return fail(DA_EINVAL, "%s overlaps %s", outs[i].name, in_names[j]);
+    const View vi = view(outs[i]);
+    for (int j = 0; j < 6; ++j)
+      if (views_overlap(vi, view(ins[j]))) return fail(DA_EINVAL, "%s overlaps %s", outs[i].name, ins[j].name);
+    const Extent ei = extent(vi.p, vi.dims, vi.s, 3, vi.last, es);
+    if (overlaps(ei, e_maps)) return fail(DA_EINVAL, "%s overlaps o_maps", outs[i].name);
+    if (overlaps(ei, e_lse)) return fail(DA_EINVAL, "%s overlaps lse", outs[i].name);
     for (int j = 0; j < i; ++j)
-      if (overlaps(eout[i], eout[j])) return fail(DA_EINVAL, "%s overlaps %s", outs[i].name, outs[j].name);
+      if (views_overlap(vi, view(outs[j]))) return fail(DA_EINVAL, "%s overlaps %s", outs[i].name, outs[j].name);
   }
   p->q1 = a->q1;
   p->q2 = a->q2;

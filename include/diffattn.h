@@ -210,7 +210,11 @@ size_t gda_bwd_workspace_bytes(const da_bwd_args* args);
  * query-major pass (dQ1, dQ2), a key-major pass (dK1, dK2, dV) and a final
  * reduction (dlambda, dw); scores and weights are recomputed from lse.
  * workspace: device, caller-owned, 16-byte aligned, >= gda_bwd_workspace_bytes
- * (DA_EWORKSPACE otherwise).  Outputs must not overlap inputs or each other. */
+ * (DA_EWORKSPACE otherwise).  Outputs must not overlap inputs or each other
+ * (DA_EINVAL): strided views of one buffer pass when they repeat with the same
+ * token stride and their columns within a token are disjoint -- the gradient
+ * of a fused projection written in its own layout; otherwise their byte
+ * ranges must be disjoint. */
 da_status gda_bwd(const da_bwd_args* args, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Decode arguments (gda_decode): one new query per sequence against caches

@@ -231,6 +231,46 @@ def test_bwd_workspace_required(L):
     assert L.gda_bwd(ctypes.byref(a), None, 0, None) == ops.DA_EWORKSPACE, ops.last_error()
 
 
+def packed_grads(a, shift_q2=0):
+    """Gradient views into one packed buffer laid out per token as [dq1 | dq2 | dk1 | dk2 | dv]
+    (the layout of a fused projection's gradient); shift_q2 moves dq2 back by that many elements."""
+    d, dv = a.d, a.dv
+    heads = (a.H_s, a.H_n, a.H_kv, a.H_n, a.H_kv)
+    widths = [h * w for h, w in zip(heads, (d, d, d, d, dv))]
+    total = sum(widths)
+    base, off = FAKE + 40 * GIB, 0
+    for i, (ptr, strides, w, h) in enumerate(zip(("grad_q1", "grad_q2", "grad_k1", "grad_k2", "grad_v"),
+                                                 ("s_gq1", "s_gq2", "s_gk1", "s_gk2", "s_gv"), widths, heads)):
+        start = off - (shift_q2 if i == 1 else 0)
+        setattr(a, ptr, base + 2 * start)
+        getattr(a, strides)[:] = [a.N * total, total, w // h]
+        off += w
+
+
+def test_bwd_gradients_into_one_packed_buffer(L):
+    # interleaved views whose per-token columns are disjoint are accepted ...
+    a = base_bwd(hs=8, hn=2, hkv=4)
+    a.s_q1[:], a.s_dout[:] = [64 * 8 * 64, 8 * 64, 64], [64 * 8 * 128, 8 * 128, 128]
+    a.s_k1[:], a.s_v[:] = [64 * 4 * 64, 4 * 64, 64], [64 * 4 * 128, 4 * 128, 128]
+    packed_grads(a)
+    assert L.gda_bwd(ctypes.byref(a), None, 0, None) == ops.DA_EWORKSPACE, ops.last_error()
+    # ... columns shared by two of them are not
+    packed_grads(a, shift_q2=8)
+    assert L.gda_bwd(ctypes.byref(a), None, 0, None) == ops.DA_EINVAL
+    assert "grad_q2 overlaps grad_q1" in ops.last_error()
+
+
+def test_fwd_out_sharing_columns_with_an_input_is_rejected(L):
+    a = base_fwd()
+    # out interleaved with q1 in one buffer, its first 8 channels on q1's last 8
+    total = 6 * 64 + 6 * 128
+    a.q1, a.out = FAKE + 40 * GIB, FAKE + 40 * GIB + 2 * (6 * 64 - 8)
+    a.s_q1[:] = [64 * total, total, 64]
+    a.s_out[:] = [64 * total, total, 128]
+    st, err = call(L, a)
+    assert st == ops.DA_EINVAL and "out overlaps q1" in err
+
+
 def test_lambda_entry_validation(L):
     f = lambda i: ctypes.c_void_p(FAKE + i * GIB)
     st = L.da_lambda_reparam(f(0), f(1), f(2), f(3), 0, ctypes.c_float(0.5), f(4), None)

@@ -151,6 +151,45 @@ def test_autograd_function(dtype, hkv):
     check_grad(as64(w.grad), want["dnorm_weight"], tag, "autograd dw")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_gradients_into_one_packed_buffer(dtype):
+    # inputs as views of one packed projection [q1 | q2 | k1 | k2 | v | pad] per token and the
+    # gradients written into one buffer of the same layout: bit-identical to separate gradient
+    # tensors, the padding columns untouched
+    B, N, hs, hn, hkv, d = 2, 150, 8, 2, 4, 64
+    heads = (hs, hn, hkv, hn, hkv)
+    widths = [h * w for h, w in zip(heads, (d, d, d, d, 2 * d))]
+    pad = 8
+    total = sum(widths) + pad * len(widths)
+    g = torch.Generator("cpu").manual_seed(77)
+    proj = torch.randn(B, N, total, generator=g).to(dtype).cuda()
+
+    def views(buf):
+        out, off = [], 0
+        for w, h in zip(widths, heads):
+            out.append(buf[:, :, off:off + w].view(B, N, h, w // h))
+            off += w + pad
+        return out
+
+    q1, q2, k1, k2, v = views(proj)
+    lse = torch.empty(2, B, hs, N, device="cuda")
+    om = torch.empty(2, B, N, hs, 2 * d, device="cuda")
+    ops.gda_fwd(q1, q2, k1, k2, v, 0.6, 0.3, lse=lse, o_maps=om)
+    dout = dout_like(B, N, hs, 2 * d, dtype, 78).cuda()
+    sep = ops.gda_bwd(q1, q2, k1, k2, v, om, lse, dout, 0.6, 0.3)
+    gbuf = torch.full((B, N, total), float("nan"), dtype=dtype, device="cuda")
+    packed = ops.gda_bwd(q1, q2, k1, k2, v, om, lse, dout, 0.6, 0.3, grads=tuple(views(gbuf)))
+    torch.cuda.synchronize()
+    for name, x, y in zip(NAMES, sep[:5], packed[:5]):
+        assert torch.equal(x, y.contiguous()), name
+    assert torch.equal(sep[5], packed[5])
+    off = 0
+    for w in widths:
+        off += w
+        assert bool(torch.isnan(gbuf[:, :, off:off + pad]).all()), "padding written"
+        off += pad
+
+
 def test_backward_empty_writes_zero_dlambda():
     inp = rand_inputs(B=0, N=16, hs=2, hn=2, hkv=2, d=64, dtype=torch.bfloat16, seed=1)
     d = {k: v.cuda() for k, v in inp.items()}
