@@ -52,9 +52,9 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "differential_at
 _PREFILL_SRC = {"fwd_bf16.hip": "d47272efd7ac7857523abeaf9b939ef93dd82175fb2d6133f5627b7e5cc5aa5e",
            "fwd_gda3_bf16.hip": "6e12ddf0799d1e53927c36c30a0c36bafc4e32723051557589df3d36876b2a43",
            "fwd_common.h": "bb6ae20a6225278b019d48ff544959515d34ac3ce94bf0133686525236becee1",
-           "abi.cpp": "b1ed8a5788ca3196abc4eeecd3b09aa88fe6bc1e480c0c6692c64160ceb2c7c0"}
+           "abi.cpp": "213b8ef6083a5b9334b57809f4192c9222f65971fceab68ed81c6f4b47a26142"}
 _DECODE_SRC = {"decode_bf16.hip": "c7e9a334551ec5bfb54b0d9ccc36ffbbbe1058d4e5b2908b122b53542a0952b8",
-           "abi.cpp": "b1ed8a5788ca3196abc4eeecd3b09aa88fe6bc1e480c0c6692c64160ceb2c7c0"}
+           "abi.cpp": "213b8ef6083a5b9334b57809f4192c9222f65971fceab68ed81c6f4b47a26142"}
 _BACKWARD_SRC = {"bwd_ring_bf16.hip": "baa62ce61839c81761dc781dc6e7c9923194180b5300f58ad834c49f0b2a3e6a",
            "bwd_rows.hip": "5fcb2e7c9d1de27467041285c83fc0866eda7e55c9463d69e2401f8423138335",
            "fwd_common.h": "bb6ae20a6225278b019d48ff544959515d34ac3ce94bf0133686525236becee1"}
@@ -68,23 +68,23 @@ def _hbm(fetch_kib, write_kib):
 
 MEASURED_TRAFFIC = {
     # prefill: the step's kernel (the map-2 and map-1 launches for shared combos)
-    ("prefill", "diff3b_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(147772.7, 98304.0)},
-    ("prefill", "gda3to1_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(114717.7, 73728.2)},
+    ("prefill", "diff3b_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(148082.4, 98304.0)},
+    ("prefill", "gda3to1_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(114552.0, 73728.1)},
     ("prefill", "gda4to1_gqa_bf16_n32768"): {"sha256": _PREFILL_SRC,
-                                            "bytes": _hbm(143337.1 + 317238.0, 131225.9 + 131072.0)},
-    ("prefill", "gda3to1_varlen_bf16_8x4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(152183.5, 101299.5)},
+                                            "bytes": _hbm(143383.3 + 317206.7, 131243.3 + 131072.0)},
+    ("prefill", "gda3to1_varlen_bf16_8x4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(152188.5, 101299.5)},
     # decode: decode_partial_kernel + decode_combine_kernel
     ("decode", "gda_decode_bf16_b64_l8192"): {"sha256": _DECODE_SRC,
-                                              "bytes": _hbm(586217.0 + 2114.4, 4122.3 + 288.0)},
+                                              "bytes": _hbm(586248.3 + 2114.4, 4121.4 + 288.0)},
     ("decode", "gda_decode_fp8_b64_l8192"): {"sha256": _DECODE_SRC,
-                                             "bytes": _hbm(294370.5 + 2114.4, 4119.4 + 288.0)},
+                                             "bytes": _hbm(294350.3 + 2114.4, 4119.4 + 288.0)},
     # backward: bwd_prep + bwd_dq_ring + bwd_dkv_ring + bwd_finalize
     ("backward", "diff3b_bf16_n4096"): {"sha256": _BACKWARD_SRC,
-                                        "bytes": _hbm(258297.9 + 387794.0 + 289458.0 + 110.6,
-                                                      112550.9 + 141310.2 + 196832.4)},
+                                        "bytes": _hbm(258330.8 + 387469.2 + 290509.8 + 110.6,
+                                                      112555.2 + 141308.3 + 196826.3)},
     ("backward", "gda3to1_bf16_n4096"): {"sha256": _BACKWARD_SRC,
-                                         "bytes": _hbm(193926.4 + 436675.0 + 536016.1 + 110.6,
-                                                       84643.9 + 59904.4 + 122998.5)},
+                                         "bytes": _hbm(193926.2 + 437390.1 + 532254.9 + 110.6,
+                                                       84651.3 + 59904.6 + 123005.6)},
 }
 
 
