@@ -77,13 +77,12 @@ __device__ __forceinline__ u32x4 fp8_to_bf16(u32x2 c) {
                __builtin_bit_cast(uint32_t, f)};
 }
 __device__ __forceinline__ u32x4 as_bf16(u32x4 c) { return c; }
-// a cache chunk; NT: non-temporal (streaming) load
-template <bool NT, typename T>
+// a cache chunk, loaded non-temporally: every cache byte is read once per
+// call, so keeping it in the caches only evicts what other loads reuse
+// (-8% for bf16 caches against plain loads, -2% for e4m3)
+template <typename T>
 __device__ __forceinline__ T ld_cache(const T* a) {
-  if constexpr (NT)
-    return __builtin_nontemporal_load(a);
-  else
-    return *a;
+  return __builtin_nontemporal_load(a);
 }
 __device__ __forceinline__ u32x4 as_bf16(u32x2 c) { return fp8_to_bf16(c); }
 
@@ -214,7 +213,7 @@ __global__ __launch_bounds__(kT, 3) void decode_partial_kernel(DecodeParams p) {
   // re-reads row ns - 1 (in bounds); its score is masked and its weight is zero.
   // Addresses: a uniform 64-bit base (scalar registers) plus a 32-bit per-lane byte
   // offset (the host bounds the position stride so chunk offsets fit in 32 bits).
-  // e4m3 caches are read with non-temporal loads (2% faster; 4% slower for bf16 caches).
+  // Cache rows are read with non-temporal loads (ld_cache).
   // rows [pos, pos + CP) of a cache: one block of a paged cache holds the whole sub-chunk
   auto cache_row0 = [&](const int64_t* st, int head, int pos) -> int64_t {
     if (p.block_table) {
@@ -229,7 +228,7 @@ __global__ __launch_bounds__(kT, 3) void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < kKC; ++i) {
       const uint32_t r = (uint32_t)min(krow + 16 * (i >> 1), ns - 1);
-      dst[i] = ld_cache<FP8>((const CK*)(K + (r * rs + 8u * ES * (uint32_t)(kq + 4 * (i & 1)))));
+      dst[i] = ld_cache((const CK*)(K + (r * rs + 8u * ES * (uint32_t)(kq + 4 * (i & 1)))));
     }
   };
   auto load_v = [&](int head, int r0, int ns) {
@@ -238,7 +237,7 @@ __global__ __launch_bounds__(kT, 3) void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
     for (int i = 0; i < kVC; ++i) {
       const uint32_t r = (uint32_t)min(vrow + 4 * i, ns - 1);
-      vr[i] = ld_cache<FP8>((const CK*)(V + (r * rs + 8u * ES * (uint32_t)vcol)));
+      vr[i] = ld_cache((const CK*)(V + (r * rs + 8u * ES * (uint32_t)vcol)));
     }
   };
   // the group's queries in LDS (each thread reads its 8 dims when scoring):
