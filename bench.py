@@ -53,7 +53,7 @@ _PREFILL_SRC = {"fwd_bf16.hip": "d47272efd7ac7857523abeaf9b939ef93dd82175fb2d613
            "fwd_gda3_bf16.hip": "6e12ddf0799d1e53927c36c30a0c36bafc4e32723051557589df3d36876b2a43",
            "fwd_common.h": "bb6ae20a6225278b019d48ff544959515d34ac3ce94bf0133686525236becee1",
            "abi.cpp": "213b8ef6083a5b9334b57809f4192c9222f65971fceab68ed81c6f4b47a26142"}
-_DECODE_SRC = {"decode_bf16.hip": "c7e9a334551ec5bfb54b0d9ccc36ffbbbe1058d4e5b2908b122b53542a0952b8",
+_DECODE_SRC = {"decode_bf16.hip": "e6011a5ce752106b4036e40c96a967168254d9825c8f60702d4a8c6f597c5e98",
            "abi.cpp": "213b8ef6083a5b9334b57809f4192c9222f65971fceab68ed81c6f4b47a26142"}
 _BACKWARD_SRC = {"bwd_ring_bf16.hip": "baa62ce61839c81761dc781dc6e7c9923194180b5300f58ad834c49f0b2a3e6a",
            "bwd_rows.hip": "5fcb2e7c9d1de27467041285c83fc0866eda7e55c9463d69e2401f8423138335",
@@ -68,23 +68,23 @@ def _hbm(fetch_kib, write_kib):
 
 MEASURED_TRAFFIC = {
     # prefill: the step's kernel (the map-2 and map-1 launches for shared combos)
-    ("prefill", "diff3b_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(148082.4, 98304.0)},
-    ("prefill", "gda3to1_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(114552.0, 73728.1)},
+    ("prefill", "diff3b_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(147892.7, 98304.0)},
+    ("prefill", "gda3to1_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(114563.9, 73728.1)},
     ("prefill", "gda4to1_gqa_bf16_n32768"): {"sha256": _PREFILL_SRC,
-                                            "bytes": _hbm(143383.3 + 317206.7, 131243.3 + 131072.0)},
-    ("prefill", "gda3to1_varlen_bf16_8x4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(152188.5, 101299.5)},
+                                            "bytes": _hbm(143378.9 + 317134.1, 131215.5 + 131072.0)},
+    ("prefill", "gda3to1_varlen_bf16_8x4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(152175.4, 101299.5)},
     # decode: decode_partial_kernel + decode_combine_kernel
     ("decode", "gda_decode_bf16_b64_l8192"): {"sha256": _DECODE_SRC,
-                                              "bytes": _hbm(586248.3 + 2114.4, 4121.4 + 288.0)},
+                                              "bytes": _hbm(595027.8 + 2114.4, 4119.8 + 288.0)},
     ("decode", "gda_decode_fp8_b64_l8192"): {"sha256": _DECODE_SRC,
-                                             "bytes": _hbm(294350.3 + 2114.4, 4119.4 + 288.0)},
+                                             "bytes": _hbm(294357.4 + 2114.4, 4119.4 + 288.0)},
     # backward: bwd_prep + bwd_dq_ring + bwd_dkv_ring + bwd_finalize
     ("backward", "diff3b_bf16_n4096"): {"sha256": _BACKWARD_SRC,
-                                        "bytes": _hbm(258330.8 + 387469.2 + 290509.8 + 110.6,
-                                                      112555.2 + 141308.3 + 196826.3)},
+                                        "bytes": _hbm(258295.7 + 392445.4 + 287458.4 + 110.6,
+                                                      112548.8 + 141310.1 + 196829.8)},
     ("backward", "gda3to1_bf16_n4096"): {"sha256": _BACKWARD_SRC,
-                                         "bytes": _hbm(193926.2 + 437390.1 + 532254.9 + 110.6,
-                                                       84651.3 + 59904.6 + 123005.6)},
+                                         "bytes": _hbm(193931.5 + 437623.8 + 540645.9 + 110.6,
+                                                      84650.4 + 59904.3 + 122995.9)},
 }
 
 
