@@ -55,7 +55,7 @@ _PREFILL_SRC = {"fwd_bf16.hip": "d47272efd7ac7857523abeaf9b939ef93dd82175fb2d613
            "abi.cpp": "213b8ef6083a5b9334b57809f4192c9222f65971fceab68ed81c6f4b47a26142"}
 _DECODE_SRC = {"decode_bf16.hip": "e6011a5ce752106b4036e40c96a967168254d9825c8f60702d4a8c6f597c5e98",
            "abi.cpp": "213b8ef6083a5b9334b57809f4192c9222f65971fceab68ed81c6f4b47a26142"}
-_BACKWARD_SRC = {"bwd_ring_bf16.hip": "baa62ce61839c81761dc781dc6e7c9923194180b5300f58ad834c49f0b2a3e6a",
+_BACKWARD_SRC = {"bwd_ring_bf16.hip": "c14ac302d2cfd9c2eda99c4e2fdb2af7d1be86f3ff0f64e97a0f023919466fa7",
            "bwd_rows.hip": "5fcb2e7c9d1de27467041285c83fc0866eda7e55c9463d69e2401f8423138335",
            "fwd_common.h": "bb6ae20a6225278b019d48ff544959515d34ac3ce94bf0133686525236becee1"}
 _KIB = 1024
@@ -68,23 +68,23 @@ def _hbm(fetch_kib, write_kib):
 
 MEASURED_TRAFFIC = {
     # prefill: the step's kernel (the map-2 and map-1 launches for shared combos)
-    ("prefill", "diff3b_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(147892.7, 98304.0)},
-    ("prefill", "gda3to1_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(114563.9, 73728.1)},
+    ("prefill", "diff3b_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(147774.7, 98304.4)},
+    ("prefill", "gda3to1_bf16_n4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(114755.4, 73728.2)},
     ("prefill", "gda4to1_gqa_bf16_n32768"): {"sha256": _PREFILL_SRC,
-                                            "bytes": _hbm(143378.9 + 317134.1, 131215.5 + 131072.0)},
-    ("prefill", "gda3to1_varlen_bf16_8x4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(152175.4, 101299.5)},
+                                            "bytes": _hbm(143368.4 + 317272.3, 131153.0 + 131072.0)},
+    ("prefill", "gda3to1_varlen_bf16_8x4096"): {"sha256": _PREFILL_SRC, "bytes": _hbm(152185.5, 101299.5)},
     # decode: decode_partial_kernel + decode_combine_kernel
     ("decode", "gda_decode_bf16_b64_l8192"): {"sha256": _DECODE_SRC,
-                                              "bytes": _hbm(595027.8 + 2114.4, 4119.8 + 288.0)},
+                                              "bytes": _hbm(594999.0 + 2114.4, 4119.4 + 288.0)},
     ("decode", "gda_decode_fp8_b64_l8192"): {"sha256": _DECODE_SRC,
-                                             "bytes": _hbm(294357.4 + 2114.4, 4119.4 + 288.0)},
+                                             "bytes": _hbm(294355.2 + 2114.4, 4119.4 + 288.0)},
     # backward: bwd_prep + bwd_dq_ring + bwd_dkv_ring + bwd_finalize
     ("backward", "diff3b_bf16_n4096"): {"sha256": _BACKWARD_SRC,
-                                        "bytes": _hbm(258295.7 + 392445.4 + 287458.4 + 110.6,
-                                                      112548.8 + 141310.1 + 196829.8)},
+                                        "bytes": _hbm(258293.8 + 393794.8 + 290292.9 + 110.6,
+                                                      112542.5 + 147455.5 + 196754.6)},
     ("backward", "gda3to1_bf16_n4096"): {"sha256": _BACKWARD_SRC,
-                                         "bytes": _hbm(193931.5 + 437623.8 + 540645.9 + 110.6,
-                                                      84650.4 + 59904.3 + 122995.9)},
+                                         "bytes": _hbm(193937.8 + 450707.0 + 456022.9 + 110.6,
+                                                      84649.0 + 61441.6 + 123085.2)},
 }
 
 

@@ -152,16 +152,19 @@ __device__ __forceinline__ void bwd_item(int logical, int ngroups, int nblk, int
 // the block issued at its own barrier had landed.
 __device__ __forceinline__ void vm_drain() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Wait until at most `after` blocks' loads (PER per wavefront each) are in flight.
-template <int PER>
+// Wait until at most `after` blocks' loads (PER per wavefront each) are in
+// flight; `after` never exceeds MAXA (the ring's depth less two), which keeps
+// the choice of wait to MAXA + 1 cases instead of five.
+template <int PER, int MAXA>
 __device__ __forceinline__ void wait_blocks(int after) {
-  if (after >= 4)
+  static_assert(MAXA >= 0 && MAXA <= 4, "at most four blocks in flight");
+  if (MAXA >= 4 && after >= 4)
     wait_vmcnt<4 * PER>();
-  else if (after == 3)
+  else if (MAXA >= 3 && after >= 3)
     wait_vmcnt<3 * PER>();
-  else if (after == 2)
+  else if (MAXA >= 2 && after >= 2)
     wait_vmcnt<2 * PER>();
-  else if (after == 1)
+  else if (MAXA >= 1 && after >= 1)
     wait_vmcnt<PER>();
   else
     wait_vmcnt<0>();
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(kQThreads, 4) void bwd_dq_ring_kernel(BwdParams p) 
   // barrier before block f: f has landed; then f + kQSlots - 1 is issued into
   // the slot of block f - 1, which every wavefront has finished with
   auto sync = [&](int f) {
-    wait_blocks<2>(min(F - 1, f + kQSlots - 2) - f);
+    wait_blocks<2, kQSlots - 2>(min(F - 1, f + kQSlots - 2) - f);
     wait_lds_and_barrier();
     if (f + kQSlots - 1 < F) issue();
   };
@@ -521,12 +524,16 @@ __global__ __launch_bounds__(kKThreads, 3) void bwd_dkv_ring_kernel(BwdParams p)
   const uint32_t vrange = (uint32_t)(N - vis_lo);  // visible queries: [vis_lo, N)
 
   // ---- DMA of one block (32 queries): wave w loads Q1 rows 8w .., Q2 rows
-  // 8w .., do rows 8w .. 8w + 7 (two KiB); wave 0 also the 32 row statistics
-  // (lanes 0-31, 16 B each).  Rows past N re-read row N - 1 (never visible).
+  // 8w .., do rows 8w .. 8w + 7 (two KiB) and the statistics of rows 8w ..
+  // 8w + 7 (lanes 0-7, 16 B each): five loads per block and wavefront, so the
+  // ring waits are the same in every wavefront.  Rows past N re-read row
+  // N - 1 (never visible).
   const uint32_t q1s = (uint32_t)p.sq1[1] * 2u, q2s = (uint32_t)p.sq2[1] * 2u;
   const uint32_t dos = (uint32_t)(p.Hs * DV) * 2u;  // do rows are dense [B][N][Hs][dv]
   const int qr0 = 8 * wave;
-  const bool rsw = wave == 0;  // this wavefront also loads the statistics: 5 loads per block, else 4
+  constexpr int kRsRows = kBK / kKWaves;  // statistics rows per wavefront
+  static_assert(kRsRows * kKWaves == kBK, "the statistics split evenly over the wavefronts");
+  const uint32_t rs_dst = RSOFF + 16u * kRsRows * wave;
   const int F = g * nb;
   int im = 0, ij = j0;
   uint32_t idst = lds_base;
@@ -549,14 +556,14 @@ __global__ __launch_bounds__(kKThreads, 3) void bwd_dkv_ring_kernel(BwdParams p)
       dma16(s_q2, o_q2, dst + KBLK + wave * 1024);
       dma16(s_do, o_d0, dst + 2 * KBLK + 2 * wave * 1024);
       dma16(s_do, o_d1, dst + 2 * KBLK + (2 * wave + 1) * 1024);
-      if (rsw && lane < kBK) dma16(s_rs, (uint32_t)lane * 16u, dst + RSOFF);
+      if (lane < kRsRows) dma16(s_rs, (uint32_t)(kRsRows * wave + lane) * 16u, dst + rs_dst);
     } else {  // the block that holds row N - 1
       const int lim = N - 1 - ij * kBK;
       dma16(s_q1, src_off(lane, qr0, false, q1s, lim), dst + wave * 1024);
       dma16(s_q2, src_off(lane, qr0, false, q2s, lim), dst + KBLK + wave * 1024);
       dma16(s_do, src_off(lane, qr0, true, dos, lim), dst + 2 * KBLK + 2 * wave * 1024);
       dma16(s_do, src_off(lane, qr0 + 4, true, dos, lim), dst + 2 * KBLK + (2 * wave + 1) * 1024);
-      if (rsw && lane < kBK) dma16(s_rs, (uint32_t)min(lane, lim) * 16u, dst + RSOFF);
+      if (lane < kRsRows) dma16(s_rs, (uint32_t)min(kRsRows * wave + lane, lim) * 16u, dst + rs_dst);
     }
     s_q1 += (size_t)kBK * q1s;
     s_q2 += (size_t)kBK * q2s;
@@ -569,11 +576,7 @@ __global__ __launch_bounds__(kKThreads, 3) void bwd_dkv_ring_kernel(BwdParams p)
     idst = idst == lds_base + (kKSlots - 1) * KSLOT ? lds_base : idst + KSLOT;
   };
   auto sync = [&](int f) {
-    const int after = min(F - 1, f + kKSlots - 2) - f;
-    if (rsw)
-      wait_blocks<5>(after);
-    else
-      wait_blocks<4>(after);
+    wait_blocks<5, kKSlots - 2>(min(F - 1, f + kKSlots - 2) - f);
     wait_lds_and_barrier();
     if (f + kKSlots - 1 < F) issue();
   };
