@@ -397,6 +397,9 @@ def probe_lib():
         L = ctypes.CDLL(PROBE_LIB)
         L.bench_hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
         L.bench_hbm_read_probe.restype = ctypes.c_int
+        L.bench_issue_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]
+        L.bench_issue_probe.restype = ctypes.c_int
         _probe = L
     return _probe
 
@@ -426,6 +429,47 @@ def stream_read_probe(nbytes, steps, warmup):
     del buf
     return {"value": nb / (ms * 1e-3) / 1e9, "unit": "GB/s", "bytes": nb,
             "kernel": "hbm_read_probe_kernel (non-temporal 16-B loads, 4 in flight per thread, 16384 x 256 threads)"}
+
+
+ISSUE_PROBE_OPS = ["v_fma_f32 v,v,const", "v_fma_f32 v,s,v", "v_fma_f32 v,v,v", "v_mul_f32 v,v", "v_add_u32 v,v",
+                   "v_cvt_pk_bf16_f32", "v_dot2c_f32_bf16", "v_exp_f32", "v_mov_b32", "v_exp_f32 (8 per 4 MFMAs)"]
+ISSUE_PROBE_PER_ITER = [32] * 9 + [8]  # VALU instructions per wavefront and iteration
+
+
+def issue_probe(iters=2048, reps=2):
+    """What runs beside the matrix pipe (bench_probe.hip, bench_issue_probe): per VALU
+    type, the time of its wavefronts alone (mode 1, two per SIMD), of the MFMA
+    wavefronts alone (mode 0, one per SIMD) and of both sharing the SIMDs (mode 2).
+    `ns_per_instr` is the SIMD's issue time per wavefront instruction with two
+    wavefronts issuing that type; `overlap` is the share of the shorter part hidden
+    under the longer: (mfma + valu/2 - both) / min(mfma, valu/2), 1 = fully hidden,
+    0 = serialised (valu/2: one of the two VALU wavefronts, as in mode 2)."""
+    import ctypes
+    import torch
+    L = probe_lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = cus * 4  # four rounds of one workgroup per CU
+    out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream()
+
+    def launch(op, mode):
+        st = L.bench_issue_probe(op, mode, iters, blocks, ctypes.c_void_p(out.data_ptr()), out.numel(),
+                                 ctypes.c_void_p(s.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"bench_issue_probe returned {st}")
+
+    rows = []
+    for rep in range(reps):
+        t_m = time_steps(lambda: launch(0, 0), 2, 1)
+        for op, name in enumerate(ISSUE_PROBE_OPS):
+            per_simd = blocks / cus * 2 * iters * ISSUE_PROBE_PER_ITER[op]  # VALU instructions per SIMD, mode 1
+            t_v = time_steps(lambda: launch(op, 1), 2, 1)
+            t_b = time_steps(lambda: launch(op, 2), 2, 1)
+            half = t_v / 2
+            rows.append({"rep": rep, "op": name, "ns_per_instr": t_v * 1e6 / per_simd, "valu_ms": half,
+                         "mfma_ms": t_m, "both_ms": t_b, "overlap": (t_m + half - t_b) / min(t_m, half)})
+    mfma_ns = min(r["mfma_ms"] for r in rows) * 1e6 / (blocks / cus * iters * 4)  # MFMAs per SIMD in mode 0
+    return {"probe": "issue", "mfma": "v_mfma_f32_32x32x16_bf16", "ns_per_mfma_per_simd": mfma_ns, "rows": rows}
 
 
 def device_info():
@@ -472,12 +516,23 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows in the CPU-baseline sample (default: every row of the 4096-token workload)")
     ap.add_argument("--out", default=None, help="also write the JSON line to this file")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="instead of the benchmark: which VALU instruction types run beside the matrix pipe "
+                         "(bench_probe.hip), one JSON line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (sharding is described in the design "
               "notes but not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.issue_probe:
+        line = json.dumps(issue_probe())
+        print(line, flush=True)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(line + "\n")
+        return
 
     w = W.WORKLOADS[args.workload]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)

@@ -12,6 +12,21 @@
 // src: device, 16-byte aligned, nbytes a multiple of 16 (0 = no-op); sink:
 // device fp32 [1], 4-byte aligned, not inside src.  Returns 0 on success, 1 on
 // invalid arguments (nothing launched), 3 on a launch failure.
+//
+// Issue probe (also measurement only): which VALU instruction types run while
+// the matrix pipe executes v_mfma_f32_32x32x16_bf16 on the same SIMD.  Each
+// workgroup has 8 wavefronts and 96 KiB of LDS (one per CU), so wavefronts w
+// and w + 4 share a SIMD.  Mode 0: wavefronts 0-3 issue MFMAs on four
+// independent accumulators, 4-7 exit; mode 1: all eight issue one VALU type
+// on eight independent chains (32 per iteration); mode 2: 0-3 as in mode 0,
+// 4-7 as in mode 1.  Registers only; one word per thread is stored at the end.
+//   int bench_issue_probe(int op, int mode, int iters, int blocks, float* out,
+//                         size_t out_floats, void* stream)
+// op: 0 v_fma_f32 v,v,const; 1 v_fma_f32 v,s,v; 2 v_fma_f32 v,v,v;
+// 3 v_mul_f32 v,v; 4 v_add_u32 v,v; 5 v_cvt_pk_bf16_f32; 6 v_dot2c_f32_bf16;
+// 7 v_exp_f32; 8 v_mov_b32; 9 v_exp_f32 at a quarter of the rate (8 per
+// iteration, against 4 MFMAs).  out: device fp32 [blocks * 512].  Returns 0, 1 on
+// invalid arguments (nothing launched) or 3 on a launch failure.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -52,4 +67,106 @@ extern "C" int bench_hbm_read_probe(const void* src, size_t nbytes, float* sink,
   hipLaunchKernelGGL(hbm_read_probe_kernel, dim3(kBlocks), dim3(kT), 0, (hipStream_t)stream, (const u32x4*)src,
                      (int64_t)(nbytes / 16), sink);
   return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kProbeThreads = 512, kProbeLds = 96 * 1024, kProbeOps = 10;
+
+template <int OP>
+__device__ __forceinline__ void valu8(float (&x)[8], float vb, float sb) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (OP == 0) asm volatile("v_fma_f32 %0, %0, %1, 0.5" : "+v"(x[i]) : "v"(vb));
+    if (OP == 1) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x[i]) : "s"(sb), "v"(vb));
+    if (OP == 2) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x[i]) : "v"(vb), "v"(vb));
+    if (OP == 3) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x[i]) : "v"(vb));
+    if (OP == 4) asm volatile("v_add_u32 %0, %0, %1" : "+v"(x[i]) : "v"(vb));
+    if (OP == 5) asm volatile("v_cvt_pk_bf16_f32 %0, %0, %1" : "+v"(x[i]) : "v"(vb));
+    if (OP == 6) asm volatile("v_dot2c_f32_bf16 %0, %1, %1" : "+v"(x[i]) : "v"(vb));
+    if (OP == 7) asm volatile("v_exp_f32 %0, %0" : "+v"(x[i]));
+    if (OP == 8) asm volatile("v_mov_b32 %0, %1" : "+v"(x[i]) : "v"(vb));
+  }
+}
+
+template <int OP, int MODE>
+__global__ __launch_bounds__(kProbeThreads) void issue_probe_kernel(float* out, int iters, float sa) {
+  extern __shared__ float probe_lds[];  // only holds the occupancy at one workgroup per CU
+  const int w = threadIdx.x >> 6;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (threadIdx.x + i));
+    b[i] = (__bf16)(0.002f * i);
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  float x[8];
+  const float vb = 0.999f + threadIdx.x * 1e-7f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = -0.001f * (threadIdx.x + i);
+  if (MODE != 1 && w < 4) {
+    for (int it = 0; it < iters; ++it) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+  } else if (MODE != 0) {
+    for (int it = 0; it < iters; ++it) {
+      if (OP == 9) {  // the light exponential stream: 8 per iteration
+        valu8<7>(x, vb, sa);
+      } else {
+        valu8<OP>(x, vb, sa);
+        valu8<OP>(x, vb, sa);
+        valu8<OP>(x, vb, sa);
+        valu8<OP>(x, vb, sa);
+      }
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += x[i];
+  out[(int64_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;
+}
+
+template <int OP, int MODE>
+int launch_issue_probe(int iters, int blocks, float* out, hipStream_t stream) {
+  auto k = issue_probe_kernel<OP, MODE>;
+  if (hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, kProbeLds) != hipSuccess) return 3;
+  hipLaunchKernelGGL(k, dim3(blocks), dim3(kProbeThreads), kProbeLds, stream, out, iters, 0.5f);
+  return hipGetLastError() == hipSuccess ? 0 : 3;
+}
+
+template <int OP>
+int launch_issue_probe_op(int mode, int iters, int blocks, float* out, hipStream_t stream) {
+  if (mode == 0) return launch_issue_probe<OP, 0>(iters, blocks, out, stream);
+  if (mode == 1) return launch_issue_probe<OP, 1>(iters, blocks, out, stream);
+  return launch_issue_probe<OP, 2>(iters, blocks, out, stream);
+}
+
+}  // namespace
+
+extern "C" int bench_issue_probe(int op, int mode, int iters, int blocks, float* out, size_t out_floats,
+                                 void* stream) {
+  if (op < 0 || op >= kProbeOps || mode < 0 || mode > 2 || iters < 1 || iters > (1 << 20) || blocks < 1 ||
+      blocks > 65536 || !out || (uintptr_t)out % 4 != 0 || out_floats < (size_t)blocks * kProbeThreads)
+    return 1;
+  const hipStream_t s = (hipStream_t)stream;
+  switch (op) {
+    case 0: return launch_issue_probe_op<0>(mode, iters, blocks, out, s);
+    case 1: return launch_issue_probe_op<1>(mode, iters, blocks, out, s);
+    case 2: return launch_issue_probe_op<2>(mode, iters, blocks, out, s);
+    case 3: return launch_issue_probe_op<3>(mode, iters, blocks, out, s);
+    case 4: return launch_issue_probe_op<4>(mode, iters, blocks, out, s);
+    case 5: return launch_issue_probe_op<5>(mode, iters, blocks, out, s);
+    case 6: return launch_issue_probe_op<6>(mode, iters, blocks, out, s);
+    case 7: return launch_issue_probe_op<7>(mode, iters, blocks, out, s);
+    case 8: return launch_issue_probe_op<8>(mode, iters, blocks, out, s);
+    default: return launch_issue_probe_op<9>(mode, iters, blocks, out, s);
+  }
 }
